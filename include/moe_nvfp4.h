@@ -1,0 +1,208 @@
+/*
+ * moe_nvfp4.h -- C ABI of the NVFP4 routed-expert (mixture-of-experts) layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  The routed-expert layer of a Qwen-style MoE decoder whose
+ * experts are NVFP4: E2M1 4-bit codes, one E4M3 scale per 16 consecutive
+ * weights along the reduction dimension, one fp32 multiplier per matrix and,
+ * for 4-bit activations, one fp32 activation input scale per matrix (page
+ * "Qwen3.8-Flash-Next NVIDIA NVFP4 for Infernix (bit-exact)", section "What
+ * is bit-exact and what is quantized").  512 routed experts with the top 10
+ * chosen per token (same page, opening description).  The expert activations
+ * run at 16, 8 or 4 bits (page "Infernix", section "Activation precision").
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are DEVICE pointers unless marked [host].  The caller owns every
+ *    buffer and keeps it alive until the work enqueued on the stream is done;
+ *    the library keeps no pointer after a call returns.  It allocates nothing.
+ *  - Calls validate their arguments on the host, enqueue kernels on stream
+ *    `s` and return without synchronising.  A device fault surfaces at the
+ *    caller's next synchronisation.
+ *  - On error nothing is enqueued (except MOE_E_HIP, reported after a launch
+ *    failed) and moe_last_error() describes it.  No C++ exception crosses
+ *    this boundary.
+ *  - bf16 tensors are passed as uint16_t bit patterns.  Matrices are row-major.
+ *  - Packed NVFP4 rows hold element 2i in the low nibble of byte i.
+ *  - Identical inputs give bitwise-identical outputs (no floating-point
+ *    atomics).  Calls are re-entrant; calls on different streams may overlap.
+ *  - Shapes: H and I are multiples of 32 and at most 4096; 1 <= k <= E <= 1024.
+ */
+#ifndef MOE_NVFP4_H
+#define MOE_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_E_ARG = -1,          /* null pointer where one is required, bad enum */
+  MOE_E_ALIGN = -2,        /* pointer not aligned as documented */
+  MOE_E_SHAPE = -3,        /* size out of the documented range */
+  MOE_E_UNSUPPORTED = -4,  /* valid but not implemented combination */
+  MOE_E_WORKSPACE = -5,    /* workspace smaller than the *_workspace_bytes() figure */
+  MOE_E_HIP = -6           /* a HIP call or kernel launch failed */
+} moe_status;
+
+/* Expert activation precision (page "Infernix", section "Activation precision"). */
+typedef enum {
+  MOE_A16 = 0, /* bf16 activations on the 4-bit weights (W4A16) */
+  MOE_A8 = 1,  /* E4M3 activations, one fp32 scale per 16 (W4A8) */
+  MOE_A4 = 2   /* NVFP4 activations under the matrix's fp32 input scale (W4A4) */
+} moe_act_mode;
+
+typedef enum { MOE_DT_BF16 = 0, MOE_DT_F32 = 1 } moe_dtype;
+
+/* One layer's experts, stacked over E, canonical layout.  The struct itself
+ * lives in host memory; its pointers are device pointers.  16-byte alignment
+ * is required for the code and scale arrays, 4-byte for the fp32 arrays.
+ *   gu_codes   [E][2I][H/2]  gate rows 0..I-1, then up rows I..2I-1
+ *   gu_scales  [E][2I][H/16] E4M3 block scales
+ *   dn_codes   [E][H][I/2]
+ *   dn_scales  [E][H][I/16]
+ *   gu_wscale  [E][2]        fp32 multiplier of the gate and the up matrix
+ *   dn_wscale  [E]           fp32 multiplier of the down matrix
+ *   gu_inscale [E][2]        fp32 activation input scales (MOE_A4 only, else may be NULL)
+ *   dn_inscale [E]           fp32 activation input scale of down (MOE_A4 only)
+ */
+typedef struct {
+  const uint8_t* gu_codes;
+  const uint8_t* gu_scales;
+  const uint8_t* dn_codes;
+  const uint8_t* dn_scales;
+  const float* gu_wscale;
+  const float* dn_wscale;
+  const float* gu_inscale;
+  const float* dn_inscale;
+  int32_t E, H, I;
+} moe_nvfp4_experts;
+
+/* Text of the last error on the calling thread; valid until the next call on it. */
+const char* moe_last_error(void);
+
+/* ------------------------------------------------------------------ router
+ * moe_route_topk: router logits, softmax, top-k, renormalise.
+ *   logits[t][e] = sum_h x[t][h] * w_router[e][h] (+ bias[e]), fp32 accumulate;
+ *   the k largest logits per token in descending order (equal logits: lower
+ *   expert first); topk_w[t][j] = p_j / sum of the chosen p with p the
+ *   softmax over all E (equal to a softmax over the chosen logits).
+ * The pages store the router in BF16 (page "Qwen3.8-Flash-Next NVIDIA NVFP4
+ * for Infernix (bit-exact)", section "What is bit-exact and what is
+ * quantized") and print no router formula; this is the Qwen-style reading.
+ *   x        [T][H] bf16          w_router [E][H] bf16     bias [E] fp32 or NULL
+ *   topk_ids [T][k] int32 (out)   topk_w   [T][k] fp32 (out)
+ *   ws: moe_route_workspace_bytes(T, E) bytes (fp32 logits), 16-byte aligned.
+ * NaN logits give unspecified ids.  T >= 1. */
+size_t moe_route_workspace_bytes(int T, int E);
+moe_status moe_route_topk(const uint16_t* x, const uint16_t* w_router, const float* bias, int T,
+                          int H, int E, int k, int32_t* topk_ids, float* topk_w, void* ws,
+                          size_t ws_bytes, hipStream_t s);
+
+/* ------------------------------------------------------------------ permute
+ * moe_permute: stable counting sort of the T*k (token, slot) pairs by expert.
+ * Pair p = t*k + j.  expert_offsets [E+1] is the exclusive scan of the expert
+ * histogram; sorted_pairs[expert_offsets[e] + r] is the r-th pair of expert e
+ * in ascending p; pair_row[p] is the inverse (row of pair p in sorted order).
+ * Ids outside [0, E) are dropped: not counted, pair_row[p] = -1, and
+ * expert_offsets[E] counts the valid pairs only.  Bit-exact and deterministic. */
+moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* expert_offsets,
+                       int32_t* sorted_pairs, int32_t* pair_row, hipStream_t s);
+
+/* ------------------------------------------------------------------ quantizers
+ * act_quant_nvfp4: NVFP4 per 16 along a row (the weight format of the page
+ * "Qwen3.8-Flash-Next NVIDIA NVFP4 for Infernix (bit-exact)", section "What
+ * is bit-exact and what is quantized", also used for 4-bit activations):
+ *   t = f32(f32(bamax / 6) / g);  s = E4M3(t);  d = f32(dec(s) * g);
+ *   code = E2M1(f32(v / d))   -- each op a correctly rounded fp32 op; E4M3 and
+ *   E2M1 round to nearest with ties to the even code, saturate (448 / 6) and
+ *   keep the sign; a block whose d is not positive gets all-zero codes.
+ * g = global[row_group ? row_group[r] : 0].
+ *   x [rows][cols] bf16 or fp32; codes [rows][cols/2]; scales [rows][cols/16].
+ * cols % 32 == 0. */
+moe_status act_quant_nvfp4(const void* x, moe_dtype xdt, int rows, int cols, const float* global,
+                           const int32_t* row_group, uint8_t* codes, uint8_t* scales,
+                           hipStream_t s);
+
+/* act_quant_fp8: the 8-bit activation mode (page "Infernix", section
+ * "Activation precision", --a8-activations), read as E4M3 codes with one fp32
+ * scale per 16: s = f32(bamax / 448); code = E4M3(f32(v / s)); s == 0 gives
+ * all-zero codes.  codes [rows][cols]; scales [rows][cols/16] fp32. */
+moe_status act_quant_fp8(const void* x, moe_dtype xdt, int rows, int cols, uint8_t* codes,
+                         float* scales, hipStream_t s);
+
+/* nvfp4_global_scale: per-matrix fp32 multiplier of NVFP4 packing,
+ * global[m] = f32(amax(|x_m|) / 2688) (2688 = 6 * 448) for the n_mat
+ * contiguous fp32 matrices of mat_elems elements each.  Deterministic. */
+moe_status nvfp4_global_scale(const float* x, int n_mat, int64_t mat_elems, float* global,
+                              hipStream_t s);
+
+/* ------------------------------------------------------------------ experts
+ * nvfp4_expert_ffn: every (token, expert) pair's SwiGLU expert in sorted order.
+ * For sorted row r of expert e (token t = sorted_pairs[r] / k):
+ *   g = x_t . Wgate_e,  u = x_t . Wup_e   (fp32 accumulate; x_t in the mode's
+ *   precision: bf16 for A16, E4M3 per 16 for A8, NVFP4 per 16 under the
+ *   matrix's input scale for A4);  h = silu(g) * u  (silu(z) = z / (1 + e^-z));
+ *   h is held at the mode's precision (bf16 / E4M3 per 16 / NVFP4 per 16 under
+ *   dn_inscale[e]);  y_pairs[r] = h . Wdown_e (fp32).
+ * The page "Infernix releases" (release 2026.10.11, "Highlights") describes
+ * the same stages on its GPU: narrow calls on one-column kernels with exact
+ * FP4 products, the down pass chained on gate/up.
+ *   w        [host] expert set          x [T][H] bf16
+ *   expert_offsets [E+1], sorted_pairs [T*k] from moe_permute
+ *   y_pairs  [T*k][H] fp32 (out; rows >= expert_offsets[E] are not written)
+ *   ws: nvfp4_expert_ffn_workspace_bytes(mode, T, k, H, I) bytes, 16-byte aligned.
+ * Workspace layout (P = T*k rows, byte offsets rounded up to 256):
+ *   A16: h bf16 [P][I]
+ *   A8 : x codes [T][H], x scales fp32 [T][H/16], h codes [P][I], h scales fp32 [P][I/16]
+ *   A4 : x codes [P][2][H/2], x scales [P][2][H/16] (gate, up), h codes [P][I/2],
+ *        h scales [P][I/16]  */
+size_t nvfp4_expert_ffn_workspace_bytes(moe_act_mode mode, int T, int k, int H, int I);
+moe_status nvfp4_expert_ffn(const moe_nvfp4_experts* w, moe_act_mode mode, const uint16_t* x,
+                            int T, int k, const int32_t* expert_offsets,
+                            const int32_t* sorted_pairs, float* y_pairs, void* ws,
+                            size_t ws_bytes, hipStream_t s);
+
+/* nvfp4_expert_ffn_stage: one stage of nvfp4_expert_ffn, same arguments and
+ * workspace: stage 0 quantizes the activations (8/4-bit modes; a no-op for
+ * A16), stage 1 runs gate/up + SwiGLU (writes the intermediate into ws),
+ * stage 2 runs down (writes y_pairs).  Running 0, 1, 2 in order on one stream
+ * equals nvfp4_expert_ffn; it lets a caller time or overlap the stages. */
+moe_status nvfp4_expert_ffn_stage(const moe_nvfp4_experts* w, moe_act_mode mode, int stage,
+                                  const uint16_t* x, int T, int k, const int32_t* expert_offsets,
+                                  const int32_t* sorted_pairs, float* y_pairs, void* ws,
+                                  size_t ws_bytes, hipStream_t s);
+
+/* ------------------------------------------------------------------ combine
+ * moe_combine: out[t] = bf16( sum_j topk_w[t][j] * y_pairs[pair_row[t*k + j]] ),
+ * j ascending, fp32 sum, one round-to-nearest-even to bf16.  Pairs with
+ * pair_row < 0 contribute nothing.  With a residual x (bf16 [T][H], not NULL)
+ * the result is the next layer's input bf16(x + bf16(sum)). */
+moe_status moe_combine(const float* y_pairs, const int32_t* pair_row, const float* topk_w, int T,
+                       int k, int H, const uint16_t* residual, uint16_t* out, hipStream_t s);
+
+/* ------------------------------------------------------------------ whole layer
+ * moe_layer_forward: route -> permute -> experts -> combine on one stream.
+ *   out [T][H] bf16 = the layer output, or bf16(residual + output) when
+ *   residual is not NULL (residual may equal x; out must not alias x).
+ *   ws: moe_layer_workspace_bytes(mode, T, k, E, H, I) bytes, 16-byte aligned.
+ *   moe_layer_workspace_layout fills offsets[7] (bytes into ws) of topk_ids
+ *   [T][k] int32, topk_w [T][k] fp32, expert_offsets [E+1] int32, sorted_pairs
+ *   [T*k] int32, pair_row [T*k] int32, y_pairs [T*k][H] fp32, and the expert
+ *   workspace (the nvfp4_expert_ffn layout above), so a caller can read them.
+ * Returns MOE_E_SHAPE from the layout call for sizes out of range. */
+moe_status moe_layer_workspace_layout(moe_act_mode mode, int T, int k, int E, int H, int I,
+                                      size_t offsets[7]);
+size_t moe_layer_workspace_bytes(moe_act_mode mode, int T, int k, int E, int H, int I);
+moe_status moe_layer_forward(const moe_nvfp4_experts* w, moe_act_mode mode, const uint16_t* x,
+                             const uint16_t* w_router, const float* router_bias, int T, int k,
+                             const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes,
+                             hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,410 @@
+"""Python binding of libmoe_nvfp4.so, the NVFP4 routed-expert layer for MI355X.
+
+Argument marshalling only: every function checks dtypes, shapes, devices and
+contiguity of torch tensors, allocates the outputs with torch, and calls the
+C entry point of the same name on the current torch stream.  Every step of the
+layer runs in the library's HIP kernels; there is no fallback.  The C ABI and
+its semantics are documented in include/moe_nvfp4.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_nvfp4.so")
+
+MOE_A16, MOE_A8, MOE_A4 = 0, 1, 2
+MODES = {"A16": MOE_A16, "A8": MOE_A8, "A4": MOE_A4}
+DT_BF16, DT_F32 = 0, 1
+STATUS = {0: "MOE_OK", -1: "MOE_E_ARG", -2: "MOE_E_ALIGN", -3: "MOE_E_SHAPE",
+          -4: "MOE_E_UNSUPPORTED", -5: "MOE_E_WORKSPACE", -6: "MOE_E_HIP"}
+
+EXPORTS = ("moe_last_error", "moe_route_workspace_bytes", "moe_route_topk", "moe_permute",
+           "act_quant_nvfp4", "act_quant_fp8", "nvfp4_global_scale",
+           "nvfp4_expert_ffn_workspace_bytes", "nvfp4_expert_ffn", "nvfp4_expert_ffn_stage",
+           "moe_combine",
+           "moe_layer_workspace_bytes", "moe_layer_workspace_layout", "moe_layer_forward")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, code, text):
+        super().__init__(f"{fn}: {STATUS.get(code, code)}: {text}")
+        self.code = code
+
+
+class _Experts(ctypes.Structure):
+    _fields_ = [("gu_codes", ctypes.c_void_p), ("gu_scales", ctypes.c_void_p),
+                ("dn_codes", ctypes.c_void_p), ("dn_scales", ctypes.c_void_p),
+                ("gu_wscale", ctypes.c_void_p), ("dn_wscale", ctypes.c_void_p),
+                ("gu_inscale", ctypes.c_void_p), ("dn_inscale", ctypes.c_void_p),
+                ("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32)]
+
+
+_lib = None
+_P, _I, _Z, _L = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_int64
+
+
+def lib():
+    """The loaded library; raises if it is not built (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() or "
+                               "python -m nvfp4_block_scaled_softmax_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "moe_last_error": ([], ctypes.c_char_p),
+            "moe_route_workspace_bytes": ([_I, _I], _Z),
+            "moe_route_topk": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
+            "moe_permute": ([_P, _I, _I, _I, _P, _P, _P, _P], _I),
+            "act_quant_nvfp4": ([_P, _I, _I, _I, _P, _P, _P, _P, _P], _I),
+            "act_quant_fp8": ([_P, _I, _I, _I, _P, _P, _P], _I),
+            "nvfp4_global_scale": ([_P, _I, _L, _P, _P], _I),
+            "nvfp4_expert_ffn_workspace_bytes": ([_I, _I, _I, _I, _I], _Z),
+            "nvfp4_expert_ffn": ([ctypes.POINTER(_Experts), _I, _P, _I, _I, _P, _P, _P, _P, _Z, _P], _I),
+            "nvfp4_expert_ffn_stage": ([ctypes.POINTER(_Experts), _I, _I, _P, _I, _I, _P, _P, _P, _P, _Z, _P], _I),
+            "moe_combine": ([_P, _P, _P, _I, _I, _I, _P, _P, _P], _I),
+            "moe_layer_workspace_bytes": ([_I, _I, _I, _I, _I, _I], _Z),
+            "moe_layer_workspace_layout": ([_I, _I, _I, _I, _I, _I, ctypes.POINTER(_Z)], _I),
+            "moe_layer_forward": ([ctypes.POINTER(_Experts), _I, _P, _P, _P, _I, _I, _P, _P, _P, _Z, _P], _I),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(fn, code):
+    if code != 0:
+        raise MoeError(fn, code, lib().moe_last_error().decode())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _bf16(t, name):
+    if t.dtype == torch.bfloat16:
+        return t
+    if t.dtype in (torch.int16, torch.uint16):
+        return t
+    raise TypeError(f"{name}: expected bfloat16 (or its 16-bit patterns), got {t.dtype}")
+
+
+def _mode(mode):
+    return MODES[mode] if isinstance(mode, str) else int(mode)
+
+
+# --------------------------------------------------------------------------- experts
+@dataclasses.dataclass
+class Experts:
+    """One layer's NVFP4 experts on the GPU, canonical layout (see the C header)."""
+    gu_codes: torch.Tensor     # uint8 [E, 2I, H/2]
+    gu_scales: torch.Tensor    # uint8 [E, 2I, H/16]
+    dn_codes: torch.Tensor     # uint8 [E, H, I/2]
+    dn_scales: torch.Tensor    # uint8 [E, H, I/16]
+    gu_wscale: torch.Tensor    # float32 [E, 2]
+    dn_wscale: torch.Tensor    # float32 [E]
+    gu_inscale: torch.Tensor | None = None   # float32 [E, 2]
+    dn_inscale: torch.Tensor | None = None   # float32 [E]
+
+    @property
+    def E(self):
+        return self.gu_codes.shape[0]
+
+    @property
+    def H(self):
+        return self.dn_codes.shape[1]
+
+    @property
+    def I(self):
+        return self.gu_codes.shape[1] // 2
+
+    def struct(self):
+        E, H, I = self.E, self.H, self.I
+        _need(self.gu_codes, "gu_codes", torch.uint8, (E, 2 * I, H // 2))
+        _need(self.gu_scales, "gu_scales", torch.uint8, (E, 2 * I, H // 16))
+        _need(self.dn_codes, "dn_codes", torch.uint8, (E, H, I // 2))
+        _need(self.dn_scales, "dn_scales", torch.uint8, (E, H, I // 16))
+        _need(self.gu_wscale, "gu_wscale", torch.float32, (E, 2))
+        _need(self.dn_wscale, "dn_wscale", torch.float32, (E,))
+        if self.gu_inscale is not None:
+            _need(self.gu_inscale, "gu_inscale", torch.float32, (E, 2))
+        if self.dn_inscale is not None:
+            _need(self.dn_inscale, "dn_inscale", torch.float32, (E,))
+        return _Experts(self.gu_codes.data_ptr(), self.gu_scales.data_ptr(),
+                        self.dn_codes.data_ptr(), self.dn_scales.data_ptr(),
+                        self.gu_wscale.data_ptr(), self.dn_wscale.data_ptr(),
+                        None if self.gu_inscale is None else self.gu_inscale.data_ptr(),
+                        None if self.dn_inscale is None else self.dn_inscale.data_ptr(),
+                        E, H, I)
+
+
+# --------------------------------------------------------------------------- entry points
+def moe_route_topk(x, w_router, k, bias=None, ids=None, w=None, ws=None):
+    """Router logits, softmax, top-k, renormalise.  Returns (ids int32 [T,k], w fp32 [T,k]).
+
+    ids / w / ws may be given (preallocated) to avoid allocations."""
+    x, w_router = _bf16(x, "x"), _bf16(w_router, "w_router")
+    T, H = x.shape
+    E = w_router.shape[0]
+    _need(x, "x")
+    _need(w_router, "w_router", shape=(E, H))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,))
+    if ids is None:
+        ids = torch.empty(T, k, dtype=torch.int32, device=x.device)
+    if w is None:
+        w = torch.empty(T, k, dtype=torch.float32, device=x.device)
+    _need(ids, "ids", torch.int32, (T, k))
+    _need(w, "w", torch.float32, (T, k))
+    nws = lib().moe_route_workspace_bytes(T, E)
+    if ws is None:
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=x.device)
+    _check("moe_route_topk", lib().moe_route_topk(_ptr(x), _ptr(w_router), _ptr(bias), T, H, E, k,
+                                                  _ptr(ids), _ptr(w), _ptr(ws), ws.numel(),
+                                                  _stream()))
+    return ids, w
+
+
+def moe_permute(topk_ids, E, off=None, sp=None, pr=None):
+    """Returns (expert_offsets [E+1], sorted_pairs [T*k], pair_row [T*k]), all int32."""
+    _need(topk_ids, "topk_ids", torch.int32)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev) if off is None else off
+    sp = torch.empty(T * k, dtype=torch.int32, device=dev) if sp is None else sp
+    pr = torch.empty(T * k, dtype=torch.int32, device=dev) if pr is None else pr
+    _need(off, "expert_offsets", torch.int32, (E + 1,))
+    _need(sp, "sorted_pairs", torch.int32, (T * k,))
+    _need(pr, "pair_row", torch.int32, (T * k,))
+    _check("moe_permute", lib().moe_permute(_ptr(topk_ids), T, k, E, _ptr(off), _ptr(sp), _ptr(pr),
+                                            _stream()))
+    return off, sp, pr
+
+
+def act_quant_nvfp4(x, global_scale, row_group=None):
+    """NVFP4 per 16 along rows of x (bf16 or fp32).  Returns (codes [R, C/2], scales [R, C/16])."""
+    _need(x, "x")
+    dt = DT_F32 if x.dtype == torch.float32 else DT_BF16
+    if dt == DT_BF16:
+        _bf16(x, "x")
+    R, C = x.shape
+    _need(global_scale, "global_scale", torch.float32)
+    if row_group is not None:
+        _need(row_group, "row_group", torch.int32, (R,))
+    codes = torch.empty(R, C // 2, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(R, C // 16, dtype=torch.uint8, device=x.device)
+    _check("act_quant_nvfp4", lib().act_quant_nvfp4(_ptr(x), dt, R, C, _ptr(global_scale),
+                                                    _ptr(row_group), _ptr(codes), _ptr(scales),
+                                                    _stream()))
+    return codes, scales
+
+
+def act_quant_fp8(x):
+    """8-bit mode per 16 along rows.  Returns (E4M3 codes [R, C], fp32 scales [R, C/16])."""
+    _need(x, "x")
+    dt = DT_F32 if x.dtype == torch.float32 else DT_BF16
+    if dt == DT_BF16:
+        _bf16(x, "x")
+    R, C = x.shape
+    codes = torch.empty(R, C, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(R, C // 16, dtype=torch.float32, device=x.device)
+    _check("act_quant_fp8", lib().act_quant_fp8(_ptr(x), dt, R, C, _ptr(codes), _ptr(scales),
+                                                _stream()))
+    return codes, scales
+
+
+def nvfp4_global_scale(x):
+    """Per-matrix multiplier f32(amax / 2688) of x [n_mat, ...] fp32."""
+    _need(x, "x", torch.float32)
+    n = x.shape[0]
+    g = torch.empty(n, dtype=torch.float32, device=x.device)
+    _check("nvfp4_global_scale", lib().nvfp4_global_scale(_ptr(x), n, x.numel() // n, _ptr(g),
+                                                          _stream()))
+    return g
+
+
+def ffn_workspace_bytes(mode, T, k, H, I):
+    return lib().nvfp4_expert_ffn_workspace_bytes(_mode(mode), T, k, H, I)
+
+
+def nvfp4_expert_ffn(experts: Experts, mode, x, k, expert_offsets, sorted_pairs, ws=None):
+    """Every pair's SwiGLU expert in sorted order.  Returns (y_pairs fp32 [T*k, H], workspace)."""
+    x = _bf16(x, "x")
+    _need(x, "x")
+    T, H = x.shape
+    s = experts.struct()
+    m = _mode(mode)
+    nws = ffn_workspace_bytes(m, T, k, H, experts.I)
+    if ws is None:
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=x.device)
+    y = torch.empty(T * k, H, dtype=torch.float32, device=x.device)
+    _check("nvfp4_expert_ffn", lib().nvfp4_expert_ffn(ctypes.byref(s), m, _ptr(x), T, k,
+                                                      _ptr(expert_offsets), _ptr(sorted_pairs),
+                                                      _ptr(y), _ptr(ws), ws.numel(), _stream()))
+    return y, ws
+
+
+def nvfp4_expert_ffn_stage(experts: Experts, mode, stage, x, k, expert_offsets, sorted_pairs, y,
+                           ws):
+    """One stage (0 quantize x, 1 gate/up + SwiGLU, 2 down) of nvfp4_expert_ffn, in place."""
+    x = _bf16(x, "x")
+    _need(x, "x")
+    T, H = x.shape
+    s = experts.struct()
+    _check("nvfp4_expert_ffn_stage",
+           lib().nvfp4_expert_ffn_stage(ctypes.byref(s), _mode(mode), stage, _ptr(x), T, k,
+                                        _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(y), _ptr(ws),
+                                        ws.numel(), _stream()))
+
+
+def moe_combine(y_pairs, pair_row, topk_w, residual=None, out=None):
+    """bf16 output [T, H] (bf16(x + out) when residual is given), as int16 bit patterns."""
+    _need(y_pairs, "y_pairs", torch.float32)
+    _need(topk_w, "topk_w", torch.float32)
+    T, k = topk_w.shape
+    H = y_pairs.shape[1]
+    _need(pair_row, "pair_row", torch.int32, (T * k,))
+    if residual is not None:
+        residual = _bf16(residual, "residual")
+        _need(residual, "residual")
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=y_pairs.device)
+    _need(out, "out", shape=(T, H))
+    _check("moe_combine", lib().moe_combine(_ptr(y_pairs), _ptr(pair_row), _ptr(topk_w), T, k, H,
+                                            _ptr(residual), _ptr(out), _stream()))
+    return out
+
+
+def layer_workspace_bytes(mode, T, k, E, H, I):
+    return lib().moe_layer_workspace_bytes(_mode(mode), T, k, E, H, I)
+
+
+def layer_workspace_layout(mode, T, k, E, H, I):
+    offs = (ctypes.c_size_t * 7)()
+    _check("moe_layer_workspace_layout",
+           lib().moe_layer_workspace_layout(_mode(mode), T, k, E, H, I, offs))
+    names = ("topk_ids", "topk_w", "expert_offsets", "sorted_pairs", "pair_row", "y_pairs", "ffn")
+    return dict(zip(names, list(offs)))
+
+
+def moe_layer_forward(experts: Experts, mode, x, w_router, k, bias=None, residual=None, ws=None,
+                      out=None):
+    """The whole layer on the current stream.  Returns (out bf16 [T, H], workspace)."""
+    x = _bf16(x, "x")
+    _need(x, "x")
+    T, H = x.shape
+    s = experts.struct()
+    m = _mode(mode)
+    w_router = _bf16(w_router, "w_router")
+    _need(w_router, "w_router", shape=(experts.E, H))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (experts.E,))
+    if residual is not None:
+        residual = _bf16(residual, "residual")
+        _need(residual, "residual", shape=(T, H))
+    nws = layer_workspace_bytes(m, T, k, experts.E, H, experts.I)
+    if ws is None:
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    _check("moe_layer_forward", lib().moe_layer_forward(ctypes.byref(s), m, _ptr(x), _ptr(w_router),
+                                                        _ptr(bias), T, k, _ptr(residual), _ptr(out),
+                                                        _ptr(ws), ws.numel(), _stream()))
+    return out, ws
+
+
+def workspace_views(ws, mode, T, k, E, H, I):
+    """Typed views of a layer workspace: ids, weights, offsets, permutation, y_pairs, FFN part."""
+    L = layer_workspace_layout(mode, T, k, E, H, I)
+    P = T * k
+
+    def view(name, n, dtype):
+        nbytes = n * torch.empty(0, dtype=dtype).element_size()
+        return ws[L[name]:L[name] + nbytes].view(dtype)
+
+    return {
+        "topk_ids": view("topk_ids", P, torch.int32).view(T, k),
+        "topk_w": view("topk_w", P, torch.float32).view(T, k),
+        "expert_offsets": view("expert_offsets", E + 1, torch.int32),
+        "sorted_pairs": view("sorted_pairs", P, torch.int32),
+        "pair_row": view("pair_row", P, torch.int32),
+        "y_pairs": view("y_pairs", P * H, torch.float32).view(P, H),
+        "ffn": ws[L["ffn"]:],
+    }
+
+
+def ffn_workspace_views(ws, mode, T, k, H, I):
+    """Typed views of the expert workspace (the layout documented in the C header)."""
+    P = T * k
+    m = _mode(mode)
+    o = 0
+    out = {}
+
+    def seg(name, nbytes, dtype, shape):
+        nonlocal o
+        n = nbytes // torch.empty(0, dtype=dtype).element_size()
+        out[name] = ws[o:o + nbytes].view(dtype).view(*shape)
+        o = (o + nbytes + 255) // 256 * 256
+        del n
+
+    if m == MOE_A16:
+        seg("h", P * I * 2, torch.bfloat16, (P, I))
+    elif m == MOE_A8:
+        seg("x_codes", T * H, torch.uint8, (T, H))
+        seg("x_scales", T * (H // 16) * 4, torch.float32, (T, H // 16))
+        seg("h_codes", P * I, torch.uint8, (P, I))
+        seg("h_scales", P * (I // 16) * 4, torch.float32, (P, I // 16))
+    else:
+        seg("x_codes", P * 2 * (H // 2), torch.uint8, (P, 2, H // 2))
+        seg("x_scales", P * 2 * (H // 16), torch.uint8, (P, 2, H // 16))
+        seg("h_codes", P * (I // 2), torch.uint8, (P, I // 2))
+        seg("h_scales", P * (I // 16), torch.uint8, (P, I // 16))
+    return out
+
+
+def pack_experts(w_gu, w_dn, gu_inscale=None, dn_inscale=None):
+    """NVFP4-pack fp32 expert weights on the GPU (each matrix under its own multiplier).
+
+    w_gu float32 [E, 2I, H] (gate rows then up rows of each expert), w_dn float32
+    [E, H, I].  Multipliers: f32(amax / 2688) per matrix (nvfp4_global_scale);
+    codes and block scales: act_quant_nvfp4 with each row's matrix multiplier.
+    """
+    _need(w_gu, "w_gu", torch.float32)
+    _need(w_dn, "w_dn", torch.float32)
+    E, I2, H = w_gu.shape
+    I = I2 // 2
+    dev = w_gu.device
+    g_gu = nvfp4_global_scale(w_gu.view(2 * E, I * H))
+    rg = (torch.arange(E * 2 * I, device=dev, dtype=torch.int32) // I).contiguous()
+    gu_codes, gu_scales = act_quant_nvfp4(w_gu.view(E * 2 * I, H), g_gu, rg)
+    g_dn = nvfp4_global_scale(w_dn.view(E, H * I))
+    rg = (torch.arange(E * H, device=dev, dtype=torch.int32) // H).contiguous()
+    dn_codes, dn_scales = act_quant_nvfp4(w_dn.view(E * H, I), g_dn, rg)
+    return Experts(gu_codes.view(E, 2 * I, H // 2), gu_scales.view(E, 2 * I, H // 16),
+                   dn_codes.view(E, H, I // 2), dn_scales.view(E, H, I // 16),
+                   g_gu.view(E, 2), g_dn, gu_inscale, dn_inscale)

@@ -1,0 +1,58 @@
+// Host-side helpers of the C ABI: the thread-local error text, argument
+// checks and launch checks.  Every entry point validates before enqueuing.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdarg.h>
+#include <string>
+
+#include "../../include/moe_nvfp4.h"
+
+namespace moe {
+
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+void clear_error();
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Checks after launches: any launch failure becomes MOE_E_HIP with HIP's text.
+inline moe_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: kernel launch failed: %s", what, hipGetErrorString(e));
+    return MOE_E_HIP;
+  }
+  return MOE_OK;
+}
+
+#define MOE_REQUIRE(cond, code, ...) \
+  do {                               \
+    if (!(cond)) {                   \
+      ::moe::set_error(__VA_ARGS__); \
+      return code;                   \
+    }                                \
+  } while (0)
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxDim = 4096;
+
+inline bool dim_ok(int d) { return d >= 32 && d <= kMaxDim && d % 32 == 0; }
+
+// Launchers implemented in the .hip files (no validation: callers validated).
+moe_status launch_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T,
+                        int H, int E, int k, int32_t* ids, float* w, float* logits, hipStream_t s);
+moe_status launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
+                          int32_t* sorted_pairs, int32_t* pair_row, hipStream_t s);
+// stage_mask: bit 0 activation quantization, bit 1 gate/up + SwiGLU, bit 2 down.
+moe_status launch_expert_ffn(const moe_nvfp4_experts& w, moe_act_mode mode, const uint16_t* x,
+                             int T, int k, const int32_t* offsets, const int32_t* sorted_pairs,
+                             float* y_pairs, void* ws, int stage_mask, hipStream_t s);
+moe_status launch_combine(const float* y_pairs, const int32_t* pair_row, const float* topk_w,
+                          int T, int k, int H, const uint16_t* residual, uint16_t* out,
+                          hipStream_t s);
+size_t expert_ffn_workspace(moe_act_mode mode, int T, int k, int H, int I);
+
+}  // namespace moe

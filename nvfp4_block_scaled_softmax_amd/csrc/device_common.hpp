@@ -1,0 +1,203 @@
+// Device helpers of the NVFP4 expert layer for gfx950 (CDNA4, wave64).
+//
+// Element formats: E2M1 4-bit codes (sign bit 3; magnitudes 0, 0.5, 1, 1.5, 2,
+// 3, 4, 6) and E4M3 8-bit codes (OCP E4M3: bias 7, subnormals, S.1111.111 NaN,
+// max 448), as in the OCP Microscaling and OFP8 specifications; the expert
+// format that uses them is described on the page "Qwen3.8-Flash-Next NVIDIA
+// NVFP4 for Infernix (bit-exact)", section "What is bit-exact and what is
+// quantized".
+//
+// Decoding uses the CDNA4 conversion instructions (exact for these formats;
+// v_cvt_scalef32_* is called with scale 1.0 because its scale operand only
+// contributes a power of two).  Rounding to E4M3 / E2M1 / bf16 is written out
+// in integer and compare operations so that ties, saturation and the sign of
+// zero are exactly the documented ones.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ bit casts
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From& f) {
+  static_assert(sizeof(To) == sizeof(From), "size");
+  To t;
+  __builtin_memcpy(&t, &f, sizeof(To));
+  return t;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ------------------------------------------------------------------ decoding
+// E4M3 byte (bits 7..0 of b) -> fp32, exact.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
+}
+
+// The two E2M1 codes in byte `sel` of w (low nibble first) as f16 / bf16 pairs.
+template <int SEL>
+__device__ __forceinline__ f16x2 e2m1x2_to_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+template <int SEL>
+__device__ __forceinline__ bf16x2 e2m1x2_to_bf16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL);
+}
+// Two E4M3 codes in half `HI` of w as an f16 pair (exact: E4M3 fits f16).
+template <bool HI>
+__device__ __forceinline__ f16x2 e4m3x2_to_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
+
+// ------------------------------------------------------------------ rounding
+// fp32 -> E4M3 code: nearest, ties to even code, |v| >= 448 (and inf) saturates
+// to 0x7E, sign kept (negative zero -> 0x80), NaN -> 0x00.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0u;                  // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;        // >= 448
+  if (a >= 0x3C800000u) {                          // >= 2^-6: normal E4M3
+    const uint32_t e = (a >> 23) - 120u;           // E4M3 exponent field
+    const uint32_t keep = (a >> 20) & 7u, rem = a & 0xFFFFFu;
+    uint32_t code = (e << 3) | keep;
+    code += (rem > 0x80000u) || (rem == 0x80000u && (keep & 1u));
+    return sign | code;
+  }
+  // subnormal E4M3: multiples of 2^-9; the scaling by 2^9 is exact
+  const float n = __builtin_rintf(__uint_as_float(a) * 512.0f);
+  return sign | (uint32_t)n;                       // n in [0, 8]; 8 is 0x08 = 2^-6
+}
+
+// fp32 -> E2M1 code: nearest, ties to even code, |q| > 6 saturates, sign kept.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float q) {
+  const float a = __builtin_fabsf(q);
+  const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return m | ((__float_as_uint(q) >> 28) & 8u);
+}
+
+// NVFP4 quantization of 16 fp32 values under global scale g: returns the E4M3
+// block scale and the 16 codes packed as two 32-bit words (value 2i in the
+// low nibble of byte i).  Each fp32 operation is one correctly rounded op, in
+// the order t = (bamax / 6) / g, d = dec(s) * g, q = v / d.
+__device__ __forceinline__ uint32_t nvfp4_quant16(const float* v, float g, uint32_t& lo,
+                                                  uint32_t& hi) {
+  float bamax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) bamax = __builtin_fmaxf(bamax, __builtin_fabsf(v[i]));
+  const float t = __fdiv_rn(__fdiv_rn(bamax, 6.0f), g);
+  const uint32_t s = f32_to_e4m3(t);
+  const float d = __fmul_rn(e4m3_to_f32(s), g);
+  lo = 0u;
+  hi = 0u;
+  if (d > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lo |= f32_to_e2m1(__fdiv_rn(v[i], d)) << (4 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hi |= f32_to_e2m1(__fdiv_rn(v[8 + i], d)) << (4 * i);
+  }
+  return s;
+}
+
+// 8-bit mode of 16 fp32 values: fp32 scale s = bamax / 448, codes E4M3(v / s)
+// packed four per 32-bit word (value i in byte i % 4 of word i / 4).
+__device__ __forceinline__ float fp8_quant16(const float* v, uint32_t* w4) {
+  float bamax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) bamax = __builtin_fmaxf(bamax, __builtin_fabsf(v[i]));
+  const float s = __fdiv_rn(bamax, 448.0f);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t w = 0u;
+    if (s > 0.0f) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) w |= f32_to_e4m3(__fdiv_rn(v[4 * q + b], s)) << (8 * b);
+    }
+    w4[q] = w;
+  }
+  return s;
+}
+
+// silu(g) * u in fp32: g / (1 + exp(-g)) * u.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return __fdiv_rn(g, 1.0f + expf(-g)) * u;
+}
+
+// ------------------------------------------------------------------ wave helpers
+// Sum over aligned groups of N lanes (N a power of two <= 64).
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = N / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Index of the s-th expert (0-based) with a non-empty segment, or -1; wave-wide,
+// every lane gets the answer.  offsets has E + 1 entries.
+__device__ __forceinline__ int find_active_expert(const int32_t* offsets, int E, int s) {
+  const int lane = lane_id();
+  int seen = 0;
+  for (int base = 0; base < E; base += kWave * 8) {
+    int cnt = 0;
+    int e0 = base + lane * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = e0 + i;
+      if (e < E) cnt += offsets[e + 1] > offsets[e];
+    }
+    // inclusive prefix over lanes
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += y;
+    }
+    const int total = __shfl(incl, kWave - 1, kWave);
+    const int target = s - seen;
+    if (target < total) {
+      // the lane whose range holds the target-th active expert
+      const int excl = incl - cnt;
+      int found = -1;
+      if (target >= excl && target < incl) {
+        int r = target - excl;
+        for (int i = 0; i < 8; ++i) {
+          const int e = e0 + i;
+          if (e < E && offsets[e + 1] > offsets[e]) {
+            if (r == 0) { found = e; break; }
+            --r;
+          }
+        }
+      }
+      // broadcast from the lane that found it
+      const unsigned long long m = __ballot(found >= 0);
+      const int src = __ffsll((long long)m) - 1;
+      return __shfl(found, src, kWave);
+    }
+    seen += total;
+  }
+  return -1;
+}
+
+}  // namespace moe

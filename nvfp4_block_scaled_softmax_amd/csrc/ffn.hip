@@ -1,0 +1,157 @@
+// nvfp4_expert_ffn: activation quantization for the 8/4-bit modes, then the
+// gate/up + SwiGLU and down kernels (narrow path; the MFMA grouped GEMM takes
+// wide 4-bit calls).
+#include "ffn_common.hpp"
+
+namespace moe {
+
+// 4-bit mode: x of every sorted row, quantized under its expert's gate and up
+// input scales.  One thread per (row, matrix, 16-block).
+__global__ void __launch_bounds__(256) k_quant_x_a4_rows(FfnArgs a) {
+  const int nb = a.H / 16;
+  const int64_t P = (int64_t)a.T * a.k;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= P * 2 * nb) return;
+  const int r = (int)(i / (2 * nb));
+  const int m = (int)((i / nb) % 2);
+  const int b = (int)(i % nb);
+  if (r >= a.offsets[a.E]) return;
+  const int e = expert_of_row(a.offsets, a.E, r);
+  const int t = a.sorted_pairs[r] / a.k;
+  const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)t * a.H + (size_t)b * 16);
+  float v[16];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint4 u = src[q];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * q + 2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+      v[8 * q + 2 * j + 1] = bf16_to_f32(w[j] >> 16);
+    }
+  }
+  uint32_t lo, hi;
+  const uint32_t s = nvfp4_quant16(v, a.gu_inscale[2 * e + m], lo, hi);
+  const size_t row = (size_t)r * 2 + m;
+  *reinterpret_cast<uint2*>(const_cast<uint8_t*>(a.xq_codes) + row * (a.H / 2) + (size_t)b * 8) =
+      make_uint2(lo, hi);
+  static_cast<uint8_t*>(const_cast<void*>(a.xq_scales))[row * nb + b] = (uint8_t)s;
+}
+
+size_t expert_ffn_workspace(moe_act_mode mode, int T, int k, int H, int I) {
+  return ffn_layout(mode, T, k, H, I).total;
+}
+
+moe_status launch_expert_ffn(const moe_nvfp4_experts& w, moe_act_mode mode, const uint16_t* x,
+                             int T, int k, const int32_t* offsets, const int32_t* sorted_pairs,
+                             float* y_pairs, void* ws, int stage_mask, hipStream_t s) {
+  const FfnLayout L = ffn_layout(mode, T, k, w.H, w.I);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  FfnArgs a;
+  a.gu_codes = w.gu_codes;
+  a.gu_scales = w.gu_scales;
+  a.dn_codes = w.dn_codes;
+  a.dn_scales = w.dn_scales;
+  a.gu_wscale = w.gu_wscale;
+  a.dn_wscale = w.dn_wscale;
+  a.gu_inscale = w.gu_inscale;
+  a.dn_inscale = w.dn_inscale;
+  a.E = w.E;
+  a.H = w.H;
+  a.I = w.I;
+  a.T = T;
+  a.k = k;
+  a.offsets = offsets;
+  a.sorted_pairs = sorted_pairs;
+  a.x = x;
+  a.xq_codes = mode == MOE_A16 ? nullptr : base + L.xq_codes;
+  a.xq_scales = mode == MOE_A16 ? nullptr : base + L.xq_scales;
+  a.h_codes = base + L.h_codes;
+  a.h_scales = mode == MOE_A16 ? nullptr : base + L.h_scales;
+  a.y = y_pairs;
+  const int P = T * k;
+  const int slots = P < w.E ? P : w.E;
+
+  if (mode == MOE_A8 && (stage_mask & 1)) {
+    moe_status st = act_quant_fp8(x, MOE_DT_BF16, T, w.H, base + L.xq_codes,
+                                  reinterpret_cast<float*>(base + L.xq_scales), s);
+    if (st != MOE_OK) return st;
+  } else if (mode == MOE_A4 && (stage_mask & 1)) {
+    const int64_t n = (int64_t)P * 2 * (w.H / 16);
+    hipLaunchKernelGGL(k_quant_x_a4_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    moe_status st = check_launch("nvfp4_expert_ffn (x quantization)");
+    if (st != MOE_OK) return st;
+  }
+  return launch_ffn_narrow(a, mode, slots, stage_mask, s);
+}
+
+}  // namespace moe
+
+extern "C" size_t nvfp4_expert_ffn_workspace_bytes(moe_act_mode mode, int T, int k, int H, int I) {
+  if (T < 1 || k < 1 || H < 32 || I < 32) return 0;
+  if (mode != MOE_A16 && mode != MOE_A8 && mode != MOE_A4) return 0;
+  return moe::expert_ffn_workspace(mode, T, k, H, I);
+}
+
+namespace moe {
+moe_status check_experts(const char* name, const moe_nvfp4_experts* w, moe_act_mode mode) {
+  MOE_REQUIRE(w, MOE_E_ARG, "%s: null expert set", name);
+  MOE_REQUIRE(mode == MOE_A16 || mode == MOE_A8 || mode == MOE_A4, MOE_E_ARG, "%s: bad mode %d",
+              name, (int)mode);
+  MOE_REQUIRE(w->gu_codes && w->gu_scales && w->dn_codes && w->dn_scales && w->gu_wscale &&
+                  w->dn_wscale,
+              MOE_E_ARG, "%s: null expert array", name);
+  MOE_REQUIRE(mode != MOE_A4 || (w->gu_inscale && w->dn_inscale), MOE_E_ARG,
+              "%s: 4-bit mode needs gu_inscale and dn_inscale", name);
+  MOE_REQUIRE(w->E >= 1 && w->E <= kMaxExperts && dim_ok(w->H) && dim_ok(w->I), MOE_E_SHAPE,
+              "%s: bad expert shape E=%d H=%d I=%d", name, w->E, w->H, w->I);
+  MOE_REQUIRE(aligned(w->gu_codes, 16) && aligned(w->gu_scales, 16) && aligned(w->dn_codes, 16) &&
+                  aligned(w->dn_scales, 16) && aligned(w->gu_wscale, 4) && aligned(w->dn_wscale, 4) &&
+                  (!w->gu_inscale || aligned(w->gu_inscale, 4)) &&
+                  (!w->dn_inscale || aligned(w->dn_inscale, 4)),
+              MOE_E_ALIGN, "%s: misaligned expert array", name);
+  return MOE_OK;
+}
+}  // namespace moe
+
+static moe_status ffn_entry(const char* name, const moe_nvfp4_experts* w, moe_act_mode mode,
+                            int stage_mask, const uint16_t* x, int T, int k,
+                            const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                            float* y_pairs, void* ws, size_t ws_bytes, hipStream_t s) {
+  moe::clear_error();
+  moe_status st = moe::check_experts(name, w, mode);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(x && expert_offsets && sorted_pairs && y_pairs && ws, MOE_E_ARG,
+              "%s: null pointer argument", name);
+  MOE_REQUIRE(T >= 1 && k >= 1 && k <= w->E && (int64_t)T * k <= (1 << 24), MOE_E_SHAPE,
+              "%s: bad shape T=%d k=%d", name, T, k);
+  MOE_REQUIRE(moe::aligned(x, 16) && moe::aligned(ws, 16) && moe::aligned(y_pairs, 16) &&
+                  moe::aligned(expert_offsets, 4) && moe::aligned(sorted_pairs, 4),
+              MOE_E_ALIGN, "%s: misaligned pointer", name);
+  const size_t need = moe::expert_ffn_workspace(mode, T, k, w->H, w->I);
+  MOE_REQUIRE(ws_bytes >= need, MOE_E_WORKSPACE, "%s: workspace %zu < %zu bytes", name, ws_bytes,
+              need);
+  return moe::launch_expert_ffn(*w, mode, x, T, k, expert_offsets, sorted_pairs, y_pairs, ws,
+                                stage_mask, s);
+}
+
+extern "C" moe_status nvfp4_expert_ffn(const moe_nvfp4_experts* w, moe_act_mode mode,
+                                       const uint16_t* x, int T, int k,
+                                       const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                                       float* y_pairs, void* ws, size_t ws_bytes, hipStream_t s) {
+  return ffn_entry("nvfp4_expert_ffn", w, mode, 7, x, T, k, expert_offsets, sorted_pairs, y_pairs,
+                   ws, ws_bytes, s);
+}
+
+extern "C" moe_status nvfp4_expert_ffn_stage(const moe_nvfp4_experts* w, moe_act_mode mode,
+                                             int stage, const uint16_t* x, int T, int k,
+                                             const int32_t* expert_offsets,
+                                             const int32_t* sorted_pairs, float* y_pairs, void* ws,
+                                             size_t ws_bytes, hipStream_t s) {
+  if (stage < 0 || stage > 2) {
+    moe::set_error("nvfp4_expert_ffn_stage: stage %d not in 0..2", stage);
+    return MOE_E_ARG;
+  }
+  return ffn_entry("nvfp4_expert_ffn_stage", w, mode, 1 << stage, x, T, k, expert_offsets,
+                   sorted_pairs, y_pairs, ws, ws_bytes, s);
+}

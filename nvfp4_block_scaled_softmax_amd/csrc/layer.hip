@@ -1,0 +1,107 @@
+// The whole routed-expert layer on one stream (route -> permute -> experts ->
+// combine), its workspace layout, and the thread-local error text.
+#include <string>
+
+#include "abi_common.hpp"
+
+namespace moe {
+
+static thread_local std::string g_error;
+
+void set_error(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+}
+
+void clear_error() { g_error.clear(); }
+
+moe_status check_experts(const char* name, const moe_nvfp4_experts* w, moe_act_mode mode);
+
+struct LayerLayout {
+  size_t ids, w, offsets, sorted, pair_row, y, ffn, route, total;
+};
+
+static bool layer_layout(moe_act_mode mode, int T, int k, int E, int H, int I, LayerLayout& L) {
+  if (T < 1 || k < 1 || E < 1 || E > kMaxExperts || k > E || !dim_ok(H) || !dim_ok(I) ||
+      (int64_t)T * k > (1 << 24))
+    return false;
+  if (mode != MOE_A16 && mode != MOE_A8 && mode != MOE_A4) return false;
+  const size_t P = (size_t)T * k;
+  size_t o = 0;
+  auto seg = [&](size_t bytes) { const size_t at = o; o = round_up(o + bytes, 256); return at; };
+  L.ids = seg(P * 4);
+  L.w = seg(P * 4);
+  L.offsets = seg((size_t)(E + 1) * 4);
+  L.sorted = seg(P * 4);
+  L.pair_row = seg(P * 4);
+  L.y = seg(P * H * 4);
+  L.ffn = seg(expert_ffn_workspace(mode, T, k, H, I));
+  L.route = seg((size_t)T * E * 4);
+  L.total = o;
+  return true;
+}
+
+}  // namespace moe
+
+extern "C" const char* moe_last_error(void) { return moe::g_error.c_str(); }
+
+extern "C" size_t moe_layer_workspace_bytes(moe_act_mode mode, int T, int k, int E, int H, int I) {
+  moe::LayerLayout L;
+  return moe::layer_layout(mode, T, k, E, H, I, L) ? L.total : 0;
+}
+
+extern "C" moe_status moe_layer_workspace_layout(moe_act_mode mode, int T, int k, int E, int H,
+                                                 int I, size_t offsets[7]) {
+  moe::clear_error();
+  MOE_REQUIRE(offsets, MOE_E_ARG, "moe_layer_workspace_layout: null offsets");
+  moe::LayerLayout L;
+  MOE_REQUIRE(moe::layer_layout(mode, T, k, E, H, I, L), MOE_E_SHAPE,
+              "moe_layer_workspace_layout: bad shape or mode");
+  offsets[0] = L.ids;
+  offsets[1] = L.w;
+  offsets[2] = L.offsets;
+  offsets[3] = L.sorted;
+  offsets[4] = L.pair_row;
+  offsets[5] = L.y;
+  offsets[6] = L.ffn;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_layer_forward(const moe_nvfp4_experts* w, moe_act_mode mode,
+                                        const uint16_t* x, const uint16_t* w_router,
+                                        const float* router_bias, int T, int k,
+                                        const uint16_t* residual, uint16_t* out, void* ws,
+                                        size_t ws_bytes, hipStream_t s) {
+  moe::clear_error();
+  moe_status st = moe::check_experts("moe_layer_forward", w, mode);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(x && w_router && out && ws, MOE_E_ARG, "moe_layer_forward: null pointer argument");
+  moe::LayerLayout L;
+  MOE_REQUIRE(moe::layer_layout(mode, T, k, w->E, w->H, w->I, L), MOE_E_SHAPE,
+              "moe_layer_forward: bad shape T=%d k=%d", T, k);
+  MOE_REQUIRE(out != x, MOE_E_ARG, "moe_layer_forward: out must not alias x");
+  MOE_REQUIRE(moe::aligned(x, 16) && moe::aligned(w_router, 16) && moe::aligned(out, 16) &&
+                  moe::aligned(ws, 256) && (!residual || moe::aligned(residual, 16)) &&
+                  (!router_bias || moe::aligned(router_bias, 4)),
+              MOE_E_ALIGN, "moe_layer_forward: misaligned pointer (workspace needs 256 bytes)");
+  MOE_REQUIRE(ws_bytes >= L.total, MOE_E_WORKSPACE, "moe_layer_forward: workspace %zu < %zu bytes",
+              ws_bytes, L.total);
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  int32_t* ids = reinterpret_cast<int32_t*>(b + L.ids);
+  float* tw = reinterpret_cast<float*>(b + L.w);
+  int32_t* offs = reinterpret_cast<int32_t*>(b + L.offsets);
+  int32_t* sorted = reinterpret_cast<int32_t*>(b + L.sorted);
+  int32_t* prow = reinterpret_cast<int32_t*>(b + L.pair_row);
+  float* y = reinterpret_cast<float*>(b + L.y);
+  if ((st = moe::launch_route(x, w_router, router_bias, T, w->H, w->E, k, ids, tw,
+                              reinterpret_cast<float*>(b + L.route), s)) != MOE_OK)
+    return st;
+  if ((st = moe::launch_permute(ids, T, k, w->E, offs, sorted, prow, s)) != MOE_OK) return st;
+  if ((st = moe::launch_expert_ffn(*w, mode, x, T, k, offs, sorted, y, b + L.ffn, 7, s)) != MOE_OK)
+    return st;
+  return moe::launch_combine(y, prow, tw, T, k, w->H, residual, out, s);
+}

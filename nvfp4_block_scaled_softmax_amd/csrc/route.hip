@@ -1,0 +1,214 @@
+// Router: logits = x . Wr^T (+ bias), softmax, top-k, renormalise.
+//
+// The router is stored BF16 (page "Qwen3.8-Flash-Next NVIDIA NVFP4 for
+// Infernix (bit-exact)", section "What is bit-exact and what is quantized");
+// 512 experts, the top 10 per token (same page, opening description).  The
+// pages print no router formula; this is the Qwen-style reading (softmax over
+// all experts, the k largest, weights renormalised over the chosen ones).
+//
+// Decode (T <= 8): the 512 x H router matrix is one HBM stream.  One wave per
+// expert row; x sits in LDS; bf16 pairs meet in v_dot2_f32_bf16 (exact
+// products, fp32 sums).
+// Wide calls: a bf16 MFMA GEMM (16x16x32), operands read straight from
+// global memory in the MFMA lane layout (both are K-contiguous).
+// Top-k: one wave per token, k rounds of a wave argmax (ties to lower index).
+#include "abi_common.hpp"
+#include "device_common.hpp"
+
+namespace moe {
+
+constexpr int kNarrowT = 8;
+
+__global__ void __launch_bounds__(256) k_router_logits_narrow(const uint16_t* __restrict__ x,
+                                                              const uint16_t* __restrict__ wr,
+                                                              const float* __restrict__ bias,
+                                                              int T, int H, int E,
+                                                              float* __restrict__ logits) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint4* xs = reinterpret_cast<uint4*>(smem);       // [T][H/8] chunks of 8 bf16
+  const int nch = H / 8;
+  for (int i = threadIdx.x; i < T * nch; i += blockDim.x)
+    xs[i] = reinterpret_cast<const uint4*>(x)[i];
+  __syncthreads();
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int e = blockIdx.x * 4 + wave;
+  if (e >= E) return;
+  const uint4* wrow = reinterpret_cast<const uint4*>(wr + (size_t)e * H);
+  float acc[kNarrowT];
+#pragma unroll
+  for (int t = 0; t < kNarrowT; ++t) acc[t] = 0.0f;
+  // all of this lane's chunks of the row in flight at once (H <= 4096: <= 8 chunks)
+  constexpr int kMaxChunks = kMaxDim / 8 / kWave;
+  uint4 wv[kMaxChunks];
+#pragma unroll
+  for (int j = 0; j < kMaxChunks; ++j) {
+    const int c = lane + kWave * j;
+    if (c < nch) wv[j] = wrow[c];
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxChunks; ++j) {
+    const int c = lane + kWave * j;
+    if (c >= nch) break;
+    const uint4 w = wv[j];
+#pragma unroll
+    for (int t = 0; t < kNarrowT; ++t) {
+      if (t < T) {
+        const uint4 xv = xs[t * nch + c];
+        float a = acc[t];
+        a = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(w.x), bitcast<bf16x2>(xv.x), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(w.y), bitcast<bf16x2>(xv.y), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(w.z), bitcast<bf16x2>(xv.z), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(w.w), bitcast<bf16x2>(xv.w), a, false);
+        acc[t] = a;
+      }
+    }
+  }
+  const float b = bias ? bias[e] : 0.0f;
+#pragma unroll
+  for (int t = 0; t < kNarrowT; ++t) {
+    if (t < T) {
+      const float v = group_sum<kWave>(acc[t]);
+      if (lane == 0) logits[(size_t)t * E + e] = v + b;
+    }
+  }
+}
+
+// Wide logits: block = 4 waves = 64 tokens x 64 experts; wave = 32 x 32 (2 x 2 MFMA tiles).
+__global__ void __launch_bounds__(256) k_router_logits_mfma(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ wr,
+                                                            const float* __restrict__ bias,
+                                                            int T, int H, int E,
+                                                            float* __restrict__ logits) {
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int t0 = blockIdx.y * 64 + (wave >> 1) * 32;
+  const int e0 = blockIdx.x * 64 + (wave & 1) * 32;
+  const int r = lane & 15, g = lane >> 4;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint4 zero = {0u, 0u, 0u, 0u};
+  for (int k0 = 0; k0 < H; k0 += 32) {
+    uint4 a[2], b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = t0 + 16 * i + r;
+      a[i] = t < T ? *reinterpret_cast<const uint4*>(x + (size_t)t * H + k0 + 8 * g) : zero;
+      const int e = e0 + 16 * i + r;
+      b[i] = e < E ? *reinterpret_cast<const uint4*>(wr + (size_t)e * H + k0 + 8 * g) : zero;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(a[i]),
+                                                            bitcast<bf16x8>(b[j]), acc[i][j], 0, 0, 0);
+  }
+  // C layout: lane holds rows (tokens) 4g + q, column (expert) r of each tile.
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = e0 + 16 * j + r;
+    if (e >= E) continue;
+    const float b = bias ? bias[e] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = t0 + 16 * i + 4 * g + q;
+        if (t < T) logits[(size_t)t * E + e] = acc[i][j][q] + b;
+      }
+  }
+}
+
+// One wave per token.  Expert e lives in lane e % 64, slot e / 64.
+constexpr int kMaxSlots = kMaxExperts / kWave;  // 16
+
+__global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, int T, int E,
+                                              int k, int32_t* __restrict__ ids,
+                                              float* __restrict__ w) {
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * E;
+  float v[kMaxSlots];
+  uint32_t taken = 0u;
+#pragma unroll
+  for (int i = 0; i < kMaxSlots; ++i) {
+    const int e = lane + kWave * i;
+    v[i] = e < E ? row[e] : -__builtin_huge_valf();
+    if (e >= E) taken |= 1u << i;
+  }
+  float top_v = 0.0f, first_v = 0.0f;
+  int top_id = 0;
+  for (int j = 0; j < k; ++j) {
+    // local best: largest value, lowest expert index on ties (slots ascend in index)
+    float bv = -__builtin_huge_valf();
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < kMaxSlots; ++i) {
+      const bool free_ = !((taken >> i) & 1u);
+      const int e = lane + kWave * i;
+      if (free_ && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if ((bi % kWave) == lane) taken |= 1u << (bi / kWave);
+    if (j == 0) first_v = bv;
+    if (lane == j) { top_v = bv; top_id = bi; }
+  }
+  // renormalised softmax over the chosen logits: exp(l_j - l_max) / sum
+  const float ex = lane < k ? expf(top_v - first_v) : 0.0f;
+  const float sum = group_sum<kWave>(ex);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = top_id;
+    w[(size_t)t * k + lane] = __fdiv_rn(ex, sum);
+  }
+}
+
+moe_status launch_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T,
+                        int H, int E, int k, int32_t* ids, float* w, float* logits,
+                        hipStream_t s) {
+  if (T <= kNarrowT) {
+    const size_t lds = (size_t)T * H * 2;
+    hipLaunchKernelGGL(k_router_logits_narrow, dim3((E + 3) / 4), dim3(256), lds, s, x, w_router,
+                       bias, T, H, E, logits);
+  } else {
+    hipLaunchKernelGGL(k_router_logits_mfma, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s,
+                       x, w_router, bias, T, H, E, logits);
+  }
+  moe_status st = check_launch("moe_route_topk (logits)");
+  if (st != MOE_OK) return st;
+  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w);
+  return check_launch("moe_route_topk (top-k)");
+}
+
+}  // namespace moe
+
+extern "C" size_t moe_route_workspace_bytes(int T, int E) {
+  if (T < 1 || E < 1) return 0;
+  return moe::round_up((size_t)T * E * sizeof(float), 256);
+}
+
+extern "C" moe_status moe_route_topk(const uint16_t* x, const uint16_t* w_router, const float* bias,
+                                     int T, int H, int E, int k, int32_t* topk_ids, float* topk_w,
+                                     void* ws, size_t ws_bytes, hipStream_t s) {
+  moe::clear_error();
+  MOE_REQUIRE(x && w_router && topk_ids && topk_w && ws, MOE_E_ARG,
+              "moe_route_topk: null pointer argument");
+  MOE_REQUIRE(T >= 1 && moe::dim_ok(H) && E >= 1 && E <= moe::kMaxExperts && k >= 1 && k <= E &&
+                  k <= moe::kWave,
+              MOE_E_SHAPE, "moe_route_topk: bad shape T=%d H=%d E=%d k=%d", T, H, E, k);
+  MOE_REQUIRE(moe::aligned(x, 16) && moe::aligned(w_router, 16) && moe::aligned(ws, 16) &&
+                  moe::aligned(topk_ids, 4) && moe::aligned(topk_w, 4) &&
+                  (!bias || moe::aligned(bias, 4)),
+              MOE_E_ALIGN, "moe_route_topk: misaligned pointer");
+  MOE_REQUIRE(ws_bytes >= moe_route_workspace_bytes(T, E), MOE_E_WORKSPACE,
+              "moe_route_topk: workspace %zu < %zu bytes", ws_bytes, moe_route_workspace_bytes(T, E));
+  return moe::launch_route(x, w_router, bias, T, H, E, k, topk_ids, topk_w,
+                           static_cast<float*>(ws), s);
+}

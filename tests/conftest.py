@@ -11,3 +11,18 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (runs through the C-ABI library)")
     config.addinivalue_line("markers", "slow: full-size case, minutes of host work")
+
+
+def pytest_collection_finish(session):
+    # start the oracle's packing pool before any test touches the GPU
+    if any(item.get_closest_marker("gpu") for item in session.items):
+        from tests import oracle_cache
+        oracle_cache.start_pool()
+
+
+def pytest_sessionfinish(session, exitstatus):
+    try:
+        from tests import oracle_cache
+        oracle_cache.stop_pool()
+    except Exception:
+        pass

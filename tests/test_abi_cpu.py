@@ -1,0 +1,104 @@
+"""The C-ABI library without a GPU: it loads, exports every function the header
+declares, sizes workspaces, and rejects bad arguments on the host (documented
+negative codes, nothing enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_block_scaled_softmax_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_nvfp4.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "return")))
+
+
+def test_library_exports_every_declared_function():
+    L = moe.lib()
+    declared = _declared()
+    assert "moe_layer_forward" in declared and "act_quant_nvfp4" in declared
+    missing = [n for n in declared if not hasattr(L, n)]
+    assert not missing, missing
+    assert sorted(moe.EXPORTS) == declared
+
+
+def test_workspace_sizes():
+    L = moe.lib()
+    assert L.moe_route_workspace_bytes(8, 512) == 8 * 512 * 4
+    assert L.moe_route_workspace_bytes(0, 512) == 0
+    # 4-bit mode: x codes/scales per pair and matrix, h codes/scales per pair
+    P, H, I = 80, 3072, 512
+    want = sum((n + 255) // 256 * 256 for n in (P * 2 * H // 2, P * 2 * H // 16, P * I // 2, P * I // 16))
+    assert L.nvfp4_expert_ffn_workspace_bytes(moe.MOE_A4, 8, 10, H, I) == want
+    assert L.nvfp4_expert_ffn_workspace_bytes(moe.MOE_A16, 1, 10, H, I) == 10 * I * 2
+    assert L.nvfp4_expert_ffn_workspace_bytes(7, 1, 10, H, I) == 0
+    assert L.moe_layer_workspace_bytes(moe.MOE_A16, 1, 10, 512, 3072, 500) == 0   # I % 32 != 0
+    lay = moe.layer_workspace_layout("A4", 1024, 10, 512, 3072, 512)
+    assert lay["topk_ids"] == 0 and all(v % 256 == 0 for v in lay.values())
+
+
+def _err(code):
+    return moe.STATUS[code], moe.lib().moe_last_error().decode()
+
+
+P16 = ctypes.c_void_p(4096)     # aligned non-null host address, never dereferenced
+P4 = ctypes.c_void_p(4100)      # 4-byte aligned, not 16
+
+
+def test_route_validation():
+    L = moe.lib()
+    assert _err(L.moe_route_topk(None, P16, None, 1, 3072, 512, 10, P16, P16, P16, 1 << 20, None))[0] == "MOE_E_ARG"
+    assert _err(L.moe_route_topk(P16, P16, None, 1, 3000, 512, 10, P16, P16, P16, 1 << 20, None))[0] == "MOE_E_SHAPE"
+    assert _err(L.moe_route_topk(P16, P16, None, 1, 3072, 512, 513, P16, P16, P16, 1 << 20, None))[0] == "MOE_E_SHAPE"
+    assert _err(L.moe_route_topk(P16, P16, None, 1, 3072, 2048, 10, P16, P16, P16, 1 << 30, None))[0] == "MOE_E_SHAPE"
+    assert _err(L.moe_route_topk(P4, P16, None, 1, 3072, 512, 10, P16, P16, P16, 1 << 20, None))[0] == "MOE_E_ALIGN"
+    code, text = _err(L.moe_route_topk(P16, P16, None, 1, 3072, 512, 10, P16, P16, P16, 16, None))
+    assert code == "MOE_E_WORKSPACE" and "workspace" in text
+
+
+def test_permute_and_combine_validation():
+    L = moe.lib()
+    assert _err(L.moe_permute(P16, 1, 10, 5, P16, P16, P16, None))[0] == "MOE_E_SHAPE"
+    assert _err(L.moe_permute(None, 1, 2, 5, P16, P16, P16, None))[0] == "MOE_E_ARG"
+    assert _err(L.moe_combine(P16, P16, P16, 1, 2, 3000, None, P16, None))[0] == "MOE_E_SHAPE"
+    assert _err(L.moe_combine(P16, P16, P16, 1, 2, 3072, ctypes.c_void_p(4098), P16, None))[0] == "MOE_E_ALIGN"
+
+
+def test_quant_validation():
+    L = moe.lib()
+    assert _err(L.act_quant_nvfp4(P16, 0, 4, 48, P16, None, P16, P16, None))[0] == "MOE_E_SHAPE"
+    assert _err(L.act_quant_nvfp4(P16, 5, 4, 64, P16, None, P16, P16, None))[0] == "MOE_E_ARG"
+    assert _err(L.act_quant_fp8(P16, 0, 4, 64, P16, None, None))[0] == "MOE_E_ARG"
+    assert _err(L.nvfp4_global_scale(P16, 2, 6, P16, None))[0] == "MOE_E_SHAPE"
+
+
+def test_expert_validation():
+    L = moe.lib()
+    s = moe._Experts(4096, 4096, 4096, 4096, 4096, 4096, None, None, 512, 3072, 512)
+    args = (P16, 1, 10, P16, P16, P16, P16, 1 << 30, None)
+    assert _err(L.nvfp4_expert_ffn(ctypes.byref(s), moe.MOE_A4, *args))[0] == "MOE_E_ARG"  # no inscales
+    assert _err(L.nvfp4_expert_ffn(ctypes.byref(s), 9, *args))[0] == "MOE_E_ARG"
+    s.I = 500
+    assert _err(L.nvfp4_expert_ffn(ctypes.byref(s), moe.MOE_A16, *args))[0] == "MOE_E_SHAPE"
+    s.I = 512
+    code, _ = _err(L.nvfp4_expert_ffn(ctypes.byref(s), moe.MOE_A16, P16, 1, 10, P16, P16, P16, P16, 100, None))
+    assert code == "MOE_E_WORKSPACE"
+    assert _err(L.nvfp4_expert_ffn_stage(ctypes.byref(s), moe.MOE_A16, 3, *args))[0] == "MOE_E_ARG"
+    out = ctypes.c_void_p(8192)
+    assert _err(L.moe_layer_forward(ctypes.byref(s), moe.MOE_A16, P16, P16, None, 1, 10, None, P16,
+                                    out, 1 << 30, None))[0] == "MOE_E_ARG"          # out aliases x
+    assert _err(L.moe_layer_forward(ctypes.byref(s), moe.MOE_A16, P16, P16, None, 1, 10, None, out,
+                                    ctypes.c_void_p(4096 + 16), 1 << 30, None))[0] == "MOE_E_ALIGN"
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        moe.moe_permute(torch.zeros(2, 2, dtype=torch.int32), 4)
