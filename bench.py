@@ -14,9 +14,9 @@ Cache from serving the weights, the steps cycle over 8 independently seeded
 copies of the layer and 64 seeded token batches.
 
 roofline: the gate/up + SwiGLU kernel (the largest weight stream of the step),
-timed per launch with HIP events recorded on the stream it runs on, in a
-second timed pass that runs the layer stage by stage; its algorithmic bytes
-are the touched experts' gate/up codes + scales.
+timed with HIP events on the stream it runs on, in a second timed pass that
+launches it back to back over the layer copies (each with its own routing);
+its algorithmic bytes are the touched experts' gate/up codes + scales.
 
 cpu_baseline: the oracle (oracle/, double precision numpy, one BLAS thread)
 on a bounded sample of the same workload, on this machine's host CPU.
@@ -129,81 +129,75 @@ def run_gpu(w, mode, steps, warmup, n_layers, n_batches):
     ms = ev0.elapsed_time(ev1) / steps
     total_bytes = sum(combo_bytes[s % combos] for s in range(steps))
 
-    # timed pass B: stage by stage, HIP events around the gate/up kernel
+    # timed pass B: the gate/up + SwiGLU kernel alone, launched back to back (the
+    # queue stays full, so the HIP events bracket GPU time only), cycling over the
+    # layer copies so its weights come from HBM; the routing is each layer's own
+    # from the untimed pass, stored per layer.
     L = moe.layer_workspace_layout(mode, T, k, E, H, I)
-    ffn_ws = ws[L["ffn"]:]
-    ids, tw = views["topk_ids"], views["topk_w"]
-    offs, sp, pr, y = views["expert_offsets"], views["sorted_pairs"], views["pair_row"], views["y_pairs"]
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    stage_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    per_layer = []
+    for l in range(n_layers):
+        step(l)                            # layer l with token batch l
+        v = moe.workspace_views(ws, mode, T, k, E, H, I)
+        fws = torch.empty(moe.ffn_workspace_bytes(mode, T, k, H, I), dtype=torch.uint8, device=dev)
+        moe.nvfp4_expert_ffn_stage(layers[l][0], mode, 0, xs[l % n_batches], k, v["expert_offsets"],
+                                   v["sorted_pairs"], v["y_pairs"], fws)
+        n_e = len(np.unique(v["topk_ids"].cpu().numpy()))
+        per_layer.append((v["expert_offsets"].clone(), v["sorted_pairs"].clone(), fws, n_e))
+    y = torch.empty(T * k, H, dtype=torch.float32, device=dev)
 
-    route_ws = torch.empty(moe.lib().moe_route_workspace_bytes(T, E), dtype=torch.uint8, device=dev)
-    out2 = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
-
-    def staged(s, e_pair=None, marks=None):
-        ex, router, bias = layers[s % n_layers]
-        x = xs[s % n_batches]
-        if marks: marks[0].record()
-        moe.moe_route_topk(x, router, k, bias, ids=ids, w=tw, ws=route_ws)
-        if marks: marks[1].record()
-        moe.moe_permute(ids, E, offs, sp, pr)
-        if marks: marks[2].record()
-        moe.nvfp4_expert_ffn_stage(ex, mode, 0, x, k, offs, sp, y, ffn_ws)
-        if e_pair: e_pair[0].record()
-        moe.nvfp4_expert_ffn_stage(ex, mode, 1, x, k, offs, sp, y, ffn_ws)
-        if e_pair: e_pair[1].record()
-        moe.nvfp4_expert_ffn_stage(ex, mode, 2, x, k, offs, sp, y, ffn_ws)
-        if marks: marks[3].record()
-        moe.moe_combine(y, pr, tw, out=out2)
-        if marks: marks[4].record()
+    def gate_up(s):
+        l = s % n_layers
+        off, sp, fws, _ = per_layer[l]
+        moe.nvfp4_expert_ffn_stage(layers[l][0], mode, 1, xs[l % n_batches], k, off, sp, y, fws)
 
     for s in range(warmup):
-        staged(s)
+        gate_up(s)
     torch.cuda.synchronize()
+    ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev2.record()
     for s in range(steps):
-        staged(s, evs[s], stage_ev[s])
+        gate_up(s)
+    ev3.record()
     torch.cuda.synchronize()
-    gu_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    gu_bytes = np.array([combo_gu_bytes[s % combos] for s in range(steps)], np.float64)
-    achieved = float(np.mean(gu_bytes) / (np.mean(gu_ms) * 1e-3) / 1e9)
-    stage_names = ("route", "permute", "experts", "combine")
-    stages = {n: float(np.mean([m[i].elapsed_time(m[i + 1]) for m in stage_ev]) * 1e3)
-              for i, n in enumerate(stage_names)}
-    stages["gate_up_kernel"] = float(np.mean(gu_ms) * 1e3)
+    gu_us = ev2.elapsed_time(ev3) / steps * 1e3
+    gu_bytes = float(np.mean([per_layer[s % n_layers][3] for s in range(steps)])) * (2 * I * H // 2 + 2 * I * H // 16)
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
     return {
         "ms_per_step": ms,
         "gbs": total_bytes / steps / (ms * 1e-3) / 1e9,
         "bytes_per_step": total_bytes / steps,
         "gu_achieved_gbs": achieved,
-        "gu_bytes_per_launch": float(np.mean(gu_bytes)),
-        "gu_us": float(np.mean(gu_ms) * 1e3),
-        "stages_us": stages,
+        "gu_bytes_per_launch": gu_bytes,
+        "gu_us": gu_us,
     }
 
 
 # --------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(w, mode, budget_s=20.0, max_tokens=16):
-    """The oracle on a bounded sample of the workload: whole-layer calls on single tokens."""
+def _pack_one(args):
+    w, e = args
+    from oracle import layer as OL
+    return e, OL.pack_expert(*(synth.expert_matrix(w, 0, e, m) for m in range(3)))
+
+
+def cpu_baseline(w, mode, budget_s=20.0, max_tokens=12):
+    """The oracle on a bounded sample of the workload: whole-layer calls on single
+    tokens of layer 0.  Runs before the GPU is touched; the experts the sample
+    needs are packed first (checkpoint preparation, not timed) in a process pool."""
+    import multiprocessing as mp
     from threadpoolctl import threadpool_limits
     from oracle import layer as OL
     wr = synth.router_weight(w, 0)
     bias = synth.zipf_bias(w)
-    cache = {}
-
-    def get(e):
-        if e not in cache:
-            cache[e] = OL.pack_expert(*(synth.expert_matrix(w, 0, e, m) for m in range(3)))
-        return cache[e]
-
+    xs = [synth.tokens(w, batch=b) for b in range(max_tokens)]
+    need = sorted(set(int(e) for x in xs for e in OL.route(x, wr, w.k, bias).ids.reshape(-1)))
+    # spawn, not fork: the host generator's OpenMP pool is already running here
+    with mp.get_context("spawn").Pool(max(1, min(8, (os.cpu_count() or 2) - 1))) as pool:
+        cache = dict(pool.map(_pack_one, [(w, e) for e in need]))
     done, t_total, bytes_total = 0, 0.0, 0
     with threadpool_limits(limits=1):
-        for b in range(max_tokens):
-            x = synth.tokens(w, batch=b)
-            r = OL.route(x, wr, w.k, bias)
-            for e in np.unique(r.ids):        # packing is checkpoint preparation: not timed
-                get(int(e))
+        for x in xs:
             t0 = time.perf_counter()
-            res = OL.moe_layer(x, wr, w.k, get, mode, bias)
+            res = OL.moe_layer(x, wr, w.k, cache.__getitem__, mode, bias)
             t_total += time.perf_counter() - t0
             bytes_total += touched_bytes(w, res.route.ids)[1]
             done += 1
@@ -211,7 +205,7 @@ def cpu_baseline(w, mode, budget_s=20.0, max_tokens=16):
                 break
     return {"value": bytes_total / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} single-token layer calls (layer 0, token batches 0..{done - 1}), "
-                      f"{t_total:.1f} s of oracle compute, expert packing excluded",
+                      f"{t_total:.1f} s of oracle compute on one core, expert packing excluded",
             "tokens_per_s": done * w.T / t_total}
 
 
@@ -232,14 +226,16 @@ def main(argv=None):
         return 2
     w = synth.CONFIGS[args.workload]
     mode = w.modes[0]
+    cpu = None
+    if not args.no_cpu_baseline:      # host-only, before anything touches the GPU
+        print(f"[bench] cpu baseline: oracle on workload {w.index}", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, mode)
+        print(f"[bench] cpu baseline done: {cpu['value']:.3f} GB/s", file=sys.stderr, flush=True)
     print(f"[bench] workload {w.index} ({w.name}) mode {mode}: building {args.layers} layers",
           file=sys.stderr, flush=True)
     r = run_gpu(w, mode, args.steps, args.warmup, args.layers, args.batches)
     print(f"[bench] gpu done: {r['ms_per_step'] * 1e3:.1f} us/step, {r['gbs']:.0f} GB/s",
           file=sys.stderr, flush=True)
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, mode)
     line = {
         "metric": METRIC,
         "value": round(r["gbs"], 2),
@@ -260,7 +256,6 @@ def main(argv=None):
         "tokens_per_s": round(w.T / (r["ms_per_step"] * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * r["gbs"] / HBM_PEAK_GBS, 2),
         "bytes_per_step": int(r["bytes_per_step"]),
-        "stages_us": {k2: round(v, 2) for k2, v in r["stages_us"].items()},
         "roofline": {"kernel": "k_gateup_narrow (gate/up + SwiGLU)", "bound": "hbm",
                      "achieved": round(r["gu_achieved_gbs"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(r["gu_achieved_gbs"] / HBM_PEAK_GBS, 4),

@@ -144,6 +144,10 @@ class Experts:
         return self.gu_codes.shape[1] // 2
 
     def struct(self):
+        """The C struct (validated once, then cached: the tensors must not be replaced)."""
+        cached = self.__dict__.get("_cstruct")
+        if cached is not None:
+            return cached
         E, H, I = self.E, self.H, self.I
         _need(self.gu_codes, "gu_codes", torch.uint8, (E, 2 * I, H // 2))
         _need(self.gu_scales, "gu_scales", torch.uint8, (E, 2 * I, H // 16))
@@ -155,12 +159,14 @@ class Experts:
             _need(self.gu_inscale, "gu_inscale", torch.float32, (E, 2))
         if self.dn_inscale is not None:
             _need(self.dn_inscale, "dn_inscale", torch.float32, (E,))
-        return _Experts(self.gu_codes.data_ptr(), self.gu_scales.data_ptr(),
-                        self.dn_codes.data_ptr(), self.dn_scales.data_ptr(),
-                        self.gu_wscale.data_ptr(), self.dn_wscale.data_ptr(),
-                        None if self.gu_inscale is None else self.gu_inscale.data_ptr(),
-                        None if self.dn_inscale is None else self.dn_inscale.data_ptr(),
-                        E, H, I)
+        st = _Experts(self.gu_codes.data_ptr(), self.gu_scales.data_ptr(),
+                      self.dn_codes.data_ptr(), self.dn_scales.data_ptr(),
+                      self.gu_wscale.data_ptr(), self.dn_wscale.data_ptr(),
+                      None if self.gu_inscale is None else self.gu_inscale.data_ptr(),
+                      None if self.dn_inscale is None else self.dn_inscale.data_ptr(),
+                      E, H, I)
+        self.__dict__["_cstruct"] = st
+        return st
 
 
 # --------------------------------------------------------------------------- entry points

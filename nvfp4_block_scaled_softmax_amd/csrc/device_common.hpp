@@ -154,6 +154,40 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// DPP lane moves within rows of 16 (gfx9 encodings): xor 1, xor 2, mirror in 8, mirror in 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+// Maximum over the wave, the same value in every lane: DPP within each row of
+// 16 lanes, then the four row results through scalar reads.
+__device__ __forceinline__ float wave_max(float v) {
+  v = __builtin_fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = __builtin_fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = __builtin_fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = __builtin_fmaxf(v, dpp_f32<kDppMirror>(v));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return __builtin_fmaxf(__builtin_fmaxf(r0, r1), __builtin_fmaxf(r2, r3));
+}
+
+// Sum over the wave in a fixed order, the same value in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Index of the s-th expert (0-based) with a non-empty segment, or -1; wave-wide,
 // every lane gets the answer.  offsets has E + 1 entries.
 __device__ __forceinline__ int find_active_expert(const int32_t* offsets, int E, int s) {

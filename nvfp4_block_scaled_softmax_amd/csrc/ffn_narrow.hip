@@ -326,8 +326,9 @@ template <int MODE>
 static moe_status run(const FfnArgs& a, int slots, int stage_mask, hipStream_t s) {
   const int per_col_gu = (a.H / 32) * ChunkLds<MODE>::kStride;
   const int per_col_dn = (a.I / 32) * ChunkLds<MODE>::kStride;
-  const int cols_gu = max(1, min(8, kLdsBudget / per_col_gu));
-  const int cols_dn = max(1, min(8, kLdsBudget / per_col_dn));
+  // an expert has at most T columns; LDS is sized for what a call can need
+  const int cols_gu = max(1, min(min(8, a.T), kLdsBudget / per_col_gu));
+  const int cols_dn = max(1, min(min(8, a.T), kLdsBudget / per_col_dn));
   if (stage_mask & 2) {
     dispatch<MODE, true>(a, a.H, slots, cols_gu, s);
     moe_status st = check_launch("nvfp4_expert_ffn (gate/up)");

@@ -27,24 +27,25 @@ __global__ void __launch_bounds__(256) k_router_logits_narrow(const uint16_t* __
   extern __shared__ __align__(16) uint8_t smem[];
   uint4* xs = reinterpret_cast<uint4*>(smem);       // [T][H/8] chunks of 8 bf16
   const int nch = H / 8;
-  for (int i = threadIdx.x; i < T * nch; i += blockDim.x)
-    xs[i] = reinterpret_cast<const uint4*>(x)[i];
-  __syncthreads();
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int e = blockIdx.x * 4 + wave;
-  if (e >= E) return;
-  const uint4* wrow = reinterpret_cast<const uint4*>(wr + (size_t)e * H);
-  float acc[kNarrowT];
-#pragma unroll
-  for (int t = 0; t < kNarrowT; ++t) acc[t] = 0.0f;
-  // all of this lane's chunks of the row in flight at once (H <= 4096: <= 8 chunks)
+  // this lane's chunks of the router row go out first (H <= 4096: <= 8 chunks),
+  // so their HBM latency overlaps the staging of x
   constexpr int kMaxChunks = kMaxDim / 8 / kWave;
   uint4 wv[kMaxChunks];
+  const uint4* wrow = reinterpret_cast<const uint4*>(wr + (size_t)(e < E ? e : 0) * H);
 #pragma unroll
   for (int j = 0; j < kMaxChunks; ++j) {
     const int c = lane + kWave * j;
     if (c < nch) wv[j] = wrow[c];
   }
+  for (int i = threadIdx.x; i < T * nch; i += blockDim.x)
+    xs[i] = reinterpret_cast<const uint4*>(x)[i];
+  __syncthreads();
+  if (e >= E) return;
+  float acc[kNarrowT];
+#pragma unroll
+  for (int t = 0; t < kNarrowT; ++t) acc[t] = 0.0f;
 #pragma unroll
   for (int j = 0; j < kMaxChunks; ++j) {
     const int c = lane + kWave * j;
@@ -121,9 +122,12 @@ __global__ void __launch_bounds__(256) k_router_logits_mfma(const uint16_t* __re
   }
 }
 
-// One wave per token.  Expert e lives in lane e % 64, slot e / 64.
-constexpr int kMaxSlots = kMaxExperts / kWave;  // 16
-
+// One wave per token.  Lane L holds the S contiguous experts L*S .. L*S+S-1, so
+// among lanes tied on the maximum the lowest lane holds the lowest index.
+// Each round: every lane's best free slot (strict >, so a lane keeps its lowest
+// index among equal values), the wave maximum, the lowest lane holding it;
+// that expert is marked taken.  No branches depend on the data.
+template <int S>
 __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, int T, int E,
                                               int k, int32_t* __restrict__ ids,
                                               float* __restrict__ w) {
@@ -131,43 +135,54 @@ __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, 
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
   const float* row = logits + (size_t)t * E;
-  float v[kMaxSlots];
+  const float ninf = -__builtin_huge_valf();
+  float v[S];
   uint32_t taken = 0u;
 #pragma unroll
-  for (int i = 0; i < kMaxSlots; ++i) {
-    const int e = lane + kWave * i;
-    v[i] = e < E ? row[e] : -__builtin_huge_valf();
-    if (e >= E) taken |= 1u << i;
+  for (int i = 0; i < S; ++i) {
+    const int e = lane * S + i;
+    const float x = row[e < E ? e : E - 1];      // in-bounds load, masked below
+    v[i] = e < E ? x : ninf;
+    taken |= (e < E ? 0u : 1u) << i;
   }
-  float top_v = 0.0f, first_v = 0.0f;
-  int top_id = 0;
+  float sel_v = 0.0f, first_v = 0.0f;
+  int sel_i = 0;
   for (int j = 0; j < k; ++j) {
-    // local best: largest value, lowest expert index on ties (slots ascend in index)
-    float bv = -__builtin_huge_valf();
-    int bi = 0x7FFFFFFF;
+    float bv = ninf;
+    int bs = S;                                   // no free slot
 #pragma unroll
-    for (int i = 0; i < kMaxSlots; ++i) {
-      const bool free_ = !((taken >> i) & 1u);
-      const int e = lane + kWave * i;
-      if (free_ && (v[i] > bv || (v[i] == bv && e < bi))) { bv = v[i]; bi = e; }
+    for (int i = S - 1; i >= 0; --i) {            // descending: ties end on the lowest slot
+      const bool better = !((taken >> i) & 1u) && v[i] >= bv;
+      bv = better ? v[i] : bv;
+      bs = better ? i : bs;
     }
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    if ((bi % kWave) == lane) taken |= 1u << (bi / kWave);
-    if (j == 0) first_v = bv;
-    if (lane == j) { top_v = bv; top_id = bi; }
+    const float m = wave_max(bs < S ? bv : ninf);
+    const unsigned long long hit = __ballot(bs < S && bv == m);
+    const int win_lane = __ffsll((long long)hit) - 1;
+    const int win_slot = __builtin_amdgcn_readlane(bs, win_lane);
+    const int win = win_lane * S + win_slot;
+    if (lane == win_lane) taken |= 1u << win_slot;
+    if (j == 0) first_v = m;
+    sel_v = lane == j ? m : sel_v;
+    sel_i = lane == j ? win : sel_i;
   }
   // renormalised softmax over the chosen logits: exp(l_j - l_max) / sum
-  const float ex = lane < k ? expf(top_v - first_v) : 0.0f;
-  const float sum = group_sum<kWave>(ex);
+  const float ex = lane < k ? expf(sel_v - first_v) : 0.0f;
+  const float sum = wave_sum(ex);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = top_id;
+    ids[(size_t)t * k + lane] = sel_i;
     w[(size_t)t * k + lane] = __fdiv_rn(ex, sum);
   }
+}
+
+static void launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                        hipStream_t s) {
+  const dim3 grid((T + 3) / 4), block(256);
+  if (E <= 64) hipLaunchKernelGGL(k_topk<1>, grid, block, 0, s, logits, T, E, k, ids, w);
+  else if (E <= 128) hipLaunchKernelGGL(k_topk<2>, grid, block, 0, s, logits, T, E, k, ids, w);
+  else if (E <= 256) hipLaunchKernelGGL(k_topk<4>, grid, block, 0, s, logits, T, E, k, ids, w);
+  else if (E <= 512) hipLaunchKernelGGL(k_topk<8>, grid, block, 0, s, logits, T, E, k, ids, w);
+  else hipLaunchKernelGGL(k_topk<16>, grid, block, 0, s, logits, T, E, k, ids, w);
 }
 
 moe_status launch_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T,
@@ -183,7 +198,7 @@ moe_status launch_route(const uint16_t* x, const uint16_t* w_router, const float
   }
   moe_status st = check_launch("moe_route_topk (logits)");
   if (st != MOE_OK) return st;
-  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w);
+  launch_topk(logits, T, E, k, ids, w, s);
   return check_launch("moe_route_topk (top-k)");
 }
 

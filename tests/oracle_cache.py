@@ -1,7 +1,7 @@
 """Oracle-packed experts for the parity tests, built in a process pool.
 
 Packing one full-size expert in the oracle takes ~0.7 s of numpy; the GPU
-tests need tens of them.  The pool is started (fork) by conftest before any
+tests need tens of them.  The pool is started (spawned) by conftest before any
 test initialises the GPU; its workers only run numpy and the host generator.
 """
 from __future__ import annotations
@@ -21,7 +21,7 @@ def start_pool():
     global _POOL
     if _POOL is None:
         n = max(1, min(8, (os.cpu_count() or 2) - 1))
-        _POOL = mp.get_context("fork").Pool(n)
+        _POOL = mp.get_context("spawn").Pool(n)
 
 
 def stop_pool():
