@@ -256,7 +256,8 @@ def main(argv=None):
         "tokens_per_s": round(w.T / (r["ms_per_step"] * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * r["gbs"] / HBM_PEAK_GBS, 2),
         "bytes_per_step": int(r["bytes_per_step"]),
-        "roofline": {"kernel": "k_gateup_narrow (gate/up + SwiGLU)", "bound": "hbm",
+        "roofline": {"kernel": ("k_gateup_wide_a4" if (mode == "A4" and w.T > 8) else "k_gateup_narrow")
+                               + " (gate/up + SwiGLU)", "bound": "hbm",
                      "achieved": round(r["gu_achieved_gbs"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(r["gu_achieved_gbs"] / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": int(r["gu_bytes_per_launch"]),

@@ -1,6 +1,6 @@
 // nvfp4_expert_ffn: activation quantization for the 8/4-bit modes, then the
-// gate/up + SwiGLU and down kernels (narrow path; the MFMA grouped GEMM takes
-// wide 4-bit calls).
+// gate/up + SwiGLU and down kernels: the narrow path for calls of up to 8
+// tokens, the MFMA grouped GEMM for wider 4-bit calls.
 #include "ffn_common.hpp"
 
 namespace moe {
@@ -82,6 +82,8 @@ moe_status launch_expert_ffn(const moe_nvfp4_experts& w, moe_act_mode mode, cons
     moe_status st = check_launch("nvfp4_expert_ffn (x quantization)");
     if (st != MOE_OK) return st;
   }
+  if (mode == MOE_A4 && T > kNarrowMaxT && w.H % 128 == 0 && w.I % 128 == 0)
+    return launch_ffn_wide_a4(a, slots, stage_mask, base + L.plan, s);
   return launch_ffn_narrow(a, mode, slots, stage_mask, s);
 }
 

@@ -27,12 +27,12 @@ struct FfnArgs {
 };
 
 struct FfnLayout {
-  size_t xq_codes, xq_scales, h_codes, h_scales, total;
+  size_t xq_codes, xq_scales, h_codes, h_scales, plan, total;
 };
 
 inline FfnLayout ffn_layout(moe_act_mode mode, int T, int k, int H, int I) {
   const size_t P = (size_t)T * k;
-  FfnLayout L{0, 0, 0, 0, 0};
+  FfnLayout L{0, 0, 0, 0, 0, 0};
   size_t o = 0;
   auto seg = [&](size_t bytes) { const size_t at = o; o = round_up(o + bytes, 256); return at; };
   if (mode == MOE_A16) {
@@ -47,6 +47,7 @@ inline FfnLayout ffn_layout(moe_act_mode mode, int T, int k, int H, int I) {
     L.xq_scales = seg(P * 2 * (H / 16));
     L.h_codes = seg(P * (I / 2));
     L.h_scales = seg(P * (I / 16));
+    L.plan = seg((size_t)kMaxExperts * 16);
   }
   L.total = o;
   return L;
@@ -153,6 +154,10 @@ __device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int 
 
 moe_status launch_ffn_narrow(const FfnArgs& a, moe_act_mode mode, int slots, int stage_mask,
                              hipStream_t s);
-moe_status launch_ffn_wide_a4(const FfnArgs& a, int slots, hipStream_t s);
+moe_status launch_ffn_wide_a4(const FfnArgs& a, int slots, int stage_mask, void* plan_ws,
+                              hipStream_t s);
+
+// Calls with more than this many tokens take the MFMA path (4-bit mode).
+constexpr int kNarrowMaxT = 8;
 
 }  // namespace moe

@@ -316,3 +316,27 @@ def test_layer_is_deterministic(dev):
     a, _ = moe.moe_layer_forward(experts, "A16", x, wr, w.k)
     b, _ = moe.moe_layer_forward(experts, "A16", x, wr, w.k)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("H,I", [(256, 128), (384, 256), (640, 384), (96, 160), (3072, 512)])
+def test_expert_ffn_wide_hot_expert(dev, H, I):
+    """4-bit calls wider than 8 tokens take the MFMA path when H and I are
+    multiples of 128 (K loops of 1-5 and 24 steps), the one-column kernels
+    otherwise (96, 160): one expert with more than 128 tokens (several passes),
+    others with a few, one with none."""
+    E, k, T = 6, 2, 300
+    w = _small_workload(20 + H % 7, E, k, H, I, T)
+    ins = _inscales_for(E, 21)
+    cache = oracle_cache.ExpertCache(w, 0, ins)
+    cache.prefetch(range(E))
+    experts = _upload([cache(e) for e in range(E)], dev, ins)
+    x = synth.tokens(w, batch=5, T=T)
+    rng = np.random.default_rng(22)
+    ids = np.stack([[0, int(rng.choice([1, 2, 3, 5], p=[0.6, 0.3, 0.05, 0.05]))] for _ in range(T)]).astype(np.int32)
+    p = OL.permute(ids, E)
+    assert np.diff(p.offsets)[0] == T and np.diff(p.offsets)[4] == 0
+    say("ffn wide", H, I, np.diff(p.offsets))
+    y, wsb = moe.nvfp4_expert_ffn(experts, "A4", bf16_dev(x, dev), k, to_dev(p.offsets, dev),
+                                  to_dev(p.sorted_pairs, dev))
+    views = {n: host(v) for n, v in moe.ffn_workspace_views(wsb, "A4", T, k, H, I).items()}
+    parity.check_experts(w, "A4", x, cache, k, p.offsets, p.sorted_pairs, host(y), views)
