@@ -159,8 +159,9 @@ moe_status nvfp4_global_scale(const float* x, int n_mat, int64_t mat_elems, floa
  *   A16: h bf16 [P][I]
  *   A8 : x codes [T][H], x scales fp32 [T][H/16], h codes [P][I], h scales fp32 [P][I/16]
  *   A4 : x codes [P][2][H/2], x scales [P][2][H/16] (gate, up), h codes [P][I/2],
- *        h scales [P][I/16], work plan int32 [1024][4] (T > 8 only: active
- *        experts by descending token count, each as expert, first row, rows)  */
+ *        h scales [P][I/16], work plan int32 [min(P, 1024) + P/32][4] (used
+ *        when T > 8: chunks of at most 32 rows of one expert, each as expert,
+ *        first sorted row, rows; unused entries have expert -1)  */
 size_t nvfp4_expert_ffn_workspace_bytes(moe_act_mode mode, int T, int k, int H, int I);
 moe_status nvfp4_expert_ffn(const moe_nvfp4_experts* w, moe_act_mode mode, const uint16_t* x,
                             int T, int k, const int32_t* expert_offsets,

@@ -390,7 +390,8 @@ def ffn_workspace_views(ws, mode, T, k, H, I):
         seg("x_scales", P * 2 * (H // 16), torch.uint8, (P, 2, H // 16))
         seg("h_codes", P * (I // 2), torch.uint8, (P, I // 2))
         seg("h_scales", P * (I // 16), torch.uint8, (P, I // 16))
-        seg("plan", 1024 * 16, torch.int32, (1024, 4))
+        n_plan = min(P, 1024) + P // 32
+        seg("plan", n_plan * 16, torch.int32, (n_plan, 4))
     return out
 
 

@@ -83,7 +83,7 @@ moe_status launch_expert_ffn(const moe_nvfp4_experts& w, moe_act_mode mode, cons
     if (st != MOE_OK) return st;
   }
   if (mode == MOE_A4 && T > kNarrowMaxT && w.H % 128 == 0 && w.I % 128 == 0)
-    return launch_ffn_wide_a4(a, slots, stage_mask, base + L.plan, s);
+    return launch_ffn_wide_a4(a, stage_mask, base + L.plan, s);
   return launch_ffn_narrow(a, mode, slots, stage_mask, s);
 }
 

@@ -47,7 +47,7 @@ inline FfnLayout ffn_layout(moe_act_mode mode, int T, int k, int H, int I) {
     L.xq_scales = seg(P * 2 * (H / 16));
     L.h_codes = seg(P * (I / 2));
     L.h_scales = seg(P * (I / 16));
-    L.plan = seg((size_t)kMaxExperts * 16);
+    L.plan = seg(((P < (size_t)kMaxExperts ? P : (size_t)kMaxExperts) + P / 32) * 16);
   }
   L.total = o;
   return L;
@@ -154,8 +154,9 @@ __device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int 
 
 moe_status launch_ffn_narrow(const FfnArgs& a, moe_act_mode mode, int slots, int stage_mask,
                              hipStream_t s);
-moe_status launch_ffn_wide_a4(const FfnArgs& a, int slots, int stage_mask, void* plan_ws,
-                              hipStream_t s);
+moe_status launch_ffn_wide_a4(const FfnArgs& a, int stage_mask, void* plan_ws, hipStream_t s);
+// Entries of the wide path's work plan for P sorted rows of E experts.
+int wide_plan_entries(int P, int E);
 
 // Calls with more than this many tokens take the MFMA path (4-bit mode).
 constexpr int kNarrowMaxT = 8;

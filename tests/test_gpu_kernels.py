@@ -340,3 +340,11 @@ def test_expert_ffn_wide_hot_expert(dev, H, I):
                                   to_dev(p.sorted_pairs, dev))
     views = {n: host(v) for n, v in moe.ffn_workspace_views(wsb, "A4", T, k, H, I).items()}
     parity.check_experts(w, "A4", x, cache, k, p.offsets, p.sorted_pairs, host(y), views)
+    if H % 128 == 0 and I % 128 == 0:
+        # the work plan: each expert's rows in chunks of at most 32, experts in order
+        want = [(e, r0, min(32, p.offsets[e + 1] - r0)) for e in range(E)
+                for r0 in range(p.offsets[e], p.offsets[e + 1], 32)]
+        plan = views["plan"]
+        assert [tuple(int(v) for v in row[:3]) for row in plan[:len(want)]] == want
+        n_used = min(T * k, E) + T * k // 32            # entries the kernels read
+        assert np.all(plan[len(want):n_used, 0] == -1)
