@@ -108,9 +108,14 @@ moe_status moe_route_topk(const uint16_t* x, const uint16_t* w_router, const flo
  * histogram; sorted_pairs[expert_offsets[e] + r] is the r-th pair of expert e
  * in ascending p; pair_row[p] is the inverse (row of pair p in sorted order).
  * Ids outside [0, E) are dropped: not counted, pair_row[p] = -1, and
- * expert_offsets[E] counts the valid pairs only.  Bit-exact and deterministic. */
+ * expert_offsets[E] counts the valid pairs only.  Bit-exact and deterministic.
+ *   ws: moe_permute_workspace_bytes(T, k, E) bytes, 4-byte aligned (0 bytes, ws
+ *   may be NULL, up to 2048 pairs; more pairs run on several workgroups and
+ *   keep per-block expert counts there).  MOE_E_WORKSPACE if smaller. */
+size_t moe_permute_workspace_bytes(int T, int k, int E);
 moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* expert_offsets,
-                       int32_t* sorted_pairs, int32_t* pair_row, hipStream_t s);
+                       int32_t* sorted_pairs, int32_t* pair_row, void* ws, size_t ws_bytes,
+                       hipStream_t s);
 
 /* ------------------------------------------------------------------ quantizers
  * act_quant_nvfp4: NVFP4 per 16 along a row (the weight format of the page

@@ -23,7 +23,8 @@ DT_BF16, DT_F32 = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_E_ARG", -2: "MOE_E_ALIGN", -3: "MOE_E_SHAPE",
           -4: "MOE_E_UNSUPPORTED", -5: "MOE_E_WORKSPACE", -6: "MOE_E_HIP"}
 
-EXPORTS = ("moe_last_error", "moe_route_workspace_bytes", "moe_route_topk", "moe_permute",
+EXPORTS = ("moe_last_error", "moe_route_workspace_bytes", "moe_route_topk",
+           "moe_permute_workspace_bytes", "moe_permute",
            "act_quant_nvfp4", "act_quant_fp8", "nvfp4_global_scale",
            "nvfp4_expert_ffn_workspace_bytes", "nvfp4_expert_ffn", "nvfp4_expert_ffn_stage",
            "moe_combine",
@@ -60,7 +61,8 @@ def lib():
             "moe_last_error": ([], ctypes.c_char_p),
             "moe_route_workspace_bytes": ([_I, _I], _Z),
             "moe_route_topk": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
-            "moe_permute": ([_P, _I, _I, _I, _P, _P, _P, _P], _I),
+            "moe_permute_workspace_bytes": ([_I, _I, _I], _Z),
+            "moe_permute": ([_P, _I, _I, _I, _P, _P, _P, _P, _Z, _P], _I),
             "act_quant_nvfp4": ([_P, _I, _I, _I, _P, _P, _P, _P, _P], _I),
             "act_quant_fp8": ([_P, _I, _I, _I, _P, _P, _P], _I),
             "nvfp4_global_scale": ([_P, _I, _L, _P, _P], _I),
@@ -196,7 +198,7 @@ def moe_route_topk(x, w_router, k, bias=None, ids=None, w=None, ws=None):
     return ids, w
 
 
-def moe_permute(topk_ids, E, off=None, sp=None, pr=None):
+def moe_permute(topk_ids, E, off=None, sp=None, pr=None, ws=None):
     """Returns (expert_offsets [E+1], sorted_pairs [T*k], pair_row [T*k]), all int32."""
     _need(topk_ids, "topk_ids", torch.int32)
     T, k = topk_ids.shape
@@ -207,8 +209,12 @@ def moe_permute(topk_ids, E, off=None, sp=None, pr=None):
     _need(off, "expert_offsets", torch.int32, (E + 1,))
     _need(sp, "sorted_pairs", torch.int32, (T * k,))
     _need(pr, "pair_row", torch.int32, (T * k,))
+    need = lib().moe_permute_workspace_bytes(T, k, E)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
     _check("moe_permute", lib().moe_permute(_ptr(topk_ids), T, k, E, _ptr(off), _ptr(sp), _ptr(pr),
-                                            _stream()))
+                                            _ptr(ws) if ws is not None else None,
+                                            ws.numel() if ws is not None else 0, _stream()))
     return off, sp, pr
 
 

@@ -45,7 +45,8 @@ inline bool dim_ok(int d) { return d >= 32 && d <= kMaxDim && d % 32 == 0; }
 moe_status launch_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T,
                         int H, int E, int k, int32_t* ids, float* w, float* logits, hipStream_t s);
 moe_status launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
-                          int32_t* sorted_pairs, int32_t* pair_row, hipStream_t s);
+                          int32_t* sorted_pairs, int32_t* pair_row, void* ws, hipStream_t s);
+size_t permute_workspace(int P, int E);
 // stage_mask: bit 0 activation quantization, bit 1 gate/up + SwiGLU, bit 2 down.
 moe_status launch_expert_ffn(const moe_nvfp4_experts& w, moe_act_mode mode, const uint16_t* x,
                              int T, int k, const int32_t* offsets, const int32_t* sorted_pairs,

@@ -40,7 +40,9 @@ static bool layer_layout(moe_act_mode mode, int T, int k, int E, int H, int I, L
   L.pair_row = seg(P * 4);
   L.y = seg(P * H * 4);
   L.ffn = seg(expert_ffn_workspace(mode, T, k, H, I));
-  L.route = seg((size_t)T * E * 4);
+  // router logits, dead after top-k; then the permutation's block counts
+  const size_t route = (size_t)T * E * 4, perm = permute_workspace((int)P, E);
+  L.route = seg(route > perm ? route : perm);
   L.total = o;
   return true;
 }
@@ -100,7 +102,8 @@ extern "C" moe_status moe_layer_forward(const moe_nvfp4_experts* w, moe_act_mode
   if ((st = moe::launch_route(x, w_router, router_bias, T, w->H, w->E, k, ids, tw,
                               reinterpret_cast<float*>(b + L.route), s)) != MOE_OK)
     return st;
-  if ((st = moe::launch_permute(ids, T, k, w->E, offs, sorted, prow, s)) != MOE_OK) return st;
+  if ((st = moe::launch_permute(ids, T, k, w->E, offs, sorted, prow, b + L.route, s)) != MOE_OK)
+    return st;
   if ((st = moe::launch_expert_ffn(*w, mode, x, T, k, offs, sorted, y, b + L.ffn, 7, s)) != MOE_OK)
     return st;
   return moe::launch_combine(y, prow, tw, T, k, w->H, residual, out, s);

@@ -74,51 +74,84 @@ __global__ void __launch_bounds__(256) k_router_logits_narrow(const uint16_t* __
   }
 }
 
-// Wide logits: block = 4 waves = 64 tokens x 64 experts; wave = 32 x 32 (2 x 2 MFMA tiles).
+// Wide logits (prefill): workgroup = 32 tokens x 32 experts, 4 waves splitting
+// K into four ranges; each wave accumulates the whole 32 x 32 tile over its
+// range (2 x 2 MFMA tiles, K 32 per step), keeping three steps of operands in
+// flight in four register sets (the body names each set at a fixed place, so
+// no copy waits on a load; loads past the range re-read its last step).  The
+// four partial tiles meet in LDS and are summed in wave order, so the result
+// does not depend on timing.  Rows past T or E read clamped rows and are not
+// stored.
+constexpr int kRtSets = 4;
+
 __global__ void __launch_bounds__(256) k_router_logits_mfma(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ wr,
                                                             const float* __restrict__ bias,
                                                             int T, int H, int E,
                                                             float* __restrict__ logits) {
-  const int wave = threadIdx.x / kWave, lane = lane_id();
-  const int t0 = blockIdx.y * 64 + (wave >> 1) * 32;
-  const int e0 = blockIdx.x * 64 + (wave & 1) * 32;
+  __shared__ float part[4][32 * 32];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = lane_id();
+  const int t0 = blockIdx.y * 32, e0 = blockIdx.x * 32;
   const int r = lane & 15, g = lane >> 4;
+  const int total = H / 32, per = (total + 3) / 4;
+  const int n = max(0, min(per, total - wave * per));   // this wave's steps (0 for tiny H)
+  const int k_first = n > 0 ? wave * per : 0;             // keeps every read inside its row
+  const uint16_t* xa[2];
+  const uint16_t* wb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    xa[i] = x + (size_t)min(t0 + 16 * i + r, T - 1) * H + 8 * g + 32 * k_first;
+    wb[i] = wr + (size_t)min(e0 + 16 * i + r, E - 1) * H + 8 * g + 32 * k_first;
+  }
   f32x4 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint4 zero = {0u, 0u, 0u, 0u};
-  for (int k0 = 0; k0 < H; k0 += 32) {
-    uint4 a[2], b[2];
+  uint4 fa[kRtSets][2], fb[kRtSets][2];
+  auto load = [&](uint4 (&a)[2], uint4 (&b)[2], int st) {
+    const int k = 32 * min(st, max(n - 1, 0));
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int t = t0 + 16 * i + r;
-      a[i] = t < T ? *reinterpret_cast<const uint4*>(x + (size_t)t * H + k0 + 8 * g) : zero;
-      const int e = e0 + 16 * i + r;
-      b[i] = e < E ? *reinterpret_cast<const uint4*>(wr + (size_t)e * H + k0 + 8 * g) : zero;
+      a[i] = *reinterpret_cast<const uint4*>(xa[i] + k);
+      b[i] = *reinterpret_cast<const uint4*>(wb[i] + k);
     }
+  };
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+  for (int d = 0; d < kRtSets - 1; ++d) load(fa[d], fb[d], d);
+  for (int s0 = 0; s0 < n; s0 += kRtSets) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(a[i]),
-                                                            bitcast<bf16x8>(b[j]), acc[i][j], 0, 0, 0);
+    for (int u = 0; u < kRtSets; ++u) {
+      const int st = s0 + u;
+      load(fa[(u + kRtSets - 1) % kRtSets], fb[(u + kRtSets - 1) % kRtSets], st + kRtSets - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st < n) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                bitcast<bf16x8>(fa[u][i]), bitcast<bf16x8>(fb[u][j]), acc[i][j], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   // C layout: lane holds rows (tokens) 4g + q, column (expert) r of each tile.
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int e = e0 + 16 * j + r;
-    if (e >= E) continue;
-    const float b = bias ? bias[e] : 0.0f;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int t = t0 + 16 * i + 4 * g + q;
-        if (t < T) logits[(size_t)t * E + e] = acc[i][j][q] + b;
-      }
+      for (int q = 0; q < 4; ++q) part[wave][(16 * i + 4 * g + q) * 32 + 16 * j + r] = acc[i][j][q];
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = u * 256 + threadIdx.x;
+    const int t = t0 + idx / 32, e = e0 + idx % 32;
+    if (t < T && e < E) {
+      const float v = ((part[0][idx] + part[1][idx]) + part[2][idx]) + part[3][idx];
+      logits[(size_t)t * E + e] = v + (bias ? bias[e] : 0.0f);
+    }
   }
 }
 
@@ -193,7 +226,7 @@ moe_status launch_route(const uint16_t* x, const uint16_t* w_router, const float
     hipLaunchKernelGGL(k_router_logits_narrow, dim3((E + 3) / 4), dim3(256), lds, s, x, w_router,
                        bias, T, H, E, logits);
   } else {
-    hipLaunchKernelGGL(k_router_logits_mfma, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s,
+    hipLaunchKernelGGL(k_router_logits_mfma, dim3((E + 31) / 32, (T + 31) / 32), dim3(256), 0, s,
                        x, w_router, bias, T, H, E, logits);
   }
   moe_status st = check_launch("moe_route_topk (logits)");

@@ -66,8 +66,15 @@ def test_route_validation():
 
 def test_permute_and_combine_validation():
     L = moe.lib()
-    assert _err(L.moe_permute(P16, 1, 10, 5, P16, P16, P16, None))[0] == "MOE_E_SHAPE"
-    assert _err(L.moe_permute(None, 1, 2, 5, P16, P16, P16, None))[0] == "MOE_E_ARG"
+    assert _err(L.moe_permute(P16, 1, 10, 5, P16, P16, P16, None, 0, None))[0] == "MOE_E_SHAPE"
+    assert _err(L.moe_permute(None, 1, 2, 5, P16, P16, P16, None, 0, None))[0] == "MOE_E_ARG"
+    # up to 2048 pairs one workgroup needs no workspace; more pairs need per-block counts
+    assert L.moe_permute_workspace_bytes(1, 10, 512) == 0
+    assert L.moe_permute_workspace_bytes(204, 10, 512) == 0
+    assert L.moe_permute_workspace_bytes(1024, 10, 512) == 10 * 512 * 4
+    assert L.moe_permute_workspace_bytes(1025, 10, 512) == 11 * 512 * 4
+    code, text = _err(L.moe_permute(P16, 1024, 10, 512, P16, P16, P16, None, 0, None))
+    assert code == "MOE_E_WORKSPACE" and "workspace" in text
     assert _err(L.moe_combine(P16, P16, P16, 1, 2, 3000, None, P16, None))[0] == "MOE_E_SHAPE"
     assert _err(L.moe_combine(P16, P16, P16, 1, 2, 3072, ctypes.c_void_p(4098), P16, None))[0] == "MOE_E_ALIGN"
 

@@ -182,6 +182,19 @@ def test_route_matches_oracle(dev, wi, T):
     assert len(flipped) <= max(1, T // 100), flipped
 
 
+@pytest.mark.parametrize("T,H,E,k", [(45, 32, 40, 3), (45, 64, 40, 3), (70, 96, 33, 5), (33, 4096, 97, 8)])
+def test_route_wide_ragged(dev, T, H, E, k):
+    """T > 8 takes the MFMA logits kernel: ragged token and expert tiles, K ranges
+    shorter than the four-way split (H = 32, 64, 96), and the largest H."""
+    rng = np.random.default_rng(T + H + E)
+    x = F.f64_to_bf16(rng.standard_normal((T, H)))
+    wr = F.f64_to_bf16(rng.standard_normal((E, H)) / np.sqrt(H))
+    say("route wide", T, H, E, k)
+    ids, tw = moe.moe_route_topk(bf16_dev(x, dev), bf16_dev(wr, dev), k)
+    r, flipped = parity.check_route(x, wr, None, k, host(ids), host(tw))
+    assert len(flipped) <= 1, flipped
+
+
 def test_route_ties_and_small_k(dev):
     # equal logits: ids 0..k-1 in order, uniform weights
     x = np.zeros((3, 256), np.uint16)
@@ -197,7 +210,7 @@ def test_route_ties_and_small_k(dev):
 
 # --------------------------------------------------------------------------- permute
 @pytest.mark.parametrize("T,k,E", [(1, 10, 512), (8, 10, 512), (2, 10, 512), (1024, 10, 512),
-                                   (33, 2, 8), (3000, 8, 1024), (7, 1, 1)])
+                                   (33, 2, 8), (3000, 8, 1024), (7, 1, 1), (257, 8, 64), (1024, 10, 512)])
 def test_permute_matches_oracle(dev, T, k, E):
     rng = np.random.default_rng(T * 1000 + k * 10 + E)
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
@@ -218,6 +231,28 @@ def test_permute_drops_invalid_ids(dev):
     assert host(off).tolist() == [0, 2, 3, 3, 4, 4, 6]
     assert host(sp)[:6].tolist() == [0, 7, 3, 6, 1, 5]
     assert host(pr).tolist() == [0, 4, -1, 2, -1, 5, 3, 1]
+
+
+def test_permute_multiblock_invalid_ids(dev):
+    """More than 2048 pairs (the several-workgroup path) with out-of-range ids
+    scattered over the blocks, including a block boundary."""
+    rng = np.random.default_rng(77)
+    T, k, E = 700, 4, 96
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    bad = rng.choice(T * k, 40, replace=False)
+    ids.reshape(-1)[bad] = rng.choice([-1, E, E + 7, -5], 40)
+    ids.reshape(-1)[1023:1026] = -1
+    off, sp, pr = moe.moe_permute(to_dev(ids, dev), E)
+    # expected: the stable sort of the valid pairs only; dropped pairs get row -1
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    want_off = np.concatenate([[0], np.cumsum(np.bincount(flat[valid], minlength=E))])
+    order = np.flatnonzero(valid)[np.argsort(flat[valid], kind="stable")]
+    want_pr = np.full(flat.size, -1)
+    want_pr[order] = np.arange(order.size)
+    assert np.array_equal(host(off), want_off)
+    assert np.array_equal(host(sp)[:order.size], order)
+    assert np.array_equal(host(pr), want_pr)
 
 
 # --------------------------------------------------------------------------- combine
