@@ -99,7 +99,7 @@ def run_gpu(w, mode, steps, warmup, n_layers, n_batches):
     del bufs
     torch.cuda.empty_cache()
     xs = [token_batch(w, b, dev) for b in range(n_batches)]
-    ws = torch.empty(moe.layer_workspace_bytes(mode, T, k, E, H, I), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(moe.layer_workspace_bytes(mode, T, k, E, H, I), dtype=torch.uint8, device=dev)
     out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
     combos = n_layers * n_batches // np.gcd(n_layers, n_batches)
 

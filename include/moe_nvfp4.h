@@ -195,7 +195,11 @@ moe_status moe_combine(const float* y_pairs, const int32_t* pair_row, const floa
  * moe_layer_forward: route -> permute -> experts -> combine on one stream.
  *   out [T][H] bf16 = the layer output, or bf16(residual + output) when
  *   residual is not NULL (residual may equal x; out must not alias x).
- *   ws: moe_layer_workspace_bytes(mode, T, k, E, H, I) bytes, 16-byte aligned.
+ *   ws: moe_layer_workspace_bytes(mode, T, k, E, H, I) bytes, 256-byte aligned,
+ *   zero-filled before its first use: up to 8 tokens the layer runs fused (the
+ *   routing in one launch, the experts with the combine in another) and keeps
+ *   inter-workgroup counters in the workspace, which every call leaves at zero.
+ *   Calls sharing a workspace must not overlap.
  *   moe_layer_workspace_layout fills offsets[7] (bytes into ws) of topk_ids
  *   [T][k] int32, topk_w [T][k] fp32, expert_offsets [E+1] int32, sorted_pairs
  *   [T*k] int32, pair_row [T*k] int32, y_pairs [T*k][H] fp32, and the expert
@@ -203,6 +207,10 @@ moe_status moe_combine(const float* y_pairs, const int32_t* pair_row, const floa
  * Returns MOE_E_SHAPE from the layout call for sizes out of range. */
 moe_status moe_layer_workspace_layout(moe_act_mode mode, int T, int k, int E, int H, int I,
                                       size_t offsets[7]);
+/* Byte offset in a layer workspace of a uint32 that counts waits of the fused
+ * decode path which reached their bound (a stalled producer); it stays 0 in
+ * correct operation and is meant for tests and health checks. */
+size_t moe_layer_wait_timeouts_offset(void);
 size_t moe_layer_workspace_bytes(moe_act_mode mode, int T, int k, int E, int H, int I);
 moe_status moe_layer_forward(const moe_nvfp4_experts* w, moe_act_mode mode, const uint16_t* x,
                              const uint16_t* w_router, const float* router_bias, int T, int k,

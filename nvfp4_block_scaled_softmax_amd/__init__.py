@@ -28,7 +28,8 @@ EXPORTS = ("moe_last_error", "moe_route_workspace_bytes", "moe_route_topk",
            "act_quant_nvfp4", "act_quant_fp8", "nvfp4_global_scale",
            "nvfp4_expert_ffn_workspace_bytes", "nvfp4_expert_ffn", "nvfp4_expert_ffn_stage",
            "moe_combine",
-           "moe_layer_workspace_bytes", "moe_layer_workspace_layout", "moe_layer_forward")
+           "moe_layer_workspace_bytes", "moe_layer_workspace_layout", "moe_layer_wait_timeouts_offset",
+           "moe_layer_forward")
 
 
 class MoeError(RuntimeError):
@@ -72,6 +73,7 @@ def lib():
             "moe_combine": ([_P, _P, _P, _I, _I, _I, _P, _P, _P], _I),
             "moe_layer_workspace_bytes": ([_I, _I, _I, _I, _I, _I], _Z),
             "moe_layer_workspace_layout": ([_I, _I, _I, _I, _I, _I, ctypes.POINTER(_Z)], _I),
+            "moe_layer_wait_timeouts_offset": ([], _Z),
             "moe_layer_forward": ([ctypes.POINTER(_Experts), _I, _P, _P, _P, _I, _I, _P, _P, _P, _Z, _P], _I),
         }
         for name, (args, res) in sig.items():
@@ -326,7 +328,9 @@ def layer_workspace_layout(mode, T, k, E, H, I):
 
 def moe_layer_forward(experts: Experts, mode, x, w_router, k, bias=None, residual=None, ws=None,
                       out=None):
-    """The whole layer on the current stream.  Returns (out bf16 [T, H], workspace)."""
+    """The whole layer on the current stream.  Returns (out bf16 [T, H], workspace).
+    A workspace passed in must have been zero-filled before its first use (the
+    library leaves it ready for the next call)."""
     x = _bf16(x, "x")
     _need(x, "x")
     T, H = x.shape
@@ -341,13 +345,19 @@ def moe_layer_forward(experts: Experts, mode, x, w_router, k, bias=None, residua
         _need(residual, "residual", shape=(T, H))
     nws = layer_workspace_bytes(m, T, k, experts.E, H, experts.I)
     if ws is None:
-        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=x.device)
+        ws = torch.zeros(max(nws, 16), dtype=torch.uint8, device=x.device)
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
     _check("moe_layer_forward", lib().moe_layer_forward(ctypes.byref(s), m, _ptr(x), _ptr(w_router),
                                                         _ptr(bias), T, k, _ptr(residual), _ptr(out),
                                                         _ptr(ws), ws.numel(), _stream()))
     return out, ws
+
+
+def layer_wait_timeouts(ws):
+    """Waits of the fused decode path that reached their bound (0 in correct operation)."""
+    o = lib().moe_layer_wait_timeouts_offset()
+    return int(ws[o:o + 4].view(torch.int32).item())
 
 
 def workspace_views(ws, mode, T, k, E, H, I):

@@ -55,5 +55,15 @@ moe_status launch_combine(const float* y_pairs, const int32_t* pair_row, const f
                           int T, int k, int H, const uint16_t* residual, uint16_t* out,
                           hipStream_t s);
 size_t expert_ffn_workspace(moe_act_mode mode, int T, int k, int H, int I);
+// The fused decode layer (T <= 8): routing in one launch, experts + combine in
+// another; its counter block must start at zero and is left at zero.
+size_t decode_state_bytes();
+size_t decode_timeouts_offset();
+bool decode_fusable(int T, int H, int I);
+moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, const uint16_t* x,
+                               const uint16_t* w_router, const float* bias, int T, int k,
+                               const uint16_t* residual, uint16_t* out, int32_t* ids, float* tw,
+                               int32_t* offsets, int32_t* sorted, int32_t* prow, float* y,
+                               float* logits, void* ffn_ws, void* state, hipStream_t s);
 
 }  // namespace moe

@@ -4,7 +4,7 @@
 // row's 128-bit load is issued before the sum, then one 64-bit store.  No atomics: the order of the sum
 // is fixed, so results are bitwise reproducible.
 #include "abi_common.hpp"
-#include "device_common.hpp"
+#include "combine_common.hpp"
 
 namespace moe {
 
@@ -17,40 +17,8 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y,
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)T * n4) return;
   const int t = (int)(i / n4), c = (int)(i % n4);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  constexpr int U = 8;
-  for (int j0 = 0; j0 < k; j0 += U) {
-    int r[U];
-    float wj[U];
-    float4 yv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + u;
-      r[u] = j < k ? pair_row[(size_t)t * k + j] : -1;
-      wj[u] = j < k ? w[(size_t)t * k + j] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      yv[u] = r[u] >= 0 ? reinterpret_cast<const float4*>(y + (size_t)r[u] * H)[c]
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {   // j ascending
-      acc.x += wj[u] * yv[u].x;
-      acc.y += wj[u] * yv[u].y;
-      acc.z += wj[u] * yv[u].z;
-      acc.w += wj[u] * yv[u].w;
-    }
-  }
-  uint32_t o0 = f32_to_bf16(acc.x), o1 = f32_to_bf16(acc.y);
-  uint32_t o2 = f32_to_bf16(acc.z), o3 = f32_to_bf16(acc.w);
-  if (residual) {
-    const uint2 rr = *reinterpret_cast<const uint2*>(residual + (size_t)t * H + (size_t)c * 4);
-    o0 = f32_to_bf16(bf16_to_f32(rr.x & 0xFFFFu) + bf16_to_f32(o0));
-    o1 = f32_to_bf16(bf16_to_f32(rr.x >> 16) + bf16_to_f32(o1));
-    o2 = f32_to_bf16(bf16_to_f32(rr.y & 0xFFFFu) + bf16_to_f32(o2));
-    o3 = f32_to_bf16(bf16_to_f32(rr.y >> 16) + bf16_to_f32(o3));
-  }
-  *reinterpret_cast<uint2*>(out + (size_t)t * H + (size_t)c * 4) = make_uint2(o0 | (o1 << 16), o2 | (o3 << 16));
+  *reinterpret_cast<uint2*>(out + (size_t)t * H + (size_t)c * 4) =
+      combine4(y, pair_row, w, t, k, H, c, residual);
 }
 
 moe_status launch_combine(const float* y_pairs, const int32_t* pair_row, const float* topk_w,

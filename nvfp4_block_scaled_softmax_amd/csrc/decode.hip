@@ -1,0 +1,276 @@
+// Fused decode layer (T <= 8 tokens): the routed-expert layer in two launches
+// instead of six.
+//
+//   A  k_route_decode:   router logits (one wave per expert row); the last
+//                        workgroup to finish runs top-k, the stable
+//                        permutation and the list of active experts.
+//   B  k_experts_decode: gate/up + SwiGLU tiles, down tiles and the combine.
+//                        A down tile issues its weight loads at once and then
+//                        waits for its expert's gate/up tiles, so the down
+//                        weights stream while gate/up computes; the last down
+//                        tile of each output-row block sums the token's expert
+//                        outputs (and the residual) for those rows.
+//
+// The arithmetic is the per-stage kernels' own (shared device functions), so
+// the fused layer is bit-identical to moe_route_topk + moe_permute +
+// nvfp4_expert_ffn + moe_combine.
+//
+// Ordering between workgroups.  In B, gate/up tiles have the lower workgroup
+// indices and down tiles the higher ones.  Workgroups are dispatched in index
+// order (round-robin over the XCDs, in order within each), so every gate/up
+// tile is resident or done before a down tile that could wait for it takes a
+// slot: the waits cannot starve the tiles they wait for.  (A ticket from one
+// shared atomic counter would not need that order, but 800 workgroups
+// serialised on one counter cost more than the whole expert pass.)  Waits are
+// bounded by a spin cap, so every wave exits whatever happens; a wait that
+// reaches the cap is counted in the state block, where tests check it.  The data handed between
+// workgroups (logits, h, y) crosses XCDs, whose L2s are not coherent with
+// each other: it is written and read with device-coherent (sc1) buffer
+// accesses that pass the XCD-local caches; a producer waits for its stores to
+// complete before its workgroup bumps the counter, and consumers poll the
+// counter with relaxed device-scope loads.  No L2 write-back or invalidate is
+// needed.
+//
+// The counters live in a small state block of the layer workspace.  It must be
+// zero before the first call; A's last workgroup clears B's counters and then
+// its own, so every call finds them at zero.
+#include "combine_common.hpp"
+#include "ffn_narrow.hpp"
+#include "permute_common.hpp"
+#include "route_common.hpp"
+
+namespace moe {
+
+constexpr int kDecMaxSlots = 512;     // active experts of a call: at most T * k <= 8 * 64
+constexpr int kDecMaxRowBlocks = kMaxDim / kDnRows;
+constexpr uint32_t kSpinCap = 1u << 22;
+
+// Each counter sits on its own 128-byte line: many workgroups poll or bump them
+// at once, and counters sharing a line would queue behind each other.
+struct alignas(128) Counter {
+  uint32_t v;
+  uint32_t pad[31];
+};
+
+struct DecodeState {
+  Counter route_done;                  // A: workgroups finished
+  Counter timeouts;                    // waits that reached the spin cap (stays 0)
+  int32_t n_active;                    // active experts (written by A)
+  Counter gu_done[kDecMaxSlots];       // B: gate/up tiles finished, per active expert
+  Counter dn_done[kDecMaxRowBlocks];   // B: down tiles finished, per output-row block
+  int4 plan[kDecMaxSlots];             // active expert: (expert, first sorted row, rows, 0)
+};
+
+size_t decode_state_bytes() { return sizeof(DecodeState); }
+size_t decode_timeouts_offset() { return offsetof(DecodeState, timeouts); }
+
+__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Thread 0 waits (bounded) until *p >= want; the data behind the count is
+// then read with device-coherent loads.
+__device__ __forceinline__ void wait_at_least(const uint32_t* p, uint32_t want, uint32_t* timeouts) {
+  if (threadIdx.x == 0) {
+    uint32_t it = 0;
+    while (ld_relaxed(p) < want && ++it < kSpinCap) __builtin_amdgcn_s_sleep(8);
+    if (it >= kSpinCap) __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ A: routing
+// 8 waves, one expert row each.  Dynamic LDS: x of the T tokens.
+template <int S>
+__global__ void __launch_bounds__(kPermThreads)
+    k_route_decode(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                   const float* __restrict__ bias, int T, int H, int E, int k,
+                   float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ tw,
+                   int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
+                   int32_t* __restrict__ pair_row, DecodeState* __restrict__ st) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int base[kMaxExperts];
+  __shared__ int rank[kMaxExperts];
+  __shared__ int wcnt[kPermWaves][kMaxExperts];
+  __shared__ int wave_tot[kPermWaves];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, wave = tid / kWave;
+  router_logits_wave<true>(x, wr, bias, T, H, E, blockIdx.x * kPermWaves + wave,
+                           reinterpret_cast<uint4*>(smem), logits);
+  wait_vmem();   // this wave's logits have reached the device-coherent level
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t done =
+        __hip_atomic_fetch_add(&st->route_done.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = done == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // ---- the last workgroup: every expert's logits are visible
+  for (int t = wave; t < T; t += kPermWaves) topk_wave<S, true>(logits, t, E, k, ids, tw);
+  for (int e = tid; e < E; e += kPermThreads) {
+    cnt[e] = 0;
+#pragma unroll
+    for (int w = 0; w < kPermWaves; ++w) wcnt[w][e] = 0;
+  }
+  __syncthreads();   // ids are written (same workgroup)
+  const int P = T * k;
+  for (int p = tid; p < P; p += kPermThreads) atomicAdd(&cnt[ids[p]], 1);
+  __syncthreads();
+  const int total = scan_experts(cnt, base, E, wave_tot);
+  for (int e = tid; e < E; e += kPermThreads) offsets[e] = base[e];
+  if (tid == 0) offsets[E] = total;
+  // active experts in ascending order: a second scan, over the 0/1 flags
+  for (int e = tid; e < E; e += kPermThreads) rank[e] = cnt[e] > 0;
+  __syncthreads();
+  const int n_active = scan_experts(rank, rank, E, wave_tot);
+  for (int e = tid; e < E; e += kPermThreads)
+    if (cnt[e] > 0) st->plan[rank[e]] = make_int4(e, base[e], cnt[e], 0);
+  if (tid == 0) st->n_active = n_active;
+  scatter_range(ids, 0, P, E, base, wcnt, sorted_pairs, pair_row);
+  // B's counters start at zero: the previous call's B has finished (it ran
+  // before this kernel on the stream); clear what it may have counted
+  for (int i = tid; i < kDecMaxSlots; i += kPermThreads) st->gu_done[i].v = 0u;
+  for (int i = tid; i < kDecMaxRowBlocks; i += kPermThreads) st->dn_done[i].v = 0u;
+  if (tid == 0) __hip_atomic_store(&st->route_done.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------ B: experts
+// Workgroups [0, G): gate/up tile (slot, rb) = (i / nrb_gu, i % nrb_gu);
+// workgroups [G, G + D): down tile of (slot, rb) likewise with nrb_dn.  Slots
+// past the active count exit at once.
+template <int MODE, int GL, int GC, int DL, int DC>
+__global__ void __launch_bounds__(256)
+    k_experts_decode(FfnArgs a, DecodeState* __restrict__ st, int max_slots, int cols_gu,
+                     int cols_dn, const int32_t* __restrict__ pair_row,
+                     const float* __restrict__ tw, const uint16_t* __restrict__ residual,
+                     uint16_t* __restrict__ out) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int s_flag;
+  const int tid = threadIdx.x;
+  const int wg = blockIdx.x;
+  const int n_active = st->n_active;
+  const int nrb_gu = a.I / kGuRows, nrb_dn = (a.H + kDnRows - 1) / kDnRows;
+  const int G = max_slots * nrb_gu;
+  if (wg < G) {
+    const int slot = wg / nrb_gu, rb = wg % nrb_gu;
+    if (slot < n_active) {
+      const int4 pl = st->plan[slot];
+      gateup_tile<MODE, GL, GC, true>(a, pl.x, pl.y, pl.z, rb, cols_gu, lds);
+      wait_vmem();   // this wave's h has reached the device-coherent level
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_fetch_add(&st->gu_done[slot].v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else {
+    const int d = wg - G, slot = d / nrb_dn, rb = d % nrb_dn;
+    if (slot < n_active) {
+      const int4 pl = st->plan[slot];
+      down_tile<MODE, DL, DC, true>(a, pl.x, pl.y, pl.z, rb, cols_dn, lds,
+                                    [&] { wait_at_least(&st->gu_done[slot].v, (uint32_t)nrb_gu, &st->timeouts.v); });
+      wait_vmem();   // this wave's y has reached the device-coherent level
+      __syncthreads();
+      if (tid == 0) {
+        const uint32_t c =
+            __hip_atomic_fetch_add(&st->dn_done[rb].v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_flag = c == (uint32_t)n_active - 1;
+      }
+      __syncthreads();
+      if (s_flag) {   // every expert's rows of this block are in: combine them
+        const int n4 = kDnRows / 4, c0 = rb * n4;
+        for (int i = tid; i < a.T * n4; i += blockDim.x) {
+          const int t = i / n4, c = c0 + i % n4;
+          if (4 * c < a.H)
+            *reinterpret_cast<uint2*>(out + (size_t)t * a.H + (size_t)c * 4) =
+                combine4<true>(a.y, pair_row, tw, t, a.k, a.H, c, residual);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launch
+template <int S>
+static void launch_a(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E,
+                     int k, float* logits, int32_t* ids, float* tw, int32_t* offsets,
+                     int32_t* sorted, int32_t* prow, DecodeState* st, hipStream_t s) {
+  hipLaunchKernelGGL(k_route_decode<S>, dim3((E + kPermWaves - 1) / kPermWaves), dim3(kPermThreads),
+                     (size_t)T * H * 2, s, x, wr, bias, T, H, E, k, logits, ids, tw, offsets,
+                     sorted, prow, st);
+}
+
+// (lanes per row, chunks per lane) of the narrow tiles for a reduction of NC
+// 32-wide chunks, as the per-stage kernels choose them; the fused kernel is
+// built for gate/up with 33..128 chunks and down with 5..32 chunks.
+static int gu_config(int nc) { return nc <= 32 ? -1 : nc <= 64 ? 2 : nc <= 96 ? 3 : nc <= 128 ? 4 : -1; }
+static int dn_config(int nc) { return nc <= 4 ? -1 : nc <= 8 ? 8 : nc <= 16 ? 16 : nc <= 32 ? 32 : -1; }
+
+bool decode_fusable(int T, int H, int I) {
+  return T <= kNarrowT && gu_config(H / 32) > 0 && dn_config(I / 32) > 0;
+}
+
+template <int MODE, int GC, int DL>
+static void launch_b3(const FfnArgs& a, DecodeState* st, int max_slots, int cols_gu, int cols_dn,
+                      const int32_t* prow, const float* tw, const uint16_t* residual,
+                      uint16_t* out, hipStream_t s) {
+  const int grid = max_slots * (a.I / kGuRows + (a.H + kDnRows - 1) / kDnRows);
+  const size_t lds_gu = (size_t)cols_gu * (a.H / 32) * ChunkLds<MODE>::kStride;
+  const size_t lds_dn = (size_t)cols_dn * (a.I / 32) * ChunkLds<MODE>::kStride;
+  hipLaunchKernelGGL((k_experts_decode<MODE, 32, GC, DL, 1>), dim3(grid), dim3(256),
+                     lds_gu > lds_dn ? lds_gu : lds_dn, s, a, st, max_slots, cols_gu, cols_dn, prow,
+                     tw, residual, out);
+}
+
+template <int MODE, int GC>
+static void launch_b2(const FfnArgs& a, int dl, DecodeState* st, int max_slots, int cols_gu,
+                      int cols_dn, const int32_t* prow, const float* tw, const uint16_t* residual,
+                      uint16_t* out, hipStream_t s) {
+  if (dl == 8) launch_b3<MODE, GC, 8>(a, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, s);
+  else if (dl == 16) launch_b3<MODE, GC, 16>(a, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, s);
+  else launch_b3<MODE, GC, 32>(a, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, s);
+}
+
+template <int MODE>
+static void launch_b(const FfnArgs& a, DecodeState* st, int max_slots, const int32_t* prow,
+                     const float* tw, const uint16_t* residual, uint16_t* out, hipStream_t s) {
+  // column groups as the per-stage kernels size them
+  const int per_col_gu = (a.H / 32) * ChunkLds<MODE>::kStride;
+  const int per_col_dn = (a.I / 32) * ChunkLds<MODE>::kStride;
+  const int cols_gu = max(1, min(min(8, a.T), kLdsBudget / per_col_gu));
+  const int cols_dn = max(1, min(min(8, a.T), kLdsBudget / per_col_dn));
+  const int gc = gu_config(a.H / 32), dl = dn_config(a.I / 32);
+  if (gc == 2) launch_b2<MODE, 2>(a, dl, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, s);
+  else if (gc == 3) launch_b2<MODE, 3>(a, dl, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, s);
+  else launch_b2<MODE, 4>(a, dl, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, s);
+}
+
+moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, const uint16_t* x,
+                               const uint16_t* w_router, const float* bias, int T, int k,
+                               const uint16_t* residual, uint16_t* out, int32_t* ids, float* tw,
+                               int32_t* offsets, int32_t* sorted, int32_t* prow, float* y,
+                               float* logits, void* ffn_ws, void* state, hipStream_t s) {
+  DecodeState* st = static_cast<DecodeState*>(state);
+  const int E = w.E, H = w.H;
+  if (E <= 64) launch_a<1>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
+  else if (E <= 128) launch_a<2>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
+  else if (E <= 256) launch_a<4>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
+  else if (E <= 512) launch_a<8>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
+  else launch_a<16>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
+  moe_status r = check_launch("moe_layer_forward (decode routing)");
+  if (r != MOE_OK) return r;
+  if (mode != MOE_A16) {   // activation quantization needs the permutation (4-bit: per pair)
+    r = launch_expert_ffn(w, mode, x, T, k, offsets, sorted, y, ffn_ws, 1, s);
+    if (r != MOE_OK) return r;
+  }
+  const FfnArgs a = make_ffn_args(w, mode, x, T, k, offsets, sorted, y, ffn_ws);
+  const int P = T * k, max_slots = P < E ? P : E;
+  switch (mode) {
+    case MOE_A16: launch_b<MOE_A16>(a, st, max_slots, prow, tw, residual, out, s); break;
+    case MOE_A8: launch_b<MOE_A8>(a, st, max_slots, prow, tw, residual, out, s); break;
+    default: launch_b<MOE_A4>(a, st, max_slots, prow, tw, residual, out, s); break;
+  }
+  return check_launch("moe_layer_forward (decode experts)");
+}
+
+}  // namespace moe

@@ -234,4 +234,74 @@ __device__ __forceinline__ int find_active_expert(const int32_t* offsets, int E,
   return -1;
 }
 
+
+// ---------------------------------------------------------------------------
+// Accesses for data one workgroup hands to another within a kernel.  The L2s
+// of the XCDs are not coherent with each other; with COH these go through
+// buffer instructions whose cache policy (sc1, device scope) writes through /
+// reads past the XCD-local caches, so the handoff needs no L2 write-back or
+// invalidate.  Without COH they are plain accesses.  base must be
+// wave-uniform; byte offsets stay below 2^31.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coh_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+constexpr int kCohPolicy = 16;   // sc1
+
+template <bool COH>
+__device__ __forceinline__ void hst8(void* base, size_t off, uint8_t v) {
+  if constexpr (COH) __builtin_amdgcn_raw_buffer_store_b8(v, coh_rsrc(base), (int)off, 0, kCohPolicy);
+  else static_cast<uint8_t*>(base)[off] = v;
+}
+template <bool COH>
+__device__ __forceinline__ void hst16(void* base, size_t off, uint16_t v) {
+  if constexpr (COH) __builtin_amdgcn_raw_buffer_store_b16(v, coh_rsrc(base), (int)off, 0, kCohPolicy);
+  else *reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(base) + off) = v;
+}
+template <bool COH>
+__device__ __forceinline__ void hst32(void* base, size_t off, uint32_t v) {
+  if constexpr (COH) __builtin_amdgcn_raw_buffer_store_b32(v, coh_rsrc(base), (int)off, 0, kCohPolicy);
+  else *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(base) + off) = v;
+}
+template <bool COH>
+__device__ __forceinline__ void hst64(void* base, size_t off, uint2 v) {
+  typedef unsigned v2u __attribute__((ext_vector_type(2)));
+  if constexpr (COH)
+    __builtin_amdgcn_raw_buffer_store_b64(v2u{v.x, v.y}, coh_rsrc(base), (int)off, 0, kCohPolicy);
+  else *reinterpret_cast<uint2*>(static_cast<uint8_t*>(base) + off) = v;
+}
+template <bool COH>
+__device__ __forceinline__ void hst128(void* base, size_t off, uint4 v) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  if constexpr (COH)
+    __builtin_amdgcn_raw_buffer_store_b128(v4u{v.x, v.y, v.z, v.w}, coh_rsrc(base), (int)off, 0, kCohPolicy);
+  else *reinterpret_cast<uint4*>(static_cast<uint8_t*>(base) + off) = v;
+}
+template <bool COH>
+__device__ __forceinline__ uint16_t hld16(const void* base, size_t off) {
+  if constexpr (COH) return __builtin_amdgcn_raw_buffer_load_b16(coh_rsrc(base), (int)off, 0, kCohPolicy);
+  else return *reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(base) + off);
+}
+template <bool COH>
+__device__ __forceinline__ uint32_t hld32(const void* base, size_t off) {
+  if constexpr (COH) return __builtin_amdgcn_raw_buffer_load_b32(coh_rsrc(base), (int)off, 0, kCohPolicy);
+  else return *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(base) + off);
+}
+template <bool COH>
+__device__ __forceinline__ uint2 hld64(const void* base, size_t off) {
+  if constexpr (COH) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(coh_rsrc(base), (int)off, 0, kCohPolicy));
+  } else {
+    return *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + off);
+  }
+}
+template <bool COH>
+__device__ __forceinline__ uint4 hld128(const void* base, size_t off) {
+  if constexpr (COH) return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(coh_rsrc(base), (int)off, 0, kCohPolicy));
+  else return *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(base) + off);
+}
+
+// Waits until every vector memory access this wave issued has completed
+// (s_waitcnt vmcnt(0); the other counters untouched).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 }  // namespace moe

@@ -42,9 +42,9 @@ size_t expert_ffn_workspace(moe_act_mode mode, int T, int k, int H, int I) {
   return ffn_layout(mode, T, k, H, I).total;
 }
 
-moe_status launch_expert_ffn(const moe_nvfp4_experts& w, moe_act_mode mode, const uint16_t* x,
-                             int T, int k, const int32_t* offsets, const int32_t* sorted_pairs,
-                             float* y_pairs, void* ws, int stage_mask, hipStream_t s) {
+FfnArgs make_ffn_args(const moe_nvfp4_experts& w, moe_act_mode mode, const uint16_t* x, int T,
+                      int k, const int32_t* offsets, const int32_t* sorted_pairs, float* y_pairs,
+                      void* ws) {
   const FfnLayout L = ffn_layout(mode, T, k, w.H, w.I);
   uint8_t* base = static_cast<uint8_t*>(ws);
   FfnArgs a;
@@ -69,6 +69,15 @@ moe_status launch_expert_ffn(const moe_nvfp4_experts& w, moe_act_mode mode, cons
   a.h_codes = base + L.h_codes;
   a.h_scales = mode == MOE_A16 ? nullptr : base + L.h_scales;
   a.y = y_pairs;
+  return a;
+}
+
+moe_status launch_expert_ffn(const moe_nvfp4_experts& w, moe_act_mode mode, const uint16_t* x,
+                             int T, int k, const int32_t* offsets, const int32_t* sorted_pairs,
+                             float* y_pairs, void* ws, int stage_mask, hipStream_t s) {
+  const FfnLayout L = ffn_layout(mode, T, k, w.H, w.I);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const FfnArgs a = make_ffn_args(w, mode, x, T, k, offsets, sorted_pairs, y_pairs, ws);
   const int P = T * k;
   const int slots = P < w.E ? P : w.E;
 

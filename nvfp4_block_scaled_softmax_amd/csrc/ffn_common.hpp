@@ -154,6 +154,10 @@ __device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int 
 
 moe_status launch_ffn_narrow(const FfnArgs& a, moe_act_mode mode, int slots, int stage_mask,
                              hipStream_t s);
+// The argument block of an nvfp4_expert_ffn call (workspace pointers included).
+FfnArgs make_ffn_args(const moe_nvfp4_experts& w, moe_act_mode mode, const uint16_t* x, int T,
+                      int k, const int32_t* offsets, const int32_t* sorted_pairs, float* y_pairs,
+                      void* ws);
 moe_status launch_ffn_wide_a4(const FfnArgs& a, int stage_mask, void* plan_ws, hipStream_t s);
 // Entries of the wide path's work plan for P sorted rows of E experts.
 int wide_plan_entries(int P, int E);

@@ -22,7 +22,7 @@ void clear_error() { g_error.clear(); }
 moe_status check_experts(const char* name, const moe_nvfp4_experts* w, moe_act_mode mode);
 
 struct LayerLayout {
-  size_t ids, w, offsets, sorted, pair_row, y, ffn, route, total;
+  size_t ids, w, offsets, sorted, pair_row, y, ffn, route, state, total;
 };
 
 static bool layer_layout(moe_act_mode mode, int T, int k, int E, int H, int I, LayerLayout& L) {
@@ -33,6 +33,9 @@ static bool layer_layout(moe_act_mode mode, int T, int k, int E, int H, int I, L
   const size_t P = (size_t)T * k;
   size_t o = 0;
   auto seg = [&](size_t bytes) { const size_t at = o; o = round_up(o + bytes, 256); return at; };
+  // first, so its place does not depend on the call's sizes (one workspace
+  // may serve calls of several token counts)
+  L.state = seg(decode_state_bytes());   // zero before the first call, left zero by each call
   L.ids = seg(P * 4);
   L.w = seg(P * 4);
   L.offsets = seg((size_t)(E + 1) * 4);
@@ -50,6 +53,10 @@ static bool layer_layout(moe_act_mode mode, int T, int k, int E, int H, int I, L
 }  // namespace moe
 
 extern "C" const char* moe_last_error(void) { return moe::g_error.c_str(); }
+
+extern "C" size_t moe_layer_wait_timeouts_offset(void) {
+  return moe::decode_timeouts_offset();   // the state block is at the start of the workspace
+}
 
 extern "C" size_t moe_layer_workspace_bytes(moe_act_mode mode, int T, int k, int E, int H, int I) {
   moe::LayerLayout L;
@@ -99,6 +106,10 @@ extern "C" moe_status moe_layer_forward(const moe_nvfp4_experts* w, moe_act_mode
   int32_t* sorted = reinterpret_cast<int32_t*>(b + L.sorted);
   int32_t* prow = reinterpret_cast<int32_t*>(b + L.pair_row);
   float* y = reinterpret_cast<float*>(b + L.y);
+  if (moe::decode_fusable(T, w->H, w->I))
+    return moe::launch_layer_decode(*w, mode, x, w_router, router_bias, T, k, residual, out, ids,
+                                    tw, offs, sorted, prow, y, reinterpret_cast<float*>(b + L.route),
+                                    b + L.ffn, b + L.state, s);
   if ((st = moe::launch_route(x, w_router, router_bias, T, w->H, w->E, k, ids, tw,
                               reinterpret_cast<float*>(b + L.route), s)) != MOE_OK)
     return st;

@@ -12,12 +12,9 @@
 // Wide calls: a bf16 MFMA GEMM (16x16x32), operands read straight from
 // global memory in the MFMA lane layout (both are K-contiguous).
 // Top-k: one wave per token, k rounds of a wave argmax (ties to lower index).
-#include "abi_common.hpp"
-#include "device_common.hpp"
+#include "route_common.hpp"
 
 namespace moe {
-
-constexpr int kNarrowT = 8;
 
 __global__ void __launch_bounds__(256) k_router_logits_narrow(const uint16_t* __restrict__ x,
                                                               const uint16_t* __restrict__ wr,
@@ -25,53 +22,8 @@ __global__ void __launch_bounds__(256) k_router_logits_narrow(const uint16_t* __
                                                               int T, int H, int E,
                                                               float* __restrict__ logits) {
   extern __shared__ __align__(16) uint8_t smem[];
-  uint4* xs = reinterpret_cast<uint4*>(smem);       // [T][H/8] chunks of 8 bf16
-  const int nch = H / 8;
-  const int wave = threadIdx.x / kWave, lane = lane_id();
-  const int e = blockIdx.x * 4 + wave;
-  // this lane's chunks of the router row go out first (H <= 4096: <= 8 chunks),
-  // so their HBM latency overlaps the staging of x
-  constexpr int kMaxChunks = kMaxDim / 8 / kWave;
-  uint4 wv[kMaxChunks];
-  const uint4* wrow = reinterpret_cast<const uint4*>(wr + (size_t)(e < E ? e : 0) * H);
-#pragma unroll
-  for (int j = 0; j < kMaxChunks; ++j) {
-    const int c = lane + kWave * j;
-    if (c < nch) wv[j] = wrow[c];
-  }
-  for (int i = threadIdx.x; i < T * nch; i += blockDim.x)
-    xs[i] = reinterpret_cast<const uint4*>(x)[i];
-  __syncthreads();
-  if (e >= E) return;
-  float acc[kNarrowT];
-#pragma unroll
-  for (int t = 0; t < kNarrowT; ++t) acc[t] = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kMaxChunks; ++j) {
-    const int c = lane + kWave * j;
-    if (c >= nch) break;
-    const uint4 w = wv[j];
-#pragma unroll
-    for (int t = 0; t < kNarrowT; ++t) {
-      if (t < T) {
-        const uint4 xv = xs[t * nch + c];
-        float a = acc[t];
-        a = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(w.x), bitcast<bf16x2>(xv.x), a, false);
-        a = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(w.y), bitcast<bf16x2>(xv.y), a, false);
-        a = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(w.z), bitcast<bf16x2>(xv.z), a, false);
-        a = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(w.w), bitcast<bf16x2>(xv.w), a, false);
-        acc[t] = a;
-      }
-    }
-  }
-  const float b = bias ? bias[e] : 0.0f;
-#pragma unroll
-  for (int t = 0; t < kNarrowT; ++t) {
-    if (t < T) {
-      const float v = group_sum<kWave>(acc[t]);
-      if (lane == 0) logits[(size_t)t * E + e] = v + b;
-    }
-  }
+  router_logits_wave(x, wr, bias, T, H, E, blockIdx.x * 4 + threadIdx.x / kWave,
+                     reinterpret_cast<uint4*>(smem), logits);
 }
 
 // Wide logits (prefill): workgroup = 32 tokens x 32 experts, 4 waves splitting
@@ -155,57 +107,12 @@ __global__ void __launch_bounds__(256) k_router_logits_mfma(const uint16_t* __re
   }
 }
 
-// One wave per token.  Lane L holds the S contiguous experts L*S .. L*S+S-1, so
-// among lanes tied on the maximum the lowest lane holds the lowest index.
-// Each round: every lane's best free slot (strict >, so a lane keeps its lowest
-// index among equal values), the wave maximum, the lowest lane holding it;
-// that expert is marked taken.  No branches depend on the data.
 template <int S>
 __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, int T, int E,
                                               int k, int32_t* __restrict__ ids,
                                               float* __restrict__ w) {
-  const int wave = threadIdx.x / kWave, lane = lane_id();
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
-  const float ninf = -__builtin_huge_valf();
-  float v[S];
-  uint32_t taken = 0u;
-#pragma unroll
-  for (int i = 0; i < S; ++i) {
-    const int e = lane * S + i;
-    const float x = row[e < E ? e : E - 1];      // in-bounds load, masked below
-    v[i] = e < E ? x : ninf;
-    taken |= (e < E ? 0u : 1u) << i;
-  }
-  float sel_v = 0.0f, first_v = 0.0f;
-  int sel_i = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = ninf;
-    int bs = S;                                   // no free slot
-#pragma unroll
-    for (int i = S - 1; i >= 0; --i) {            // descending: ties end on the lowest slot
-      const bool better = !((taken >> i) & 1u) && v[i] >= bv;
-      bv = better ? v[i] : bv;
-      bs = better ? i : bs;
-    }
-    const float m = wave_max(bs < S ? bv : ninf);
-    const unsigned long long hit = __ballot(bs < S && bv == m);
-    const int win_lane = __ffsll((long long)hit) - 1;
-    const int win_slot = __builtin_amdgcn_readlane(bs, win_lane);
-    const int win = win_lane * S + win_slot;
-    if (lane == win_lane) taken |= 1u << win_slot;
-    if (j == 0) first_v = m;
-    sel_v = lane == j ? m : sel_v;
-    sel_i = lane == j ? win : sel_i;
-  }
-  // renormalised softmax over the chosen logits: exp(l_j - l_max) / sum
-  const float ex = lane < k ? expf(sel_v - first_v) : 0.0f;
-  const float sum = wave_sum(ex);
-  if (lane < k) {
-    ids[(size_t)t * k + lane] = sel_i;
-    w[(size_t)t * k + lane] = __fdiv_rn(ex, sum);
-  }
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t < T) topk_wave<S>(logits, t, E, k, ids, w);
 }
 
 static void launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,

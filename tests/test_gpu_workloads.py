@@ -132,6 +132,32 @@ def test_prefill_w4a4_zipf(dev):
     assert np.all(np.isfinite(F.bf16_to_f64(out)))
 
 
+@pytest.mark.parametrize("wi,mode", [(1, "A16"), (3, "A8"), (2, "A4")])
+def test_decode_fused_equals_stages(dev, wi, mode):
+    """Up to 8 tokens moe_layer_forward runs fused (two launches, counters in the
+    workspace).  Its output and the routing it leaves in the workspace equal the
+    per-stage entry points' bit for bit, over calls of changing token counts on
+    one zero-initialised workspace (each call must leave its counters at zero)."""
+    w = synth.CONFIGS[wi]
+    ex, router, bias = gpu_layer(w, 0, mode, dev)
+    ws = torch.zeros(moe.layer_workspace_bytes(mode, 8, w.k, w.E, w.H, w.I), dtype=torch.uint8, device=dev)
+    for T, batch in ((w.T, 0), (1, 5), (8, 6), (2, 7), (w.T, 8), (w.T, 8)):
+        xg = bench.token_batch(w, batch, dev, T)
+        say("fused decode", wi, mode, "T", T, "batch", batch)
+        ids, tw = moe.moe_route_topk(xg, router, w.k, bias)
+        off, sp, pr = moe.moe_permute(ids, w.E)
+        y, _ = moe.nvfp4_expert_ffn(ex, mode, xg, w.k, off, sp)
+        ref = moe.moe_combine(y, pr, tw, residual=xg)
+        out, _ = moe.moe_layer_forward(ex, mode, xg, router, w.k, bias=bias, residual=xg, ws=ws)
+        torch.cuda.synchronize()
+        v = moe.workspace_views(ws, mode, T, w.k, w.E, w.H, w.I)
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+        assert torch.equal(v["topk_ids"], ids) and torch.equal(v["topk_w"], tw)
+        assert torch.equal(v["expert_offsets"], off)
+        assert torch.equal(v["sorted_pairs"], sp) and torch.equal(v["pair_row"], pr)
+    assert moe.layer_wait_timeouts(ws) == 0
+
+
 @pytest.mark.parametrize("mode", ["A16", "A8"])
 def test_stack_layers(dev, mode):
     """48-layer decode stack, T=2: each layer consumes the previous layer's residual
