@@ -13,10 +13,13 @@ router matrix) over the measured step time.  To keep the 256 MB Infinity
 Cache from serving the weights, the steps cycle over 8 independently seeded
 copies of the layer and 64 seeded token batches.
 
-roofline: the gate/up + SwiGLU kernel (the largest weight stream of the step),
-timed with HIP events on the stream it runs on, in a second timed pass that
-launches it back to back over the layer copies (each with its own routing);
-its algorithmic bytes are the touched experts' gate/up codes + scales.
+roofline: the kernel that streams the expert weights, timed with HIP events on
+the stream it runs on, in a second timed pass of back-to-back launches over
+the layer copies.  Up to 8 tokens (fused layer) that is the experts + combine
+kernel, whose algorithmic bytes are the touched experts' packed codes + scales;
+it runs after its routing kernel, so it is timed as (routing + experts) minus
+routing alone.  For wider calls it is the gate/up + SwiGLU kernel (bytes: the
+touched experts' gate/up codes + scales).
 
 cpu_baseline: the oracle (oracle/, double precision numpy, one BLAS thread)
 on a bounded sample of the same workload, on this machine's host CPU.
@@ -108,14 +111,14 @@ def run_gpu(w, mode, steps, warmup, n_layers, n_batches):
         moe.moe_layer_forward(ex, mode, xs[s % n_batches], router, k, bias=bias, ws=ws, out=out)
 
     # untimed pass: the experts each (layer, batch) combination touches
-    combo_bytes, combo_gu_bytes = [], []
+    combo_bytes, combo_n = [], []
     views = moe.workspace_views(ws, mode, T, k, E, H, I)
     for s in range(combos):
         step(s)
         ids = views["topk_ids"].cpu().numpy()
         n, b = touched_bytes(w, ids)
         combo_bytes.append(b)
-        combo_gu_bytes.append(n * (2 * I * H // 2 + 2 * I * H // 16))
+        combo_n.append(n)
     for s in range(warmup):
         step(s)
     torch.cuda.synchronize()
@@ -129,46 +132,78 @@ def run_gpu(w, mode, steps, warmup, n_layers, n_batches):
     ms = ev0.elapsed_time(ev1) / steps
     total_bytes = sum(combo_bytes[s % combos] for s in range(steps))
 
-    # timed pass B: the gate/up + SwiGLU kernel alone, launched back to back (the
-    # queue stays full, so the HIP events bracket GPU time only), cycling over the
-    # layer copies so its weights come from HBM; the routing is each layer's own
-    # from the untimed pass, stored per layer.
-    L = moe.layer_workspace_layout(mode, T, k, E, H, I)
-    per_layer = []
-    for l in range(n_layers):
-        step(l)                            # layer l with token batch l
-        v = moe.workspace_views(ws, mode, T, k, E, H, I)
-        fws = torch.empty(moe.ffn_workspace_bytes(mode, T, k, H, I), dtype=torch.uint8, device=dev)
-        moe.nvfp4_expert_ffn_stage(layers[l][0], mode, 0, xs[l % n_batches], k, v["expert_offsets"],
-                                   v["sorted_pairs"], v["y_pairs"], fws)
-        n_e = len(np.unique(v["topk_ids"].cpu().numpy()))
-        per_layer.append((v["expert_offsets"].clone(), v["sorted_pairs"].clone(), fws, n_e))
-    y = torch.empty(T * k, H, dtype=torch.float32, device=dev)
+    # timed pass B: the step's largest weight stream alone, launched back to back
+    # (the queue stays full, so the HIP events bracket GPU time only), cycling
+    # over the layer copies so its weights come from HBM.
+    fused = bool(moe.lib().moe_layer_is_fused(T, H, I))
+    gu_bytes_e = 2 * I * H // 2 + 2 * I * H // 16        # one expert's gate/up codes + scales
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    if fused:
+        # Up to 8 tokens the layer is two kernels: routing (stage 0) and the experts
+        # with the combine (stage 1, the weight stream).  Stage 1 needs its stage 0
+        # first, so it is timed as (stage 0 + stage 1) minus stage 0 alone.
+        def half(s, stages):
+            ex, router, bias = layers[s % n_layers]
+            for st_ in stages:
+                moe.moe_layer_forward_stage(ex, mode, st_, xs[s % n_batches], router, k, bias, None, ws, out)
+        for s in range(warmup):
+            half(s, (0, 1))
+        torch.cuda.synchronize()
+        ev[0].record()
+        for s in range(steps):
+            half(s, (0,))
+        ev[1].record()
+        torch.cuda.synchronize()
+        ev[2].record()
+        for s in range(steps):
+            half(s, (0, 1))
+        ev[3].record()
+        torch.cuda.synchronize()
+        route_us = ev[0].elapsed_time(ev[1]) / steps * 1e3
+        kern_us = ev[2].elapsed_time(ev[3]) / steps * 1e3 - route_us
+        n_e = float(np.mean([combo_n[s % combos] for s in range(steps)]))
+        kern_bytes = n_e * w.expert_bytes
+        kernel = "k_experts_decode (gate/up + SwiGLU + down + combine, fused)"
+    else:
+        L = moe.layer_workspace_layout(mode, T, k, E, H, I)
+        per_layer = []
+        for l in range(n_layers):
+            step(l)                            # layer l with token batch l
+            v = moe.workspace_views(ws, mode, T, k, E, H, I)
+            fws = torch.empty(moe.ffn_workspace_bytes(mode, T, k, H, I), dtype=torch.uint8, device=dev)
+            moe.nvfp4_expert_ffn_stage(layers[l][0], mode, 0, xs[l % n_batches], k, v["expert_offsets"],
+                                       v["sorted_pairs"], v["y_pairs"], fws)
+            n_e = len(np.unique(v["topk_ids"].cpu().numpy()))
+            per_layer.append((v["expert_offsets"].clone(), v["sorted_pairs"].clone(), fws, n_e))
+        y = torch.empty(T * k, H, dtype=torch.float32, device=dev)
 
-    def gate_up(s):
-        l = s % n_layers
-        off, sp, fws, _ = per_layer[l]
-        moe.nvfp4_expert_ffn_stage(layers[l][0], mode, 1, xs[l % n_batches], k, off, sp, y, fws)
+        def gate_up(s):
+            l = s % n_layers
+            off, sp, fws, _ = per_layer[l]
+            moe.nvfp4_expert_ffn_stage(layers[l][0], mode, 1, xs[l % n_batches], k, off, sp, y, fws)
 
-    for s in range(warmup):
-        gate_up(s)
-    torch.cuda.synchronize()
-    ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev2.record()
-    for s in range(steps):
-        gate_up(s)
-    ev3.record()
-    torch.cuda.synchronize()
-    gu_us = ev2.elapsed_time(ev3) / steps * 1e3
-    gu_bytes = float(np.mean([per_layer[s % n_layers][3] for s in range(steps)])) * (2 * I * H // 2 + 2 * I * H // 16)
-    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+        for s in range(warmup):
+            gate_up(s)
+        torch.cuda.synchronize()
+        ev[0].record()
+        for s in range(steps):
+            gate_up(s)
+        ev[1].record()
+        torch.cuda.synchronize()
+        route_us = None
+        kern_us = ev[0].elapsed_time(ev[1]) / steps * 1e3
+        kern_bytes = float(np.mean([per_layer[s % n_layers][3] for s in range(steps)])) * gu_bytes_e
+        kernel = ("k_gateup_wide_a4" if (mode == "A4" and T > 8) else "k_gateup_narrow") + " (gate/up + SwiGLU)"
+    achieved = kern_bytes / (kern_us * 1e-6) / 1e9
     return {
         "ms_per_step": ms,
         "gbs": total_bytes / steps / (ms * 1e-3) / 1e9,
         "bytes_per_step": total_bytes / steps,
-        "gu_achieved_gbs": achieved,
-        "gu_bytes_per_launch": gu_bytes,
-        "gu_us": gu_us,
+        "kernel": kernel,
+        "kern_achieved_gbs": achieved,
+        "kern_bytes_per_launch": kern_bytes,
+        "kern_us": kern_us,
+        "route_us": route_us,
     }
 
 
@@ -209,6 +244,51 @@ def cpu_baseline(w, mode, budget_s=20.0, max_tokens=12):
             "tokens_per_s": done * w.T / t_total}
 
 
+# --------------------------------------------------------------------------- traffic
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration():
+    """Five device-to-device copies of COPY_BYTES (torch's copy kernel): each reads
+    and writes exactly COPY_BYTES, the reference for the HBM byte counters."""
+    import torch
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 5}), flush=True)
+    return 0
+
+
+def kernel_sources_digest():
+    """SHA-1 over the library's kernel sources (csrc/*.hip, *.hpp, sorted): a stored
+    counter measurement is reported only while the kernels it measured are unchanged."""
+    import glob
+    import hashlib
+    h = hashlib.sha1()
+    csrc = os.path.join(ROOT, "nvfp4_block_scaled_softmax_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload_index):
+    """HBM bytes per launch of the roofline kernel from profiles/traffic_w<i>.json
+    (written from rocprofv3 FETCH_SIZE and WRITE_SIZE runs, scaled by the copy
+    calibration), or None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_w{workload_index}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("sources_sha1") != kernel_sources_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
 # --------------------------------------------------------------------------- main
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -219,7 +299,12 @@ def main(argv=None):
     ap.add_argument("--layers", type=int, default=8, help="seeded layer copies cycled through")
     ap.add_argument("--batches", type=int, default=64, help="seeded token batches cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 256 MiB device copy (x5): the known-size reference that "
+                         "scales the FETCH_SIZE / WRITE_SIZE counters of the traffic measurement")
     args = ap.parse_args(argv)
+    if args.copy_calibration:
+        return copy_calibration()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the layer runs whole on one MI355X).", file=sys.stderr)
@@ -256,12 +341,13 @@ def main(argv=None):
         "tokens_per_s": round(w.T / (r["ms_per_step"] * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * r["gbs"] / HBM_PEAK_GBS, 2),
         "bytes_per_step": int(r["bytes_per_step"]),
-        "roofline": {"kernel": ("k_gateup_wide_a4" if (mode == "A4" and w.T > 8) else "k_gateup_narrow")
-                               + " (gate/up + SwiGLU)", "bound": "hbm",
-                     "achieved": round(r["gu_achieved_gbs"], 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(r["gu_achieved_gbs"] / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": int(r["gu_bytes_per_launch"]),
-                     "us_per_launch": round(r["gu_us"], 2), "traffic": None},
+        "roofline": {"kernel": r["kernel"], "bound": "hbm",
+                     "achieved": round(r["kern_achieved_gbs"], 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(r["kern_achieved_gbs"] / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": int(r["kern_bytes_per_launch"]),
+                     "us_per_launch": round(r["kern_us"], 2),
+                     "routing_us_per_launch": None if r["route_us"] is None else round(r["route_us"], 2),
+                     "traffic": stored_traffic(w.index)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

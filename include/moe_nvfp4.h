@@ -211,11 +211,27 @@ moe_status moe_layer_workspace_layout(moe_act_mode mode, int T, int k, int E, in
  * decode path which reached their bound (a stalled producer); it stays 0 in
  * correct operation and is meant for tests and health checks. */
 size_t moe_layer_wait_timeouts_offset(void);
+
+/* 1 when moe_layer_forward runs the fused two-launch path for these sizes (up
+ * to 8 tokens, H/32 in 33..128, I/32 in 5..32), else 0 (per-stage kernels). */
+int moe_layer_is_fused(int T, int H, int I);
 size_t moe_layer_workspace_bytes(moe_act_mode mode, int T, int k, int E, int H, int I);
 moe_status moe_layer_forward(const moe_nvfp4_experts* w, moe_act_mode mode, const uint16_t* x,
                              const uint16_t* w_router, const float* router_bias, int T, int k,
                              const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes,
                              hipStream_t s);
+
+/* moe_layer_forward_stage: one half of moe_layer_forward, same arguments and
+ * workspace: stage 0 routes (router logits, top-k, permutation, and the
+ * activation quantization of the 8/4-bit modes), stage 1 runs the experts and
+ * the combine.  Stage 0 then stage 1 on one stream equals moe_layer_forward;
+ * stage 1 needs the stage 0 of the same call before it.  It lets a caller time
+ * the two halves (the fused decode path runs one kernel per half). */
+moe_status moe_layer_forward_stage(const moe_nvfp4_experts* w, moe_act_mode mode, int stage,
+                                   const uint16_t* x, const uint16_t* w_router,
+                                   const float* router_bias, int T, int k,
+                                   const uint16_t* residual, uint16_t* out, void* ws,
+                                   size_t ws_bytes, hipStream_t s);
 
 #ifdef __cplusplus
 }

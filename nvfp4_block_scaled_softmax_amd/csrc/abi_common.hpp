@@ -60,10 +60,12 @@ size_t expert_ffn_workspace(moe_act_mode mode, int T, int k, int H, int I);
 size_t decode_state_bytes();
 size_t decode_timeouts_offset();
 bool decode_fusable(int T, int H, int I);
-moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, const uint16_t* x,
-                               const uint16_t* w_router, const float* bias, int T, int k,
-                               const uint16_t* residual, uint16_t* out, int32_t* ids, float* tw,
-                               int32_t* offsets, int32_t* sorted, int32_t* prow, float* y,
-                               float* logits, void* ffn_ws, void* state, hipStream_t s);
+// stage_mask: bit 0 routing (+ activation quantization), bit 1 experts + combine.
+moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, int stage_mask,
+                               const uint16_t* x, const uint16_t* w_router, const float* bias,
+                               int T, int k, const uint16_t* residual, uint16_t* out,
+                               int32_t* ids, float* tw, int32_t* offsets, int32_t* sorted,
+                               int32_t* prow, float* y, float* logits, void* ffn_ws, void* state,
+                               hipStream_t s);
 
 }  // namespace moe

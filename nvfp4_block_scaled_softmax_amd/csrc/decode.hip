@@ -245,32 +245,39 @@ static void launch_b(const FfnArgs& a, DecodeState* st, int max_slots, const int
   else launch_b2<MODE, 4>(a, dl, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, s);
 }
 
-moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, const uint16_t* x,
-                               const uint16_t* w_router, const float* bias, int T, int k,
-                               const uint16_t* residual, uint16_t* out, int32_t* ids, float* tw,
-                               int32_t* offsets, int32_t* sorted, int32_t* prow, float* y,
-                               float* logits, void* ffn_ws, void* state, hipStream_t s) {
+moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, int stage_mask,
+                               const uint16_t* x, const uint16_t* w_router, const float* bias,
+                               int T, int k, const uint16_t* residual, uint16_t* out,
+                               int32_t* ids, float* tw, int32_t* offsets, int32_t* sorted,
+                               int32_t* prow, float* y, float* logits, void* ffn_ws, void* state,
+                               hipStream_t s) {
   DecodeState* st = static_cast<DecodeState*>(state);
   const int E = w.E, H = w.H;
-  if (E <= 64) launch_a<1>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
-  else if (E <= 128) launch_a<2>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
-  else if (E <= 256) launch_a<4>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
-  else if (E <= 512) launch_a<8>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
-  else launch_a<16>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
-  moe_status r = check_launch("moe_layer_forward (decode routing)");
-  if (r != MOE_OK) return r;
-  if (mode != MOE_A16) {   // activation quantization needs the permutation (4-bit: per pair)
-    r = launch_expert_ffn(w, mode, x, T, k, offsets, sorted, y, ffn_ws, 1, s);
+  moe_status r;
+  if (stage_mask & 1) {   // routing, and the activation quantization of the 8/4-bit modes
+    if (E <= 64) launch_a<1>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
+    else if (E <= 128) launch_a<2>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
+    else if (E <= 256) launch_a<4>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
+    else if (E <= 512) launch_a<8>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
+    else launch_a<16>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
+    r = check_launch("moe_layer_forward (decode routing)");
     if (r != MOE_OK) return r;
+    if (mode != MOE_A16) {   // needs the permutation (4-bit: per pair)
+      r = launch_expert_ffn(w, mode, x, T, k, offsets, sorted, y, ffn_ws, 1, s);
+      if (r != MOE_OK) return r;
+    }
   }
-  const FfnArgs a = make_ffn_args(w, mode, x, T, k, offsets, sorted, y, ffn_ws);
-  const int P = T * k, max_slots = P < E ? P : E;
-  switch (mode) {
-    case MOE_A16: launch_b<MOE_A16>(a, st, max_slots, prow, tw, residual, out, s); break;
-    case MOE_A8: launch_b<MOE_A8>(a, st, max_slots, prow, tw, residual, out, s); break;
-    default: launch_b<MOE_A4>(a, st, max_slots, prow, tw, residual, out, s); break;
+  if (stage_mask & 2) {   // experts and combine
+    const FfnArgs a = make_ffn_args(w, mode, x, T, k, offsets, sorted, y, ffn_ws);
+    const int P = T * k, max_slots = P < E ? P : E;
+    switch (mode) {
+      case MOE_A16: launch_b<MOE_A16>(a, st, max_slots, prow, tw, residual, out, s); break;
+      case MOE_A8: launch_b<MOE_A8>(a, st, max_slots, prow, tw, residual, out, s); break;
+      default: launch_b<MOE_A4>(a, st, max_slots, prow, tw, residual, out, s); break;
+    }
+    return check_launch("moe_layer_forward (decode experts)");
   }
-  return check_launch("moe_layer_forward (decode experts)");
+  return MOE_OK;
 }
 
 }  // namespace moe

@@ -54,6 +54,8 @@ static bool layer_layout(moe_act_mode mode, int T, int k, int E, int H, int I, L
 
 extern "C" const char* moe_last_error(void) { return moe::g_error.c_str(); }
 
+extern "C" int moe_layer_is_fused(int T, int H, int I) { return moe::decode_fusable(T, H, I) ? 1 : 0; }
+
 extern "C" size_t moe_layer_wait_timeouts_offset(void) {
   return moe::decode_timeouts_offset();   // the state block is at the start of the workspace
 }
@@ -80,24 +82,23 @@ extern "C" moe_status moe_layer_workspace_layout(moe_act_mode mode, int T, int k
   return MOE_OK;
 }
 
-extern "C" moe_status moe_layer_forward(const moe_nvfp4_experts* w, moe_act_mode mode,
-                                        const uint16_t* x, const uint16_t* w_router,
-                                        const float* router_bias, int T, int k,
-                                        const uint16_t* residual, uint16_t* out, void* ws,
-                                        size_t ws_bytes, hipStream_t s) {
+static moe_status layer_call(const char* name, const moe_nvfp4_experts* w, moe_act_mode mode,
+                             int stage_mask, const uint16_t* x, const uint16_t* w_router,
+                             const float* router_bias, int T, int k, const uint16_t* residual,
+                             uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s) {
   moe::clear_error();
-  moe_status st = moe::check_experts("moe_layer_forward", w, mode);
+  moe_status st = moe::check_experts(name, w, mode);
   if (st != MOE_OK) return st;
-  MOE_REQUIRE(x && w_router && out && ws, MOE_E_ARG, "moe_layer_forward: null pointer argument");
+  MOE_REQUIRE(x && w_router && out && ws, MOE_E_ARG, "%s: null pointer argument", name);
   moe::LayerLayout L;
   MOE_REQUIRE(moe::layer_layout(mode, T, k, w->E, w->H, w->I, L), MOE_E_SHAPE,
-              "moe_layer_forward: bad shape T=%d k=%d", T, k);
-  MOE_REQUIRE(out != x, MOE_E_ARG, "moe_layer_forward: out must not alias x");
+              "%s: bad shape T=%d k=%d", name, T, k);
+  MOE_REQUIRE(out != x, MOE_E_ARG, "%s: out must not alias x", name);
   MOE_REQUIRE(moe::aligned(x, 16) && moe::aligned(w_router, 16) && moe::aligned(out, 16) &&
                   moe::aligned(ws, 256) && (!residual || moe::aligned(residual, 16)) &&
                   (!router_bias || moe::aligned(router_bias, 4)),
-              MOE_E_ALIGN, "moe_layer_forward: misaligned pointer (workspace needs 256 bytes)");
-  MOE_REQUIRE(ws_bytes >= L.total, MOE_E_WORKSPACE, "moe_layer_forward: workspace %zu < %zu bytes",
+              MOE_E_ALIGN, "%s: misaligned pointer (workspace needs 256 bytes)", name);
+  MOE_REQUIRE(ws_bytes >= L.total, MOE_E_WORKSPACE, "%s: workspace %zu < %zu bytes", name,
               ws_bytes, L.total);
   uint8_t* b = static_cast<uint8_t*>(ws);
   int32_t* ids = reinterpret_cast<int32_t*>(b + L.ids);
@@ -107,15 +108,46 @@ extern "C" moe_status moe_layer_forward(const moe_nvfp4_experts* w, moe_act_mode
   int32_t* prow = reinterpret_cast<int32_t*>(b + L.pair_row);
   float* y = reinterpret_cast<float*>(b + L.y);
   if (moe::decode_fusable(T, w->H, w->I))
-    return moe::launch_layer_decode(*w, mode, x, w_router, router_bias, T, k, residual, out, ids,
-                                    tw, offs, sorted, prow, y, reinterpret_cast<float*>(b + L.route),
-                                    b + L.ffn, b + L.state, s);
-  if ((st = moe::launch_route(x, w_router, router_bias, T, w->H, w->E, k, ids, tw,
-                              reinterpret_cast<float*>(b + L.route), s)) != MOE_OK)
-    return st;
-  if ((st = moe::launch_permute(ids, T, k, w->E, offs, sorted, prow, b + L.route, s)) != MOE_OK)
-    return st;
-  if ((st = moe::launch_expert_ffn(*w, mode, x, T, k, offs, sorted, y, b + L.ffn, 7, s)) != MOE_OK)
-    return st;
-  return moe::launch_combine(y, prow, tw, T, k, w->H, residual, out, s);
+    return moe::launch_layer_decode(*w, mode, stage_mask, x, w_router, router_bias, T, k,
+                                    residual, out, ids, tw, offs, sorted, prow, y,
+                                    reinterpret_cast<float*>(b + L.route), b + L.ffn, b + L.state, s);
+  if (stage_mask & 1) {
+    if ((st = moe::launch_route(x, w_router, router_bias, T, w->H, w->E, k, ids, tw,
+                                reinterpret_cast<float*>(b + L.route), s)) != MOE_OK)
+      return st;
+    if ((st = moe::launch_permute(ids, T, k, w->E, offs, sorted, prow, b + L.route, s)) != MOE_OK)
+      return st;
+    if ((st = moe::launch_expert_ffn(*w, mode, x, T, k, offs, sorted, y, b + L.ffn, 1, s)) != MOE_OK)
+      return st;
+  }
+  if (stage_mask & 2) {
+    if ((st = moe::launch_expert_ffn(*w, mode, x, T, k, offs, sorted, y, b + L.ffn, 6, s)) != MOE_OK)
+      return st;
+    return moe::launch_combine(y, prow, tw, T, k, w->H, residual, out, s);
+  }
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_layer_forward(const moe_nvfp4_experts* w, moe_act_mode mode,
+                                        const uint16_t* x, const uint16_t* w_router,
+                                        const float* router_bias, int T, int k,
+                                        const uint16_t* residual, uint16_t* out, void* ws,
+                                        size_t ws_bytes, hipStream_t s) {
+  return layer_call("moe_layer_forward", w, mode, 3, x, w_router, router_bias, T, k, residual, out,
+                    ws, ws_bytes, s);
+}
+
+extern "C" moe_status moe_layer_forward_stage(const moe_nvfp4_experts* w, moe_act_mode mode,
+                                              int stage, const uint16_t* x,
+                                              const uint16_t* w_router, const float* router_bias,
+                                              int T, int k, const uint16_t* residual,
+                                              uint16_t* out, void* ws, size_t ws_bytes,
+                                              hipStream_t s) {
+  if (stage != 0 && stage != 1) {
+    moe::clear_error();
+    moe::set_error("moe_layer_forward_stage: stage %d is not 0 or 1", stage);
+    return MOE_E_ARG;
+  }
+  return layer_call("moe_layer_forward_stage", w, mode, 1 << stage, x, w_router, router_bias, T,
+                    k, residual, out, ws, ws_bytes, s);
 }

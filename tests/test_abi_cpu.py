@@ -65,6 +65,15 @@ def test_route_validation():
     assert code == "MOE_E_WORKSPACE" and "workspace" in text
 
 
+def test_layer_stage_and_fused_queries():
+    L = moe.lib()
+    assert L.moe_layer_is_fused(1, 3072, 512) == 1 and L.moe_layer_is_fused(8, 3072, 512) == 1
+    assert L.moe_layer_is_fused(9, 3072, 512) == 0          # wider calls: per-stage kernels
+    assert L.moe_layer_is_fused(1, 256, 128) == 0           # small H/I: per-stage kernels
+    code, text = _err(L.moe_layer_forward_stage(None, 0, 2, P16, P16, None, 1, 2, None, P16, P16, 1 << 20, None))
+    assert code == "MOE_E_ARG" and "stage" in text
+
+
 def test_permute_and_combine_validation():
     L = moe.lib()
     assert _err(L.moe_permute(P16, 1, 10, 5, P16, P16, P16, None, 0, None))[0] == "MOE_E_SHAPE"

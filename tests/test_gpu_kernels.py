@@ -348,9 +348,15 @@ def test_layer_is_deterministic(dev):
     experts = _upload([cache(e) for e in range(w.E)], dev)
     x = bf16_dev(synth.tokens(w, batch=1, T=64), dev)
     wr = bf16_dev(synth.router_weight(w), dev)
-    a, _ = moe.moe_layer_forward(experts, "A16", x, wr, w.k)
+    a, ws = moe.moe_layer_forward(experts, "A16", x, wr, w.k)
     b, _ = moe.moe_layer_forward(experts, "A16", x, wr, w.k)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # per-stage path (these sizes are not fused): the two halves equal the whole
+    c = torch.empty_like(a)
+    for stage in (0, 1):
+        moe.moe_layer_forward_stage(experts, "A16", stage, x, wr, w.k, None, None, ws, c)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
 @pytest.mark.parametrize("H,I", [(256, 128), (384, 256), (640, 384), (96, 160), (3072, 512)])

@@ -155,6 +155,12 @@ def test_decode_fused_equals_stages(dev, wi, mode):
         assert torch.equal(v["topk_ids"], ids) and torch.equal(v["topk_w"], tw)
         assert torch.equal(v["expert_offsets"], off)
         assert torch.equal(v["sorted_pairs"], sp) and torch.equal(v["pair_row"], pr)
+        # the two halves run separately give the same result
+        out2 = torch.empty_like(out)
+        for stage in (0, 1):
+            moe.moe_layer_forward_stage(ex, mode, stage, xg, router, w.k, bias, xg, ws, out2)
+        torch.cuda.synchronize()
+        assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
     assert moe.layer_wait_timeouts(ws) == 0
 
 
