@@ -44,6 +44,7 @@ namespace moe {
 constexpr int kDecMaxSlots = 512;     // active experts of a call: at most T * k <= 8 * 64
 constexpr int kDecMaxRowBlocks = kMaxDim / kDnRows;
 constexpr uint32_t kSpinCap = 1u << 22;
+constexpr int kSmallP = 64;           // up to this many pairs the routing tail ranks them directly
 
 // Each counter sits on its own 128-byte line: many workgroups poll or bump them
 // at once, and counters sharing a line would queue behind each other.
@@ -94,6 +95,8 @@ __global__ void __launch_bounds__(kPermThreads)
   __shared__ int rank[kMaxExperts];
   __shared__ int wcnt[kPermWaves][kMaxExperts];
   __shared__ int wave_tot[kPermWaves];
+  __shared__ int pid[kSmallP];
+  __shared__ int pfirst[kSmallP];
   __shared__ int s_last;
   const int tid = threadIdx.x, wave = tid / kWave;
   router_logits_wave<true>(x, wr, bias, T, H, E, blockIdx.x * kPermWaves + wave,
@@ -109,26 +112,64 @@ __global__ void __launch_bounds__(kPermThreads)
   if (!s_last) return;
   // ---- the last workgroup: every expert's logits are visible
   for (int t = wave; t < T; t += kPermWaves) topk_wave<S, true>(logits, t, E, k, ids, tw);
-  for (int e = tid; e < E; e += kPermThreads) {
-    cnt[e] = 0;
-#pragma unroll
-    for (int w = 0; w < kPermWaves; ++w) wcnt[w][e] = 0;
-  }
   __syncthreads();   // ids are written (same workgroup)
   const int P = T * k;
-  for (int p = tid; p < P; p += kPermThreads) atomicAdd(&cnt[ids[p]], 1);
-  __syncthreads();
-  const int total = scan_experts(cnt, base, E, wave_tot);
-  for (int e = tid; e < E; e += kPermThreads) offsets[e] = base[e];
-  if (tid == 0) offsets[E] = total;
-  // active experts in ascending order: a second scan, over the 0/1 flags
-  for (int e = tid; e < E; e += kPermThreads) rank[e] = cnt[e] > 0;
-  __syncthreads();
-  const int n_active = scan_experts(rank, rank, E, wave_tot);
-  for (int e = tid; e < E; e += kPermThreads)
-    if (cnt[e] > 0) st->plan[rank[e]] = make_int4(e, base[e], cnt[e], 0);
-  if (tid == 0) st->n_active = n_active;
-  scatter_range(ids, 0, P, E, base, wcnt, sorted_pairs, pair_row);
+  if (P <= kSmallP) {
+    // Few pairs: each pair's row is (#pairs with a smaller id) + (#earlier pairs
+    // with its id), i.e. the stable order; offsets[e] counts the ids below e.
+    if (tid < P) pid[tid] = ids[tid];
+    __syncthreads();
+    int e = 0, lt = 0, eq_before = 0, n_eq = 0;
+    if (tid < P) {
+      e = pid[tid];
+      for (int q = 0; q < P; ++q) {
+        const int f = pid[q];
+        lt += f < e;
+        eq_before += (f == e) & (q < tid);
+        n_eq += f == e;
+      }
+      pfirst[tid] = eq_before == 0;   // the first pair of its expert
+    }
+    __syncthreads();
+    if (tid < P) {
+      int first_lt = 0;                // distinct experts below e
+      for (int q = 0; q < P; ++q) first_lt += pfirst[q] & (pid[q] < e);
+      const int row = lt + eq_before;
+      sorted_pairs[row] = tid;
+      pair_row[tid] = row;
+      if (eq_before == 0) st->plan[first_lt] = make_int4(e, lt, n_eq, 0);
+    }
+    for (int x = tid; x <= E; x += kPermThreads) {
+      int below = 0;
+      for (int q = 0; q < P; ++q) below += pid[q] < x;
+      offsets[x] = below;
+    }
+    if (tid == 0) {
+      int n = 0;
+      for (int q = 0; q < P; ++q) n += pfirst[q];
+      st->n_active = n;
+    }
+  } else {
+    for (int e = tid; e < E; e += kPermThreads) {
+      cnt[e] = 0;
+#pragma unroll
+      for (int w = 0; w < kPermWaves; ++w) wcnt[w][e] = 0;
+    }
+    __syncthreads();
+    for (int p = tid; p < P; p += kPermThreads) atomicAdd(&cnt[ids[p]], 1);
+    __syncthreads();
+    const int total = scan_experts(cnt, base, E, wave_tot);
+    for (int e = tid; e < E; e += kPermThreads) offsets[e] = base[e];
+    if (tid == 0) offsets[E] = total;
+    // active experts in ascending order: a second scan, over the 0/1 flags
+    for (int e = tid; e < E; e += kPermThreads) rank[e] = cnt[e] > 0;
+    __syncthreads();
+    const int n_active = scan_experts(rank, rank, E, wave_tot);
+    for (int e = tid; e < E; e += kPermThreads)
+      if (cnt[e] > 0) st->plan[rank[e]] = make_int4(e, base[e], cnt[e], 0);
+    if (tid == 0) st->n_active = n_active;
+    scatter_range(ids, 0, P, E, base, wcnt, sorted_pairs, pair_row);
+  }
   // B's counters start at zero: the previous call's B has finished (it ran
   // before this kernel on the stream); clear what it may have counted
   for (int i = tid; i < kDecMaxSlots; i += kPermThreads) st->gu_done[i].v = 0u;
