@@ -4,14 +4,11 @@
 
 namespace moe {
 
-// out values of token t, hidden 4c .. 4c+3: the weighted sum over the token's
-// pairs in j order (fp32 fused multiply-adds), rounded to bf16, then the
-// optional residual add in fp32 of the two bf16 values, rounded again.
-template <bool COH = false>
-__device__ __forceinline__ uint2 combine4(const float* __restrict__ y,
-                                          const int32_t* __restrict__ pair_row,
-                                          const float* __restrict__ w, int t, int k, int H, int c,
-                                          const uint16_t* __restrict__ residual) {
+// The weighted sum over token t's pairs in j order (fp32 fused multiply-adds)
+// of four consecutive hidden values; load_y(r) gives them for sorted row r.
+template <typename LoadY>
+__device__ __forceinline__ float4 combine_acc4(LoadY&& load_y, const int32_t* pair_row,
+                                               const float* w, int t, int k) {
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   constexpr int U = 8;
   for (int j0 = 0; j0 < k; j0 += U) {
@@ -25,9 +22,7 @@ __device__ __forceinline__ uint2 combine4(const float* __restrict__ y,
       wj[u] = j < k ? w[(size_t)t * k + j] : 0.0f;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      yv[u] = r[u] >= 0 ? __builtin_bit_cast(float4, hld128<COH>(y, 4 * ((size_t)r[u] * H) + 16 * (size_t)c))
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = 0; u < U; ++u) yv[u] = r[u] >= 0 ? load_y(r[u]) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int u = 0; u < U; ++u) {   // j ascending
       acc.x = __builtin_fmaf(wj[u], yv[u].x, acc.x);
@@ -36,16 +31,37 @@ __device__ __forceinline__ uint2 combine4(const float* __restrict__ y,
       acc.w = __builtin_fmaf(wj[u], yv[u].w, acc.w);
     }
   }
+  return acc;
+}
+
+// The sum rounded to bf16, then (with a residual: rr holds its four bf16
+// values) the residual added in fp32 and rounded again.
+__device__ __forceinline__ uint2 combine_round4(float4 acc, bool has_residual, uint2 rr) {
   uint32_t o0 = f32_to_bf16(acc.x), o1 = f32_to_bf16(acc.y);
   uint32_t o2 = f32_to_bf16(acc.z), o3 = f32_to_bf16(acc.w);
-  if (residual) {
-    const uint2 rr = *reinterpret_cast<const uint2*>(residual + (size_t)t * H + (size_t)c * 4);
+  if (has_residual) {
     o0 = f32_to_bf16(bf16_to_f32(rr.x & 0xFFFFu) + bf16_to_f32(o0));
     o1 = f32_to_bf16(bf16_to_f32(rr.x >> 16) + bf16_to_f32(o1));
     o2 = f32_to_bf16(bf16_to_f32(rr.y & 0xFFFFu) + bf16_to_f32(o2));
     o3 = f32_to_bf16(bf16_to_f32(rr.y >> 16) + bf16_to_f32(o3));
   }
   return make_uint2(o0 | (o1 << 16), o2 | (o3 << 16));
+}
+
+// out values of token t, hidden 4c .. 4c+3, from y_pairs in global memory.
+template <bool COH = false>
+__device__ __forceinline__ uint2 combine4(const float* __restrict__ y,
+                                          const int32_t* __restrict__ pair_row,
+                                          const float* __restrict__ w, int t, int k, int H, int c,
+                                          const uint16_t* __restrict__ residual) {
+  const float4 acc = combine_acc4(
+      [&](int r) {
+        return __builtin_bit_cast(float4, hld128<COH>(y, 4 * ((size_t)r * H) + 16 * (size_t)c));
+      },
+      pair_row, w, t, k);
+  const uint2 rr = residual ? *reinterpret_cast<const uint2*>(residual + (size_t)t * H + (size_t)c * 4)
+                            : make_uint2(0u, 0u);
+  return combine_round4(acc, residual != nullptr, rr);
 }
 
 }  // namespace moe

@@ -99,7 +99,7 @@ __global__ void __launch_bounds__(kPermThreads)
   __shared__ int pfirst[kSmallP];
   __shared__ int s_last;
   const int tid = threadIdx.x, wave = tid / kWave;
-  router_logits_wave<true>(x, wr, bias, T, H, E, blockIdx.x * kPermWaves + wave,
+  router_logits_wave<kPermThreads, true>(x, wr, bias, T, H, E, blockIdx.x * kPermWaves + wave,
                            reinterpret_cast<uint4*>(smem), logits);
   wait_vmem();   // this wave's logits have reached the device-coherent level
   __syncthreads();
@@ -111,14 +111,13 @@ __global__ void __launch_bounds__(kPermThreads)
   __syncthreads();
   if (!s_last) return;
   // ---- the last workgroup: every expert's logits are visible
-  for (int t = wave; t < T; t += kPermWaves) topk_wave<S, true>(logits, t, E, k, ids, tw);
-  __syncthreads();   // ids are written (same workgroup)
   const int P = T * k;
+  for (int t = wave; t < T; t += kPermWaves)
+    topk_wave<S, true>(logits, t, E, k, ids, tw, P <= kSmallP ? pid : nullptr);
+  __syncthreads();   // ids are written (same workgroup)
   if (P <= kSmallP) {
     // Few pairs: each pair's row is (#pairs with a smaller id) + (#earlier pairs
     // with its id), i.e. the stable order; offsets[e] counts the ids below e.
-    if (tid < P) pid[tid] = ids[tid];
-    __syncthreads();
     int e = 0, lt = 0, eq_before = 0, n_eq = 0;
     if (tid < P) {
       e = pid[tid];
@@ -182,7 +181,7 @@ __global__ void __launch_bounds__(kPermThreads)
 // workgroups [G, G + D): down tile of (slot, rb) likewise with nrb_dn.  Slots
 // past the active count exit at once.
 template <int MODE, int GL, int GC, int DL, int DC>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kTileThreads)
     k_experts_decode(FfnArgs a, DecodeState* __restrict__ st, int max_slots, int cols_gu,
                      int cols_dn, const int32_t* __restrict__ pair_row,
                      const float* __restrict__ tw, const uint16_t* __restrict__ residual,
@@ -208,8 +207,9 @@ __global__ void __launch_bounds__(256)
     const int d = wg - G, slot = d / nrb_dn, rb = d % nrb_dn;
     if (slot < n_active) {
       const int4 pl = st->plan[slot];
-      down_tile<MODE, DL, DC, true>(a, pl.x, pl.y, pl.z, rb, cols_dn, lds,
-                                    [&] { wait_at_least(&st->gu_done[slot].v, (uint32_t)nrb_gu, &st->timeouts.v); });
+      down_tile<MODE, DL, DC, true>(a, pl.x, pl.y, pl.z, rb, cols_dn, lds, [&] {
+        wait_at_least(&st->gu_done[slot].v, (uint32_t)nrb_gu, &st->timeouts.v);
+      });
       wait_vmem();   // this wave's y has reached the device-coherent level
       __syncthreads();
       if (tid == 0) {
@@ -220,7 +220,7 @@ __global__ void __launch_bounds__(256)
       __syncthreads();
       if (s_flag) {   // every expert's rows of this block are in: combine them
         const int n4 = kDnRows / 4, c0 = rb * n4;
-        for (int i = tid; i < a.T * n4; i += blockDim.x) {
+        for (int i = tid; i < a.T * n4; i += kTileThreads) {
           const int t = i / n4, c = c0 + i % n4;
           if (4 * c < a.H)
             *reinterpret_cast<uint2*>(out + (size_t)t * a.H + (size_t)c * 4) =
@@ -258,7 +258,7 @@ static void launch_b3(const FfnArgs& a, DecodeState* st, int max_slots, int cols
   const int grid = max_slots * (a.I / kGuRows + (a.H + kDnRows - 1) / kDnRows);
   const size_t lds_gu = (size_t)cols_gu * (a.H / 32) * ChunkLds<MODE>::kStride;
   const size_t lds_dn = (size_t)cols_dn * (a.I / 32) * ChunkLds<MODE>::kStride;
-  hipLaunchKernelGGL((k_experts_decode<MODE, 32, GC, DL, 1>), dim3(grid), dim3(256),
+  hipLaunchKernelGGL((k_experts_decode<MODE, 32, GC, DL, 1>), dim3(grid), dim3(kTileThreads),
                      lds_gu > lds_dn ? lds_gu : lds_dn, s, a, st, max_slots, cols_gu, cols_dn, prow,
                      tw, residual, out);
 }

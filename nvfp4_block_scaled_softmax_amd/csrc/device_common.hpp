@@ -154,6 +154,29 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Copies items 0..n-1 (item i: v = ld(i); st(i, v)) with the workgroup's NT
+// threads, B loads in flight per thread before the first store: a staging loop
+// that stored each value before the next load would pay one memory round trip
+// per item per thread.
+template <int NT, int B, typename Ld, typename St>
+__device__ __forceinline__ void batched_copy(int n, Ld&& ld, St&& st) {
+  using V = decltype(ld(0));
+  for (int i0 = threadIdx.x; i0 < n; i0 += B * NT) {
+    V v[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int i = i0 + b * NT;
+      if (i < n) v[b] = ld(i);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int i = i0 + b * NT;
+      if (i < n) st(i, v[b]);
+    }
+  }
+}
+
+
 // DPP lane moves within rows of 16 (gfx9 encodings): xor 1, xor 2, mirror in 8, mirror in 16.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
@@ -176,6 +199,20 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // Sum over the wave in a fixed order, the same value in every lane.
+// Sum over aligned groups of N lanes (N = 2 .. 32), every lane of a group
+// receiving the group's total: DPP steps within rows of 16 lanes (pairs, quads,
+// halves, rows), one lane shuffle to join two rows.
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16 || N == 32, "group of 2..32 lanes");
+  v += dpp_f32<kDppXor1>(v);
+  if constexpr (N >= 4) v += dpp_f32<kDppXor2>(v);
+  if constexpr (N >= 8) v += dpp_f32<kDppHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp_f32<kDppMirror>(v);
+  if constexpr (N >= 32) v += __shfl_xor(v, 16, kWave);
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f32<kDppXor1>(v);
   v += dpp_f32<kDppXor2>(v);

@@ -40,7 +40,7 @@ __device__ __forceinline__ bool slot_expert(const FfnArgs& a, int* s_info) {
 }
 
 template <int MODE, int LPR, int CPL>
-__global__ void __launch_bounds__(256) k_gateup_narrow(FfnArgs a, int max_cols) {
+__global__ void __launch_bounds__(kTileThreads) k_gateup_narrow(FfnArgs a, int max_cols) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_info[3];
   if (!slot_expert(a, s_info)) return;
@@ -48,26 +48,26 @@ __global__ void __launch_bounds__(256) k_gateup_narrow(FfnArgs a, int max_cols) 
 }
 
 template <int MODE, int LPR, int CPL>
-__global__ void __launch_bounds__(256) k_down_narrow(FfnArgs a, int max_cols) {
+__global__ void __launch_bounds__(kTileThreads) k_down_narrow(FfnArgs a, int max_cols) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_info[3];
   if (!slot_expert(a, s_info)) return;
   down_tile<MODE, LPR, CPL, false>(a, s_info[0], s_info[1], s_info[2], blockIdx.x, max_cols, lds,
-                                   [] {});
+                                   NoHook{});
 }
 
 // ------------------------------------------------------------------ launch
 template <int MODE, int LPR, int CPL>
 static void launch_gu(const FfnArgs& a, int slots, int max_cols, hipStream_t s) {
   const size_t lds = (size_t)max_cols * (a.H / 32) * ChunkLds<MODE>::kStride;
-  hipLaunchKernelGGL((k_gateup_narrow<MODE, LPR, CPL>), dim3(a.I / kGuRows, slots), dim3(256), lds,
+  hipLaunchKernelGGL((k_gateup_narrow<MODE, LPR, CPL>), dim3(a.I / kGuRows, slots), dim3(kTileThreads), lds,
                      s, a, max_cols);
 }
 template <int MODE, int LPR, int CPL>
 static void launch_dn(const FfnArgs& a, int slots, int max_cols, hipStream_t s) {
   const size_t lds = (size_t)max_cols * (a.I / 32) * ChunkLds<MODE>::kStride;
   hipLaunchKernelGGL((k_down_narrow<MODE, LPR, CPL>), dim3((a.H + kDnRows - 1) / kDnRows, slots),
-                     dim3(256), lds, s, a, max_cols);
+                     dim3(kTileThreads), lds, s, a, max_cols);
 }
 
 // Lanes per row and chunks per lane for a reduction length K (K % 32 == 0, K <= 4096).

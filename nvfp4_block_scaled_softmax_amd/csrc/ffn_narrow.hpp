@@ -8,50 +8,80 @@ namespace moe {
 constexpr int kGuRows = 16;    // h rows per gate/up workgroup (= one quantization block)
 constexpr int kDnRows = 64;    // output rows per down workgroup
 constexpr int kLdsBudget = 60 * 1024;
+// Threads of every workgroup that runs these tiles.  A compile-time count: the
+// block size read at run time is a vector memory load, and its wait would also
+// wait for every weight load in flight.
+constexpr int kTileThreads = 256;
 
-template <int MODE>
+constexpr int kStageBatch = 4;
+
+// tok[col]: the token of column col (the 16/8-bit modes read x by token);
+// with BY_TOKEN the columns are the tokens 0..ncol-1 themselves.
+template <int MODE, bool BY_TOKEN = false>
 __device__ void stage_gateup_cols(const FfnArgs& a, int e, int row0, int c0, int ncol,
-                                  uint8_t* lds) {
+                                  const int* tok, uint8_t* lds) {
   constexpr int S = ChunkLds<MODE>::kStride;
   const int H = a.H, NC = H / 32;
-  const int tid = threadIdx.x;
   if (MODE == MOE_A16) {
     // 4 x 16 B per chunk
-    for (int i = tid; i < ncol * NC * 4; i += blockDim.x) {
-      const int col = i / (NC * 4), rem = i % (NC * 4), ch = rem / 4, q = rem % 4;
-      const int t = a.sorted_pairs[row0 + c0 + col] / a.k;
-      const uint4 v = reinterpret_cast<const uint4*>(a.x + (size_t)t * H)[ch * 4 + q];
-      *reinterpret_cast<uint4*>(lds + ((size_t)col * NC + ch) * S + 16 * q) = v;
-    }
+    batched_copy<kTileThreads, kStageBatch>(
+        ncol * NC * 4,
+        [&](int i) {
+          const int col = i / (NC * 4), rem = i % (NC * 4);
+          return reinterpret_cast<const uint4*>(a.x + (size_t)(BY_TOKEN ? col : tok[col]) * H)[rem];
+        },
+        [&](int i, uint4 v) {
+          const int col = i / (NC * 4), rem = i % (NC * 4), ch = rem / 4, q = rem % 4;
+          *reinterpret_cast<uint4*>(lds + ((size_t)col * NC + ch) * S + 16 * q) = v;
+        });
   } else if (MODE == MOE_A8) {
     const float* xs = static_cast<const float*>(a.xq_scales);
-    for (int i = tid; i < ncol * NC * 3; i += blockDim.x) {
-      const int col = i / (NC * 3), rem = i % (NC * 3), ch = rem / 3, q = rem % 3;
-      const int t = a.sorted_pairs[row0 + c0 + col] / a.k;
-      uint8_t* dst = lds + ((size_t)col * NC + ch) * S;
-      if (q < 2) {
-        *reinterpret_cast<uint4*>(dst + 16 * q) =
-            reinterpret_cast<const uint4*>(a.xq_codes + (size_t)t * H)[ch * 2 + q];
-      } else {
-        *reinterpret_cast<float2*>(dst + 32) =
-            *reinterpret_cast<const float2*>(xs + (size_t)t * (H / 16) + ch * 2);
-      }
-    }
+    batched_copy<kTileThreads, kStageBatch>(
+        ncol * NC * 2,
+        [&](int i) {
+          const int col = i / (NC * 2), rem = i % (NC * 2);
+          return reinterpret_cast<const uint4*>(a.xq_codes + (size_t)(BY_TOKEN ? col : tok[col]) * H)[rem];
+        },
+        [&](int i, uint4 v) {
+          const int col = i / (NC * 2), rem = i % (NC * 2), ch = rem / 2, q = rem % 2;
+          *reinterpret_cast<uint4*>(lds + ((size_t)col * NC + ch) * S + 16 * q) = v;
+        });
+    batched_copy<kTileThreads, kStageBatch>(
+        ncol * NC,
+        [&](int i) {
+          const int col = i / NC, ch = i % NC;
+          return *reinterpret_cast<const float2*>(xs + (size_t)(BY_TOKEN ? col : tok[col]) * (H / 16) + ch * 2);
+        },
+        [&](int i, float2 v) {
+          const int col = i / NC, ch = i % NC;
+          *reinterpret_cast<float2*>(lds + ((size_t)col * NC + ch) * S + 32) = v;
+        });
   } else {
     const uint8_t* xs = static_cast<const uint8_t*>(a.xq_scales);
-    for (int i = tid; i < ncol * NC * 3; i += blockDim.x) {
-      const int col = i / (NC * 3), rem = i % (NC * 3), ch = rem / 3, q = rem % 3;
-      const size_t r = (size_t)(row0 + c0 + col);
-      uint8_t* dst = lds + ((size_t)col * NC + ch) * S;
-      if (q < 2) {   // q = matrix (0 gate, 1 up)
-        *reinterpret_cast<uint4*>(dst + 16 * q) =
-            reinterpret_cast<const uint4*>(a.xq_codes + (r * 2 + q) * (H / 2))[ch];
-      } else {
-        const uint16_t sg = *reinterpret_cast<const uint16_t*>(xs + (r * 2 + 0) * (H / 16) + 2 * ch);
-        const uint16_t su = *reinterpret_cast<const uint16_t*>(xs + (r * 2 + 1) * (H / 16) + 2 * ch);
-        *reinterpret_cast<uint32_t*>(dst + 32) = (uint32_t)sg | ((uint32_t)su << 16);
-      }
-    }
+    batched_copy<kTileThreads, kStageBatch>(
+        ncol * NC * 2,
+        [&](int i) {   // (col, matrix, chunk); matrix 0 gate, 1 up
+          const int col = i / (NC * 2), q = (i / NC) % 2, ch = i % NC;
+          const size_t r = (size_t)(row0 + c0 + col);
+          return reinterpret_cast<const uint4*>(a.xq_codes + (r * 2 + q) * (H / 2))[ch];
+        },
+        [&](int i, uint4 v) {
+          const int col = i / (NC * 2), q = (i / NC) % 2, ch = i % NC;
+          *reinterpret_cast<uint4*>(lds + ((size_t)col * NC + ch) * S + 16 * q) = v;
+        });
+    batched_copy<kTileThreads, kStageBatch>(
+        ncol * NC,
+        [&](int i) {
+          const int col = i / NC, ch = i % NC;
+          const size_t r = (size_t)(row0 + c0 + col);
+          const uint16_t sg = *reinterpret_cast<const uint16_t*>(xs + (r * 2 + 0) * (H / 16) + 2 * ch);
+          const uint16_t su = *reinterpret_cast<const uint16_t*>(xs + (r * 2 + 1) * (H / 16) + 2 * ch);
+          return (uint32_t)sg | ((uint32_t)su << 16);
+        },
+        [&](int i, uint32_t v) {
+          const int col = i / NC, ch = i % NC;
+          *reinterpret_cast<uint32_t*>(lds + ((size_t)col * NC + ch) * S + 32) = v;
+        });
   }
 }
 
@@ -59,36 +89,62 @@ template <int MODE, bool COH>
 __device__ void stage_down_cols(const FfnArgs& a, int row0, int c0, int ncol, uint8_t* lds) {
   constexpr int S = ChunkLds<MODE>::kStride;
   const int I = a.I, NC = I / 32;
-  const int tid = threadIdx.x;
   if (MODE == MOE_A16) {
     const uint16_t* h = reinterpret_cast<const uint16_t*>(a.h_codes);
-    for (int i = tid; i < ncol * NC * 4; i += blockDim.x) {
-      const int col = i / (NC * 4), rem = i % (NC * 4), ch = rem / 4, q = rem % 4;
-      const uint4 v = hld128<COH>(h, 2 * ((size_t)(row0 + c0 + col) * I) + 16 * (ch * 4 + q));
-      *reinterpret_cast<uint4*>(lds + ((size_t)col * NC + ch) * S + 16 * q) = v;
-    }
+    batched_copy<kTileThreads, kStageBatch>(
+        ncol * NC * 4,
+        [&](int i) {
+          const int col = i / (NC * 4), rem = i % (NC * 4);
+          return hld128<COH>(h, 2 * ((size_t)(row0 + c0 + col) * I) + 16 * (size_t)rem);
+        },
+        [&](int i, uint4 v) {
+          const int col = i / (NC * 4), rem = i % (NC * 4), ch = rem / 4, q = rem % 4;
+          *reinterpret_cast<uint4*>(lds + ((size_t)col * NC + ch) * S + 16 * q) = v;
+        });
   } else if (MODE == MOE_A8) {
     const float* hs = static_cast<const float*>(a.h_scales);
-    for (int i = tid; i < ncol * NC * 3; i += blockDim.x) {
-      const int col = i / (NC * 3), rem = i % (NC * 3), ch = rem / 3, q = rem % 3;
-      const size_t r = (size_t)(row0 + c0 + col);
-      uint8_t* dst = lds + ((size_t)col * NC + ch) * S;
-      if (q < 2)
-        *reinterpret_cast<uint4*>(dst + 16 * q) = hld128<COH>(a.h_codes, r * I + 16 * (ch * 2 + q));
-      else
-        *reinterpret_cast<uint2*>(dst + 32) = hld64<COH>(hs, 4 * (r * (I / 16) + ch * 2));
-    }
+    batched_copy<kTileThreads, kStageBatch>(
+        ncol * NC * 2,
+        [&](int i) {
+          const int col = i / (NC * 2), rem = i % (NC * 2);
+          return hld128<COH>(a.h_codes, (size_t)(row0 + c0 + col) * I + 16 * (size_t)rem);
+        },
+        [&](int i, uint4 v) {
+          const int col = i / (NC * 2), rem = i % (NC * 2), ch = rem / 2, q = rem % 2;
+          *reinterpret_cast<uint4*>(lds + ((size_t)col * NC + ch) * S + 16 * q) = v;
+        });
+    batched_copy<kTileThreads, kStageBatch>(
+        ncol * NC,
+        [&](int i) {
+          const int col = i / NC, ch = i % NC;
+          return hld64<COH>(hs, 4 * ((size_t)(row0 + c0 + col) * (I / 16) + ch * 2));
+        },
+        [&](int i, uint2 v) {
+          const int col = i / NC, ch = i % NC;
+          *reinterpret_cast<uint2*>(lds + ((size_t)col * NC + ch) * S + 32) = v;
+        });
   } else {
     const uint8_t* hs = static_cast<const uint8_t*>(a.h_scales);
-    for (int i = tid; i < ncol * NC * 2; i += blockDim.x) {
-      const int col = i / (NC * 2), rem = i % (NC * 2), ch = rem / 2, q = rem % 2;
-      const size_t r = (size_t)(row0 + c0 + col);
-      uint8_t* dst = lds + ((size_t)col * NC + ch) * S;
-      if (q == 0)
-        *reinterpret_cast<uint4*>(dst) = hld128<COH>(a.h_codes, r * (I / 2) + 16 * ch);
-      else
-        *reinterpret_cast<uint32_t*>(dst + 32) = hld16<COH>(hs, r * (I / 16) + 2 * ch);
-    }
+    batched_copy<kTileThreads, kStageBatch>(
+        ncol * NC,
+        [&](int i) {
+          const int col = i / NC, ch = i % NC;
+          return hld128<COH>(a.h_codes, (size_t)(row0 + c0 + col) * (I / 2) + 16 * (size_t)ch);
+        },
+        [&](int i, uint4 v) {
+          const int col = i / NC, ch = i % NC;
+          *reinterpret_cast<uint4*>(lds + ((size_t)col * NC + ch) * S) = v;
+        });
+    batched_copy<kTileThreads, kStageBatch>(
+        ncol * NC,
+        [&](int i) {
+          const int col = i / NC, ch = i % NC;
+          return (uint32_t)hld16<COH>(hs, (size_t)(row0 + c0 + col) * (I / 16) + 2 * (size_t)ch);
+        },
+        [&](int i, uint32_t v) {
+          const int col = i / NC, ch = i % NC;
+          *reinterpret_cast<uint32_t*>(lds + ((size_t)col * NC + ch) * S + 32) = v;
+        });
   }
 }
 
@@ -96,11 +152,17 @@ __device__ void stage_down_cols(const FfnArgs& a, int row0, int c0, int ncol, ui
 // One tile: 16 h rows (rb) of expert e; 4 waves; wave w owns h rows 4w..4w+3 of
 // the tile; lanes 0-31 read the gate rows, lanes 32-63 the up rows; within a
 // half-wave, LPR lanes share a row and each reads CPL chunks of it.
+// A callable that does nothing (a tile hook that is not needed).
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
 template <int MODE, int LPR, int CPL, bool COH = false>
 __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, int ne, int rb,
                                             int max_cols, uint8_t* lds) {
   __shared__ float part[8][kGuRows][2];
   __shared__ float hbuf[8][kGuRows];
+  __shared__ int s_tok[8];
   constexpr int S = ChunkLds<MODE>::kStride;
   constexpr int SLOTS = 32 / LPR;
   constexpr int RP = (4 + SLOTS - 1) / SLOTS;
@@ -109,53 +171,75 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, i
   const int i0 = rb * kGuRows;
   const int half = lane >> 5, l32 = lane & 31, slot = l32 / LPR, kl = l32 % LPR;
 
+  // the tokens of the first column group go out before the weights, so that
+  // the x loads (issued after the weights) need not wait for the weights
+  auto col_pair = [&](int c0) {   // the pair of column lane; its token is pair / k
+    const int l = lane_id();
+    return MODE != MOE_A4 && l < min(max_cols, ne - c0) ? a.sorted_pairs[row0 + c0 + l] : 0;
+  };
+  int pair = col_pair(0);
+  __builtin_amdgcn_sched_barrier(0);
   // this lane's weight chunks: RP h rows x CPL chunks, all loads in flight together
   uint4 wq[RP][CPL];
   uint32_t wsc[RP][CPL];
 #pragma unroll
+  // Unconditional loads: lanes past the row's chunks or the wave's four rows
+  // read a clamped (valid) address and their values are never used.  A load
+  // under a branch makes the compiler merge its result with the branch's other
+  // value, and that copy waits for the load before the next one is issued.
   for (int r = 0; r < RP; ++r) {
     const int hl = slot * RP + r;  // h row within the wave's four
-    const size_t grow = (size_t)e * 2 * I + (size_t)half * I + i0 + wave * 4 + hl;
+    const size_t grow = (size_t)e * 2 * I + (size_t)half * I + i0 + wave * 4 + min(hl, 3);
     const uint8_t* crow = a.gu_codes + grow * (H / 2);
     const uint8_t* srow = a.gu_scales + grow * (H / 16);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-      const int c = kl + j * LPR;
-      if (hl < 4 && c < NC) {
-        wq[r][j] = *reinterpret_cast<const uint4*>(crow + 16 * c);
-        wsc[r][j] = *reinterpret_cast<const uint16_t*>(srow + 2 * c);
-      } else {
-        wq[r][j] = make_uint4(0u, 0u, 0u, 0u);
-        wsc[r][j] = 0u;
-      }
+      const int c = min(kl + j * LPR, NC - 1);
+      wq[r][j] = *reinterpret_cast<const uint4*>(crow + 16 * c);
+      wsc[r][j] = *reinterpret_cast<const uint16_t*>(srow + 2 * c);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);   // every load issued before any use of one
+  // Up to max_cols tokens in all (16/8-bit modes): x of every token goes to LDS
+  // now, with no wait for the pairs' tokens, and columns index it by token.
+  const bool by_token = MODE != MOE_A4 && a.T <= max_cols;
+  if (by_token) stage_gateup_cols<MODE, true>(a, e, 0, 0, a.T, nullptr, lds);
   const float wsc_m = a.gu_wscale[2 * e + half];
   const float in_m = MODE == MOE_A4 ? a.gu_inscale[2 * e + half] : 1.0f;
+  const float dn_in = MODE == MOE_A4 ? a.dn_inscale[e] : 0.0f;   // the intermediate's input scale
 
   for (int c0 = 0; c0 < ne; c0 += max_cols) {
     const int ncol = min(max_cols, ne - c0);
+    if (threadIdx.x < ncol) s_tok[threadIdx.x] = pair / a.k;
     __syncthreads();
-    stage_gateup_cols<MODE>(a, e, row0, c0, ncol, lds);
+    if (!by_token) stage_gateup_cols<MODE>(a, e, row0, c0, ncol, s_tok, lds);
     __syncthreads();
     for (int col = 0; col < ncol; ++col) {
-      const uint8_t* xc = lds + (size_t)col * NC * S;
+      const uint8_t* xc = lds + (size_t)(by_token ? s_tok[col] : col) * NC * S;
+      // chunk-outer: each activation chunk is read from LDS once for all rows;
+      // every row still sums its chunks in ascending order
+      float acc[RP];
+#pragma unroll
+      for (int r = 0; r < RP; ++r) acc[r] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int c = kl + j * LPR;
+        if (c < NC) {
+#pragma unroll
+          for (int r = 0; r < RP; ++r)
+            acc[r] += chunk_dot<MODE>(wq[r][j], wsc[r][j], xc + (size_t)c * S, half);
+        }
+      }
 #pragma unroll
       for (int r = 0; r < RP; ++r) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          const int c = kl + j * LPR;
-          if (c < NC) acc += chunk_dot<MODE>(wq[r][j], wsc[r][j], xc + (size_t)c * S, half);
-        }
-        acc = group_sum<LPR>(acc);
+        const float v = lane_group_sum<LPR>(acc[r]);
         const int hl = slot * RP + r;
-        if (kl == 0 && hl < 4) part[col][wave * 4 + hl][half] = acc * wsc_m * in_m;
+        if (kl == 0 && hl < 4) part[col][wave * 4 + hl][half] = v * wsc_m * in_m;
       }
     }
     __syncthreads();
     // SwiGLU and the intermediate in the mode's precision
-    for (int t = threadIdx.x; t < ncol * kGuRows; t += blockDim.x) {
+    for (int t = threadIdx.x; t < ncol * kGuRows; t += kTileThreads) {
       const int col = t / kGuRows, hr = t % kGuRows;
       const float h = swiglu(part[col][hr][0], part[col][hr][1]);
       if (MODE == MOE_A16) {
@@ -176,19 +260,20 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, i
           hst32<COH>(a.h_scales, 4 * (r * (I / 16) + rb), __builtin_bit_cast(uint32_t, sc));
         } else {
           uint32_t lo, hi;
-          const uint32_t sc = nvfp4_quant16(hbuf[col], a.dn_inscale[e], lo, hi);
+          const uint32_t sc = nvfp4_quant16(hbuf[col], dn_in, lo, hi);
           hst64<COH>(a.h_codes, r * (I / 2) + i0 / 2, make_uint2(lo, hi));
           hst8<COH>(a.h_scales, r * (I / 16) + rb, (uint8_t)sc);
         }
       }
     }
+    if (c0 + max_cols < ne) pair = col_pair(c0 + max_cols);
   }
 }
 
 // ------------------------------------------------------------------ down
 // One tile: 64 output rows (rb) of expert e; 4 waves x 16 output rows.
 // wait() runs after the weight loads are issued and before the intermediate is
-// read: the fused decode kernel waits there for the expert's gate/up tiles.
+// read: the fused decode kernel waits there for its expert's gate/up tiles.
 template <int MODE, int LPR, int CPL, bool COH, typename Wait>
 __device__ __forceinline__ void down_tile(const FfnArgs& a, int e, int row0, int ne, int rb,
                                           int max_cols, uint8_t* lds, Wait&& wait) {
@@ -204,23 +289,21 @@ __device__ __forceinline__ void down_tile(const FfnArgs& a, int e, int row0, int
   uint4 wq[RP][CPL];
   uint32_t wsc[RP][CPL];
 #pragma unroll
+  // unconditional loads from clamped addresses, as in gateup_tile: rows past H
+  // are computed from a valid row and never stored
   for (int r = 0; r < RP; ++r) {
     const int orow = o0 + wave * 16 + slot * RP + r;
-    const size_t grow = (size_t)e * H + orow;
+    const size_t grow = (size_t)e * H + min(orow, H - 1);
     const uint8_t* crow = a.dn_codes + grow * (I / 2);
     const uint8_t* srow = a.dn_scales + grow * (I / 16);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-      const int c = kl + j * LPR;
-      if (orow < H && c < NC) {
-        wq[r][j] = *reinterpret_cast<const uint4*>(crow + 16 * c);
-        wsc[r][j] = *reinterpret_cast<const uint16_t*>(srow + 2 * c);
-      } else {
-        wq[r][j] = make_uint4(0u, 0u, 0u, 0u);
-        wsc[r][j] = 0u;
-      }
+      const int c = min(kl + j * LPR, NC - 1);
+      wq[r][j] = *reinterpret_cast<const uint4*>(crow + 16 * c);
+      wsc[r][j] = *reinterpret_cast<const uint16_t*>(srow + 2 * c);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
   const float scale = a.dn_wscale[e] * (MODE == MOE_A4 ? a.dn_inscale[e] : 1.0f);
   wait();
 
@@ -231,20 +314,26 @@ __device__ __forceinline__ void down_tile(const FfnArgs& a, int e, int row0, int
     __syncthreads();
     for (int col = 0; col < ncol; ++col) {
       const uint8_t* xc = lds + (size_t)col * NC * S;
+      float acc[RP];
+#pragma unroll
+      for (int r = 0; r < RP; ++r) acc[r] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int c = kl + j * LPR;
+        if (c < NC) {
+#pragma unroll
+          for (int r = 0; r < RP; ++r)
+            acc[r] += chunk_dot<MODE>(wq[r][j], wsc[r][j], xc + (size_t)c * S, 0);
+        }
+      }
 #pragma unroll
       for (int r = 0; r < RP; ++r) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          const int c = kl + j * LPR;
-          if (c < NC) acc += chunk_dot<MODE>(wq[r][j], wsc[r][j], xc + (size_t)c * S, 0);
-        }
-        acc = group_sum<LPR>(acc);
-        if (kl == 0) outb[col][wave * 16 + slot * RP + r] = acc * scale;
+        const float v = lane_group_sum<LPR>(acc[r]);
+        if (kl == 0) outb[col][wave * 16 + slot * RP + r] = v * scale;
       }
     }
     __syncthreads();
-    for (int t = threadIdx.x; t < ncol * kDnRows; t += blockDim.x) {
+    for (int t = threadIdx.x; t < ncol * kDnRows; t += kTileThreads) {
       const int col = t / kDnRows, o = t % kDnRows;
       if (o0 + o < H)
         hst32<COH>(a.y, 4 * ((size_t)(row0 + c0 + col) * H + o0 + o), __builtin_bit_cast(uint32_t, outb[col][o]));

@@ -22,7 +22,7 @@ __global__ void __launch_bounds__(256) k_router_logits_narrow(const uint16_t* __
                                                               int T, int H, int E,
                                                               float* __restrict__ logits) {
   extern __shared__ __align__(16) uint8_t smem[];
-  router_logits_wave(x, wr, bias, T, H, E, blockIdx.x * 4 + threadIdx.x / kWave,
+  router_logits_wave<256>(x, wr, bias, T, H, E, blockIdx.x * 4 + threadIdx.x / kWave,
                      reinterpret_cast<uint4*>(smem), logits);
 }
 

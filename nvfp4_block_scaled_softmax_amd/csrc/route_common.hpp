@@ -11,7 +11,7 @@ constexpr int kNarrowT = 8;
 // Logits of expert e (this wave) for all T <= 8 tokens.  Every thread of the
 // workgroup calls it (x is staged into xs by all of them); waves with e >= E
 // only help with the staging.
-template <bool COH = false>
+template <int NT, bool COH = false>
 __device__ __forceinline__ void router_logits_wave(const uint16_t* __restrict__ x,
                                                    const uint16_t* __restrict__ wr,
                                                    const float* __restrict__ bias, int T, int H,
@@ -25,12 +25,11 @@ __device__ __forceinline__ void router_logits_wave(const uint16_t* __restrict__ 
   uint4 wv[kMaxChunks];
   const uint4* wrow = reinterpret_cast<const uint4*>(wr + (size_t)(e < E ? e : 0) * H);
 #pragma unroll
-  for (int j = 0; j < kMaxChunks; ++j) {
-    const int c = lane + kWave * j;
-    if (c < nch) wv[j] = wrow[c];
-  }
-  for (int i = threadIdx.x; i < T * nch; i += blockDim.x)
-    xs[i] = reinterpret_cast<const uint4*>(x)[i];
+  for (int j = 0; j < kMaxChunks; ++j) wv[j] = wrow[min(lane + kWave * j, nch - 1)];   // clamped; unused past nch
+  __builtin_amdgcn_sched_barrier(0);
+  batched_copy<NT, 2>(   // NT = threads of the workgroup
+      T * nch, [&](int i) { return reinterpret_cast<const uint4*>(x)[i]; },
+      [&](int i, uint4 v) { xs[i] = v; });
   __syncthreads();
   if (e >= E) return;
   float acc[kNarrowT];
@@ -69,9 +68,12 @@ __device__ __forceinline__ void router_logits_wave(const uint16_t* __restrict__ 
 // Each round: every lane's best free slot (strict >, so a lane keeps its lowest
 // index among equal values), the wave maximum, the lowest lane holding it;
 // that expert is marked taken.  No branches depend on the data.
+// With lds_ids, the chosen experts also go to LDS (same [t][k] layout), for a
+// caller that works on them within the workgroup.
 template <int S, bool COH = false>
 __device__ __forceinline__ void topk_wave(const float* __restrict__ logits, int t, int E, int k,
-                                          int32_t* __restrict__ ids, float* __restrict__ w) {
+                                          int32_t* __restrict__ ids, float* __restrict__ w,
+                                          int* lds_ids = nullptr) {
   const int lane = lane_id();
   const float* row = logits + (size_t)t * E;
   const float ninf = -__builtin_huge_valf();
@@ -111,6 +113,7 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ logits, int 
   if (lane < k) {
     ids[(size_t)t * k + lane] = sel_i;
     w[(size_t)t * k + lane] = __fdiv_rn(ex, sum);
+    if (lds_ids) lds_ids[t * k + lane] = sel_i;
   }
 }
 
