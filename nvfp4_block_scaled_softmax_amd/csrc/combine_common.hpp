@@ -6,7 +6,7 @@ namespace moe {
 
 // The weighted sum over token t's pairs in j order (fp32 fused multiply-adds)
 // of four consecutive hidden values; load_y(r) gives them for sorted row r.
-template <typename LoadY>
+template <bool COH = false, typename LoadY>
 __device__ __forceinline__ float4 combine_acc4(LoadY&& load_y, const int32_t* pair_row,
                                                const float* w, int t, int k) {
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -18,8 +18,8 @@ __device__ __forceinline__ float4 combine_acc4(LoadY&& load_y, const int32_t* pa
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u;
-      r[u] = j < k ? pair_row[(size_t)t * k + j] : -1;
-      wj[u] = j < k ? w[(size_t)t * k + j] : 0.0f;
+      r[u] = j < k ? (int)hld32<COH>(pair_row, 4 * ((size_t)t * k + j)) : -1;
+      wj[u] = j < k ? __builtin_bit_cast(float, hld32<COH>(w, 4 * ((size_t)t * k + j))) : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) yv[u] = r[u] >= 0 ? load_y(r[u]) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -54,7 +54,7 @@ __device__ __forceinline__ uint2 combine4(const float* __restrict__ y,
                                           const int32_t* __restrict__ pair_row,
                                           const float* __restrict__ w, int t, int k, int H, int c,
                                           const uint16_t* __restrict__ residual) {
-  const float4 acc = combine_acc4(
+  const float4 acc = combine_acc4<COH>(
       [&](int r) {
         return __builtin_bit_cast(float4, hld128<COH>(y, 4 * ((size_t)r * H) + 16 * (size_t)c));
       },

@@ -34,6 +34,9 @@
 // The counters live in a small state block of the layer workspace.  It must be
 // zero before the first call; A's last workgroup clears B's counters and then
 // its own, so every call finds them at zero.
+#include <algorithm>
+#include <atomic>
+
 #include "combine_common.hpp"
 #include "ffn_narrow.hpp"
 #include "permute_common.hpp"
@@ -60,9 +63,23 @@ struct DecodeState {
   Counter gu_done[kDecMaxSlots];       // B: gate/up tiles finished, per active expert
   Counter dn_done[kDecMaxRowBlocks];   // B: down tiles finished, per output-row block
   int4 plan[kDecMaxSlots];             // active expert: (expert, first sorted row, rows, 0)
+  // single-launch layer: every slot's plan packed with the call's epoch (see
+  // pack_pub); one copy polled by gate/up tiles, one by down tiles
+  uint64_t pub[2][kDecMaxSlots];
 };
 
 size_t decode_state_bytes() { return sizeof(DecodeState); }
+
+// A published plan entry in one 64-bit word (read and written as one atomic
+// access): bits 0-31 the call's epoch, 32-42 the expert (kNoExpert: the slot
+// is past the active count), 43-46 its rows, 47-53 its first sorted row, 54-61
+// the active count.  Holds for E <= 1024 and up to kSmallP pairs.
+constexpr uint32_t kNoExpert = 0x7FF;
+__device__ __forceinline__ uint64_t pack_pub(uint32_t epoch, uint32_t e, uint32_t rows, uint32_t row0,
+                                             uint32_t n_active) {
+  return (uint64_t)epoch | ((uint64_t)e << 32) | ((uint64_t)rows << 43) | ((uint64_t)row0 << 47) |
+         ((uint64_t)n_active << 54);
+}
 size_t decode_timeouts_offset() { return offsetof(DecodeState, timeouts); }
 
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
@@ -78,6 +95,48 @@ __device__ __forceinline__ void wait_at_least(const uint32_t* p, uint32_t want, 
     if (it >= kSpinCap) __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
+}
+
+// The stable permutation of P <= kSmallP pairs whose experts are in pid (LDS),
+// by all NT threads: a pair's sorted row is (#pairs with a smaller expert) +
+// (#earlier pairs with its expert); offsets[x] counts the experts below x.
+// Fills pfirst (the pair is its expert's first) and splan (active experts in
+// ascending order: expert, first row, rows); returns the active count.  With
+// COH the results are stored device-coherently (read back in the same launch).
+template <int NT, bool COH>
+__device__ int rank_small(const int* pid, int* pfirst, int4* splan, int P, int E,
+                          int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
+                          int32_t* __restrict__ pair_row) {
+  const int tid = threadIdx.x;
+  int e = 0, lt = 0, eq_before = 0, n_eq = 0;
+  if (tid < P) {
+    e = pid[tid];
+    for (int q = 0; q < P; ++q) {
+      const int f = pid[q];
+      lt += f < e;
+      eq_before += (f == e) & (q < tid);
+      n_eq += f == e;
+    }
+    pfirst[tid] = eq_before == 0;
+  }
+  __syncthreads();
+  if (tid < P) {
+    int first_lt = 0;   // distinct experts below e
+    for (int q = 0; q < P; ++q) first_lt += pfirst[q] & (pid[q] < e);
+    const int row = lt + eq_before;
+    hst32<COH>(sorted_pairs, 4 * (size_t)row, (uint32_t)tid);
+    hst32<COH>(pair_row, 4 * (size_t)tid, (uint32_t)row);
+    if (eq_before == 0) splan[first_lt] = make_int4(e, lt, n_eq, 0);
+  }
+  for (int x = tid; x <= E; x += NT) {
+    int below = 0;
+    for (int q = 0; q < P; ++q) below += pid[q] < x;
+    offsets[x] = below;
+  }
+  int n = 0;
+  for (int q = 0; q < P; ++q) n += pfirst[q];
+  __syncthreads();   // splan complete
+  return n;
 }
 
 // ------------------------------------------------------------------ A: routing
@@ -97,6 +156,7 @@ __global__ void __launch_bounds__(kPermThreads)
   __shared__ int wave_tot[kPermWaves];
   __shared__ int pid[kSmallP];
   __shared__ int pfirst[kSmallP];
+  __shared__ int4 splan[kSmallP];
   __shared__ int s_last;
   const int tid = threadIdx.x, wave = tid / kWave;
   router_logits_wave<kPermThreads, true>(x, wr, bias, T, H, E, blockIdx.x * kPermWaves + wave,
@@ -116,38 +176,9 @@ __global__ void __launch_bounds__(kPermThreads)
     topk_wave<S, true>(logits, t, E, k, ids, tw, P <= kSmallP ? pid : nullptr);
   __syncthreads();   // ids are written (same workgroup)
   if (P <= kSmallP) {
-    // Few pairs: each pair's row is (#pairs with a smaller id) + (#earlier pairs
-    // with its id), i.e. the stable order; offsets[e] counts the ids below e.
-    int e = 0, lt = 0, eq_before = 0, n_eq = 0;
-    if (tid < P) {
-      e = pid[tid];
-      for (int q = 0; q < P; ++q) {
-        const int f = pid[q];
-        lt += f < e;
-        eq_before += (f == e) & (q < tid);
-        n_eq += f == e;
-      }
-      pfirst[tid] = eq_before == 0;   // the first pair of its expert
-    }
-    __syncthreads();
-    if (tid < P) {
-      int first_lt = 0;                // distinct experts below e
-      for (int q = 0; q < P; ++q) first_lt += pfirst[q] & (pid[q] < e);
-      const int row = lt + eq_before;
-      sorted_pairs[row] = tid;
-      pair_row[tid] = row;
-      if (eq_before == 0) st->plan[first_lt] = make_int4(e, lt, n_eq, 0);
-    }
-    for (int x = tid; x <= E; x += kPermThreads) {
-      int below = 0;
-      for (int q = 0; q < P; ++q) below += pid[q] < x;
-      offsets[x] = below;
-    }
-    if (tid == 0) {
-      int n = 0;
-      for (int q = 0; q < P; ++q) n += pfirst[q];
-      st->n_active = n;
-    }
+    const int n_act = rank_small<kPermThreads, false>(pid, pfirst, splan, P, E, offsets, sorted_pairs, pair_row);
+    for (int i = tid; i < n_act; i += kPermThreads) st->plan[i] = splan[i];
+    if (tid == 0) st->n_active = n_act;
   } else {
     for (int e = tid; e < E; e += kPermThreads) {
       cnt[e] = 0;
@@ -170,16 +201,70 @@ __global__ void __launch_bounds__(kPermThreads)
     scatter_range(ids, 0, P, E, base, wcnt, sorted_pairs, pair_row);
   }
   // B's counters start at zero: the previous call's B has finished (it ran
-  // before this kernel on the stream); clear what it may have counted
+  // before this kernel on the stream); clear what it may have counted, and the
+  // single-launch entries (epoch 0 matches no call)
+  for (int i = tid; i < 2 * kDecMaxSlots; i += kPermThreads) st->pub[i / kDecMaxSlots][i % kDecMaxSlots] = 0u;
   for (int i = tid; i < kDecMaxSlots; i += kPermThreads) st->gu_done[i].v = 0u;
   for (int i = tid; i < kDecMaxRowBlocks; i += kPermThreads) st->dn_done[i].v = 0u;
   if (tid == 0) __hip_atomic_store(&st->route_done.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ B: experts
-// Workgroups [0, G): gate/up tile (slot, rb) = (i / nrb_gu, i % nrb_gu);
-// workgroups [G, G + D): down tile of (slot, rb) likewise with nrb_dn.  Slots
-// past the active count exit at once.
+// The expert tiles of one call, wg counted from the first expert workgroup:
+// [0, G) gate/up tile (slot, rb) = (wg / nrb_gu, wg % nrb_gu); [G, G + D) down
+// tile of (slot, rb) likewise with nrb_dn.  plan_of(slot, role) gives the
+// slot's (expert, first sorted row, rows, active experts), expert < 0 for a
+// slot past the active count (its tiles exit at once).
+template <int MODE, int GL, int GC, int DL, int DC, typename PlanOf>
+__device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __restrict__ st, int wg,
+                                             int max_slots, int cols_gu, int cols_dn,
+                                             const int32_t* __restrict__ pair_row,
+                                             const float* __restrict__ tw,
+                                             const uint16_t* __restrict__ residual,
+                                             uint16_t* __restrict__ out, uint8_t* lds,
+                                             PlanOf&& plan_of) {
+  __shared__ int s_flag;
+  const int tid = threadIdx.x;
+  const int nrb_gu = a.I / kGuRows, nrb_dn = (a.H + kDnRows - 1) / kDnRows;
+  const int G = max_slots * nrb_gu;
+  if (wg < G) {
+    const int slot = wg / nrb_gu, rb = wg % nrb_gu;
+    const int4 pl = plan_of(slot, 0);
+    if (pl.x < 0) return;
+    gateup_tile<MODE, GL, GC, true>(a, pl.x, pl.y, pl.z, rb, cols_gu, lds);
+    wait_vmem();   // this wave's h has reached the device-coherent level
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_fetch_add(&st->gu_done[slot].v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    const int d = wg - G, slot = d / nrb_dn, rb = d % nrb_dn;
+    const int4 pl = plan_of(slot, 1);
+    if (pl.x < 0) return;
+    down_tile<MODE, DL, DC, true>(a, pl.x, pl.y, pl.z, rb, cols_dn, lds, [&] {
+      wait_at_least(&st->gu_done[slot].v, (uint32_t)nrb_gu, &st->timeouts.v);
+    });
+    wait_vmem();   // this wave's y has reached the device-coherent level
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t c =
+          __hip_atomic_fetch_add(&st->dn_done[rb].v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_flag = c == (uint32_t)pl.w - 1;
+    }
+    __syncthreads();
+    if (s_flag) {   // every expert's rows of this block are in: combine them
+      const int n4 = kDnRows / 4, c0 = rb * n4;
+      for (int i = tid; i < a.T * n4; i += kTileThreads) {
+        const int t = i / n4, c = c0 + i % n4;
+        if (4 * c < a.H)
+          *reinterpret_cast<uint2*>(out + (size_t)t * a.H + (size_t)c * 4) =
+              combine4<true>(a.y, pair_row, tw, t, a.k, a.H, c, residual);
+      }
+    }
+  }
+}
+
+// The expert half on its own: the routing kernel has finished, so the plan is
+// read with plain loads.
 template <int MODE, int GL, int GC, int DL, int DC>
 __global__ void __launch_bounds__(kTileThreads)
     k_experts_decode(FfnArgs a, DecodeState* __restrict__ st, int max_slots, int cols_gu,
@@ -187,48 +272,108 @@ __global__ void __launch_bounds__(kTileThreads)
                      const float* __restrict__ tw, const uint16_t* __restrict__ residual,
                      uint16_t* __restrict__ out) {
   extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ int s_flag;
-  const int tid = threadIdx.x;
-  const int wg = blockIdx.x;
   const int n_active = st->n_active;
-  const int nrb_gu = a.I / kGuRows, nrb_dn = (a.H + kDnRows - 1) / kDnRows;
-  const int G = max_slots * nrb_gu;
-  if (wg < G) {
-    const int slot = wg / nrb_gu, rb = wg % nrb_gu;
-    if (slot < n_active) {
-      const int4 pl = st->plan[slot];
-      gateup_tile<MODE, GL, GC, true>(a, pl.x, pl.y, pl.z, rb, cols_gu, lds);
-      wait_vmem();   // this wave's h has reached the device-coherent level
-      __syncthreads();
-      if (tid == 0)
-        __hip_atomic_fetch_add(&st->gu_done[slot].v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  } else {
-    const int d = wg - G, slot = d / nrb_dn, rb = d % nrb_dn;
-    if (slot < n_active) {
-      const int4 pl = st->plan[slot];
-      down_tile<MODE, DL, DC, true>(a, pl.x, pl.y, pl.z, rb, cols_dn, lds, [&] {
-        wait_at_least(&st->gu_done[slot].v, (uint32_t)nrb_gu, &st->timeouts.v);
+  expert_tiles<MODE, GL, GC, DL, DC>(
+      a, st, blockIdx.x, max_slots, cols_gu, cols_dn, pair_row, tw, residual, out, lds,
+      [&](int slot, int) {
+        if (slot >= n_active) return make_int4(-1, 0, 0, 0);
+        const int4 pl = st->plan[slot];
+        return make_int4(pl.x, pl.y, pl.z, n_active);
       });
-      wait_vmem();   // this wave's y has reached the device-coherent level
-      __syncthreads();
-      if (tid == 0) {
-        const uint32_t c =
-            __hip_atomic_fetch_add(&st->dn_done[rb].v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_flag = c == (uint32_t)n_active - 1;
-      }
-      __syncthreads();
-      if (s_flag) {   // every expert's rows of this block are in: combine them
-        const int n4 = kDnRows / 4, c0 = rb * n4;
-        for (int i = tid; i < a.T * n4; i += kTileThreads) {
-          const int t = i / n4, c = c0 + i % n4;
-          if (4 * c < a.H)
-            *reinterpret_cast<uint2*>(out + (size_t)t * a.H + (size_t)c * 4) =
-                combine4<true>(a.y, pair_row, tw, t, a.k, a.H, c, residual);
-        }
-      }
+}
+
+// ------------------------------------------------------------------ A + B in one launch
+// Up to kSmallP pairs: workgroups [0, R) compute the router logits (one expert
+// per wave) and the last of them runs top-k and the permutation; the expert
+// tiles follow.  The last routing workgroup publishes each slot's plan entry
+// stamped with this call's epoch (a number the host does not reuse, never 0); expert
+// tiles poll their slot's entry until the stamp matches.  Everything they read
+// from the routing tail (sorted pairs, pair rows, weights) is stored
+// device-coherently and complete before any entry is written; an entry and its
+// stamp are one 64-bit word, written and polled as one atomic access.  Every
+// entry is rewritten each call, so a stale one holds the previous call's epoch.
+// The counters of the expert half are cleared by the routing tail before it
+// publishes, as the two-launch path clears them in the routing kernel.
+template <int S, int MODE, int GL, int GC, int DL, int DC>
+__global__ void __launch_bounds__(kTileThreads)
+    k_layer_decode(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                   const float* __restrict__ bias, float* __restrict__ logits,
+                   int32_t* __restrict__ ids, float* __restrict__ tw, FfnArgs a,
+                   DecodeState* __restrict__ st, int max_slots, int cols_gu, int cols_dn,
+                   int32_t* __restrict__ pair_row, const uint16_t* __restrict__ residual,
+                   uint16_t* __restrict__ out, uint32_t epoch) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int pid[kSmallP];
+  __shared__ int pfirst[kSmallP];
+  __shared__ int4 splan[kSmallP];
+  __shared__ int4 s_pl;
+  __shared__ int s_last;
+  const int tid = threadIdx.x, wave = tid / kWave;
+  const int T = a.T, H = a.H, E = a.E, k = a.k, P = T * k;
+  const int R = (E + kTileWaves - 1) / kTileWaves;
+  const int wg = blockIdx.x;
+  if (wg < R) {
+    router_logits_wave<kTileThreads, true>(x, wr, bias, T, H, E, wg * kTileWaves + wave,
+                                           reinterpret_cast<uint4*>(lds), logits);
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t done =
+          __hip_atomic_fetch_add(&st->route_done.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = done == (uint32_t)R - 1;
     }
+    __syncthreads();
+    if (!s_last) return;
+    for (int t = wave; t < T; t += kTileWaves) topk_wave<S, true>(logits, t, E, k, ids, tw, pid);
+    __syncthreads();
+    const int n_act = rank_small<kTileThreads, true>(pid, pfirst, splan, P, E,
+                                                     const_cast<int32_t*>(a.offsets),
+                                                     const_cast<int32_t*>(a.sorted_pairs), pair_row);
+    // the expert half's counters (left by the previous call) back to zero
+    const int nrb_dn = (H + kDnRows - 1) / kDnRows;
+    for (int i = tid; i < max_slots; i += kTileThreads)
+      __hip_atomic_store(&st->gu_done[i].v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = tid; i < nrb_dn; i += kTileThreads)
+      __hip_atomic_store(&st->dn_done[i].v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(&st->route_done.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_vmem();
+    __syncthreads();   // every result above is at the device-coherent level
+    // every entry, also those this call does not poll, so that each holds the
+    // previous call's epoch at most
+    for (int i = tid; i < 2 * kDecMaxSlots; i += kTileThreads) {
+      const int slot = i % kDecMaxSlots;
+      const int4 pl = slot < n_act ? splan[slot] : make_int4((int)kNoExpert, 0, 0, 0);
+      __hip_atomic_store(&st->pub[i / kDecMaxSlots][slot],
+                         pack_pub(epoch, (uint32_t)pl.x, (uint32_t)pl.z, (uint32_t)pl.y, (uint32_t)n_act),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
   }
+  expert_tiles<MODE, GL, GC, DL, DC>(
+      a, st, wg - R, max_slots, cols_gu, cols_dn, pair_row, tw, residual, out, lds,
+      [&](int slot, int role) {
+        if (tid == 0) {
+          const uint64_t* e = &st->pub[role][slot];
+          uint32_t it = 0;
+          uint64_t v;
+          while (true) {
+            v = __hip_atomic_load(e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((uint32_t)v == epoch || ++it >= kSpinCap) break;
+            __builtin_amdgcn_s_sleep(4);
+          }
+          const uint32_t ex = (uint32_t)(v >> 32) & 0x7FFu;
+          if ((uint32_t)v != epoch) {
+            __hip_atomic_fetch_add(&st->timeouts.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_pl = make_int4(-1, 0, 0, 0);   // give up on this tile
+          } else {
+            s_pl = ex == kNoExpert ? make_int4(-1, 0, 0, 0)
+                                   : make_int4((int)ex, (int)((v >> 47) & 0x7Fu), (int)((v >> 43) & 0xFu),
+                                               (int)((v >> 54) & 0xFFu));
+          }
+        }
+        __syncthreads();
+        return s_pl;
+      });
 }
 
 // ------------------------------------------------------------------ launch
@@ -286,6 +431,48 @@ static void launch_b(const FfnArgs& a, DecodeState* st, int max_slots, const int
   else launch_b2<MODE, 4>(a, dl, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, s);
 }
 
+// ---- the single-launch layer (16-bit activations, up to kSmallP pairs)
+template <int S, int GC, int DL>
+static void launch_one3(const FfnArgs& a, const uint16_t* x, const uint16_t* wr, const float* bias,
+                        float* logits, int32_t* ids, float* tw, int32_t* prow, DecodeState* st,
+                        const uint16_t* residual, uint16_t* out, uint64_t epoch, hipStream_t s) {
+  const int P = a.T * a.k, max_slots = P < a.E ? P : a.E;
+  const int cols = max(1, min(min(8, a.T), kLdsBudget / ((a.H / 32) * ChunkLds<MOE_A16>::kStride)));
+  const int cols_dn = max(1, min(min(8, a.T), kLdsBudget / ((a.I / 32) * ChunkLds<MOE_A16>::kStride)));
+  const int R = (a.E + kTileWaves - 1) / kTileWaves;
+  const int grid = R + max_slots * (a.I / kGuRows + (a.H + kDnRows - 1) / kDnRows);
+  size_t lds = (size_t)a.T * a.H * 2;
+  lds = std::max(lds, (size_t)cols * (a.H / 32) * ChunkLds<MOE_A16>::kStride);
+  lds = std::max(lds, (size_t)cols_dn * (a.I / 32) * ChunkLds<MOE_A16>::kStride);
+  hipLaunchKernelGGL((k_layer_decode<S, MOE_A16, 32, GC, DL, 1>), dim3(grid), dim3(kTileThreads), lds, s,
+                     x, wr, bias, logits, ids, tw, a, st, max_slots, cols, cols_dn, prow, residual, out,
+                     (uint32_t)epoch);
+}
+
+template <int S, int GC>
+static void launch_one2(int dl, const FfnArgs& a, const uint16_t* x, const uint16_t* wr,
+                        const float* bias, float* logits, int32_t* ids, float* tw, int32_t* prow,
+                        DecodeState* st, const uint16_t* residual, uint16_t* out, uint64_t epoch,
+                        hipStream_t s) {
+  if (dl == 8) launch_one3<S, GC, 8>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
+  else if (dl == 16) launch_one3<S, GC, 16>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
+  else launch_one3<S, GC, 32>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
+}
+
+template <int S>
+static void launch_one(const FfnArgs& a, const uint16_t* x, const uint16_t* wr, const float* bias,
+                       float* logits, int32_t* ids, float* tw, int32_t* prow, DecodeState* st,
+                       const uint16_t* residual, uint16_t* out, uint64_t epoch, hipStream_t s) {
+  const int gc = gu_config(a.H / 32), dl = dn_config(a.I / 32);
+  if (gc == 2) launch_one2<S, 2>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
+  else if (gc == 3) launch_one2<S, 3>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
+  else launch_one2<S, 4>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
+}
+
+// Epochs of single-launch calls: never reused within the process (the
+// workspace starts at zero, so 0 is never one).
+static std::atomic<uint64_t> g_epoch{0};
+
 moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, int stage_mask,
                                const uint16_t* x, const uint16_t* w_router, const float* bias,
                                int T, int k, const uint16_t* residual, uint16_t* out,
@@ -295,6 +482,23 @@ moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, in
   DecodeState* st = static_cast<DecodeState*>(state);
   const int E = w.E, H = w.H;
   moe_status r;
+  if (stage_mask == 3 && mode == MOE_A16 && T * k <= kSmallP) {
+    // one launch, unless the stream is being captured into a graph: a replay
+    // would repeat the epoch baked into the launch, so graphs get two launches
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return check_launch("moe_layer_forward (capture query)");
+    if (cs == hipStreamCaptureStatusNone) {
+      const FfnArgs a = make_ffn_args(w, mode, x, T, k, offsets, sorted, y, ffn_ws);
+      uint64_t epoch;
+      do epoch = ++g_epoch; while ((uint32_t)epoch == 0u);   // 0: a never-written entry
+      if (E <= 64) launch_one<1>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
+      else if (E <= 128) launch_one<2>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
+      else if (E <= 256) launch_one<4>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
+      else if (E <= 512) launch_one<8>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
+      else launch_one<16>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
+      return check_launch("moe_layer_forward (decode layer)");
+    }
+  }
   if (stage_mask & 1) {   // routing, and the activation quantization of the 8/4-bit modes
     if (E <= 64) launch_a<1>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
     else if (E <= 128) launch_a<2>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);

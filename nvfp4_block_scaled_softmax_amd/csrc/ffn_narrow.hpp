@@ -12,6 +12,7 @@ constexpr int kLdsBudget = 60 * 1024;
 // block size read at run time is a vector memory load, and its wait would also
 // wait for every weight load in flight.
 constexpr int kTileThreads = 256;
+constexpr int kTileWaves = kTileThreads / kWave;
 
 constexpr int kStageBatch = 4;
 
@@ -175,7 +176,9 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, i
   // the x loads (issued after the weights) need not wait for the weights
   auto col_pair = [&](int c0) {   // the pair of column lane; its token is pair / k
     const int l = lane_id();
-    return MODE != MOE_A4 && l < min(max_cols, ne - c0) ? a.sorted_pairs[row0 + c0 + l] : 0;
+    return MODE != MOE_A4 && l < min(max_cols, ne - c0)
+               ? (int)hld32<COH>(a.sorted_pairs, 4 * (size_t)(row0 + c0 + l))
+               : 0;
   };
   int pair = col_pair(0);
   __builtin_amdgcn_sched_barrier(0);

@@ -111,8 +111,8 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ logits, int 
   const float ex = lane < k ? expf(sel_v - first_v) : 0.0f;
   const float sum = wave_sum(ex);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = sel_i;
-    w[(size_t)t * k + lane] = __fdiv_rn(ex, sum);
+    hst32<COH>(ids, 4 * ((size_t)t * k + lane), (uint32_t)sel_i);
+    hst32<COH>(w, 4 * ((size_t)t * k + lane), __builtin_bit_cast(uint32_t, __fdiv_rn(ex, sum)));
     if (lds_ids) lds_ids[t * k + lane] = sel_i;
   }
 }
