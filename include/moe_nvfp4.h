@@ -212,9 +212,17 @@ moe_status moe_layer_workspace_layout(moe_act_mode mode, int T, int k, int E, in
  * correct operation and is meant for tests and health checks. */
 size_t moe_layer_wait_timeouts_offset(void);
 
-/* 1 when moe_layer_forward runs the fused two-launch path for these sizes (up
+/* 1 when moe_layer_forward runs the fused decode path for these sizes (up
  * to 8 tokens, H/32 in 33..128, I/32 in 5..32), else 0 (per-stage kernels). */
 int moe_layer_is_fused(int T, int H, int I);
+
+/* Kernel launches of one moe_layer_forward call on a stream that is not being
+ * captured into a graph: 1 for the single-launch decode layer (fused sizes,
+ * MOE_A16, T*k <= 64), 2 or 3 for the fused two-kernel path (routing, the
+ * 8/4-bit activation quantizer, experts + combine), 0 when the per-stage
+ * kernels run.  Under capture the single-launch case takes the two-kernel path:
+ * its launch carries a per-call number that a graph replay would repeat. */
+int moe_layer_launches(moe_act_mode mode, int T, int k, int H, int I);
 size_t moe_layer_workspace_bytes(moe_act_mode mode, int T, int k, int E, int H, int I);
 moe_status moe_layer_forward(const moe_nvfp4_experts* w, moe_act_mode mode, const uint16_t* x,
                              const uint16_t* w_router, const float* router_bias, int T, int k,

@@ -29,7 +29,7 @@ EXPORTS = ("moe_last_error", "moe_route_workspace_bytes", "moe_route_topk",
            "nvfp4_expert_ffn_workspace_bytes", "nvfp4_expert_ffn", "nvfp4_expert_ffn_stage",
            "moe_combine",
            "moe_layer_workspace_bytes", "moe_layer_workspace_layout", "moe_layer_wait_timeouts_offset",
-           "moe_layer_forward", "moe_layer_forward_stage", "moe_layer_is_fused")
+           "moe_layer_forward", "moe_layer_forward_stage", "moe_layer_is_fused", "moe_layer_launches")
 
 
 class MoeError(RuntimeError):
@@ -75,6 +75,7 @@ def lib():
             "moe_layer_workspace_layout": ([_I, _I, _I, _I, _I, _I, ctypes.POINTER(_Z)], _I),
             "moe_layer_wait_timeouts_offset": ([], _Z),
             "moe_layer_is_fused": ([_I, _I, _I], _I),
+            "moe_layer_launches": ([_I, _I, _I, _I, _I], _I),
             "moe_layer_forward_stage": ([ctypes.POINTER(_Experts), _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _Z, _P], _I),
             "moe_layer_forward": ([ctypes.POINTER(_Experts), _I, _P, _P, _P, _I, _I, _P, _P, _P, _Z, _P], _I),
         }
@@ -364,6 +365,11 @@ def moe_layer_forward_stage(experts: Experts, mode, stage, x, w_router, k, bias,
     _check("moe_layer_forward_stage",
            lib().moe_layer_forward_stage(ctypes.byref(s), m, stage, _ptr(x), _ptr(w_router), _ptr(bias), T,
                                          k, _ptr(residual), _ptr(out), _ptr(ws), ws.numel(), _stream()))
+
+
+def layer_launches(mode, T, k, H, I):
+    """Kernel launches of one moe_layer_forward call outside graph capture (0: per-stage path)."""
+    return int(lib().moe_layer_launches(_mode(mode), T, k, H, I))
 
 
 def layer_wait_timeouts(ws):

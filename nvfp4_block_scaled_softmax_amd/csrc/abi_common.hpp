@@ -60,6 +60,7 @@ size_t expert_ffn_workspace(moe_act_mode mode, int T, int k, int H, int I);
 size_t decode_state_bytes();
 size_t decode_timeouts_offset();
 bool decode_fusable(int T, int H, int I);
+int decode_launches(moe_act_mode mode, int T, int k, int H, int I);
 // stage_mask: bit 0 routing (+ activation quantization), bit 1 experts + combine.
 moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, int stage_mask,
                                const uint16_t* x, const uint16_t* w_router, const float* bias,

@@ -396,6 +396,13 @@ bool decode_fusable(int T, int H, int I) {
   return T <= kNarrowT && gu_config(H / 32) > 0 && dn_config(I / 32) > 0;
 }
 
+static bool single_launch(moe_act_mode mode, int T, int k) { return mode == MOE_A16 && T * k <= kSmallP; }
+
+int decode_launches(moe_act_mode mode, int T, int k, int H, int I) {
+  if (T < 1 || k < 1 || !decode_fusable(T, H, I)) return 0;
+  return single_launch(mode, T, k) ? 1 : (mode == MOE_A16 ? 2 : 3);
+}
+
 template <int MODE, int GC, int DL>
 static void launch_b3(const FfnArgs& a, DecodeState* st, int max_slots, int cols_gu, int cols_dn,
                       const int32_t* prow, const float* tw, const uint16_t* residual,
@@ -482,7 +489,7 @@ moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, in
   DecodeState* st = static_cast<DecodeState*>(state);
   const int E = w.E, H = w.H;
   moe_status r;
-  if (stage_mask == 3 && mode == MOE_A16 && T * k <= kSmallP) {
+  if (stage_mask == 3 && single_launch(mode, T, k)) {
     // one launch, unless the stream is being captured into a graph: a replay
     // would repeat the epoch baked into the launch, so graphs get two launches
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;

@@ -56,6 +56,10 @@ extern "C" const char* moe_last_error(void) { return moe::g_error.c_str(); }
 
 extern "C" int moe_layer_is_fused(int T, int H, int I) { return moe::decode_fusable(T, H, I) ? 1 : 0; }
 
+extern "C" int moe_layer_launches(moe_act_mode mode, int T, int k, int H, int I) {
+  return moe::decode_launches(mode, T, k, H, I);
+}
+
 extern "C" size_t moe_layer_wait_timeouts_offset(void) {
   return moe::decode_timeouts_offset();   // the state block is at the start of the workspace
 }

@@ -70,6 +70,15 @@ def test_layer_stage_and_fused_queries():
     assert L.moe_layer_is_fused(1, 3072, 512) == 1 and L.moe_layer_is_fused(8, 3072, 512) == 1
     assert L.moe_layer_is_fused(9, 3072, 512) == 0          # wider calls: per-stage kernels
     assert L.moe_layer_is_fused(1, 256, 128) == 0           # small H/I: per-stage kernels
+    # launches per call: one for 16-bit activations up to 64 pairs, else routing
+    # (+ the activation quantizer) + experts, or the per-stage kernels
+    assert moe.layer_launches("A16", 1, 10, 3072, 512) == 1
+    assert moe.layer_launches("A16", 6, 10, 3072, 512) == 1
+    assert moe.layer_launches("A16", 7, 10, 3072, 512) == 2
+    assert moe.layer_launches("A8", 2, 10, 3072, 512) == 3
+    assert moe.layer_launches("A4", 8, 10, 3072, 512) == 3
+    assert moe.layer_launches("A16", 9, 10, 3072, 512) == 0
+    assert moe.layer_launches("A16", 1, 2, 256, 128) == 0
     code, text = _err(L.moe_layer_forward_stage(None, 0, 2, P16, P16, None, 1, 2, None, P16, P16, 1 << 20, None))
     assert code == "MOE_E_ARG" and "stage" in text
 
