@@ -99,44 +99,54 @@ __device__ __forceinline__ void wait_at_least(const uint32_t* p, uint32_t want, 
 
 // The stable permutation of P <= kSmallP pairs whose experts are in pid (LDS),
 // by all NT threads: a pair's sorted row is (#pairs with a smaller expert) +
-// (#earlier pairs with its expert); offsets[x] counts the experts below x.
-// Fills pfirst (the pair is its expert's first) and splan (active experts in
-// ascending order: expert, first row, rows); returns the active count.  With
-// COH the results are stored device-coherently (read back in the same launch).
-template <int NT, bool COH>
-__device__ int rank_small(const int* pid, int* pfirst, int4* splan, int P, int E,
-                          int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
-                          int32_t* __restrict__ pair_row) {
-  const int tid = threadIdx.x;
-  int e = 0, lt = 0, eq_before = 0, n_eq = 0;
-  if (tid < P) {
-    e = pid[tid];
+// (#earlier pairs with its expert).  Wave 0 holds one pair per lane and
+// compares through lane reads (no memory round trips); splan gets the active
+// experts in ascending order (expert, first row, rows), *s_n their count, which
+// is returned.  With COH the results are stored device-coherently (read back in
+// the same launch).  The expert offsets are small_offsets' part.
+template <bool COH>
+__device__ int rank_small(const int* pid, int4* splan, int* s_n, int P,
+                          int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_row) {
+  const int tid = threadIdx.x, lane = lane_id();
+  if (tid < kWave) {
+    const bool mine = lane < P;
+    const int e = mine ? pid[lane] : 0x7FFFFFFF;
+    int lt = 0, eq_before = 0, n_eq = 0;
     for (int q = 0; q < P; ++q) {
-      const int f = pid[q];
+      const int f = __builtin_amdgcn_readlane(e, q);
       lt += f < e;
-      eq_before += (f == e) & (q < tid);
+      eq_before += f == e && q < lane;
       n_eq += f == e;
     }
-    pfirst[tid] = eq_before == 0;
+    const unsigned long long first = __ballot(mine && eq_before == 0);   // each expert's first pair
+    int first_lt = 0;                                                    // distinct experts below e
+    for (int q = 0; q < P; ++q)
+      if ((first >> q) & 1ull) first_lt += __builtin_amdgcn_readlane(e, q) < e;
+    if (mine) {
+      const int row = lt + eq_before;
+      hst32<COH>(sorted_pairs, 4 * (size_t)row, (uint32_t)lane);
+      hst32<COH>(pair_row, 4 * (size_t)lane, (uint32_t)row);
+      if (eq_before == 0) splan[first_lt] = make_int4(e, lt, n_eq, 0);
+    }
+    if (lane == 0) *s_n = __popcll(first);
   }
   __syncthreads();
-  if (tid < P) {
-    int first_lt = 0;   // distinct experts below e
-    for (int q = 0; q < P; ++q) first_lt += pfirst[q] & (pid[q] < e);
-    const int row = lt + eq_before;
-    hst32<COH>(sorted_pairs, 4 * (size_t)row, (uint32_t)tid);
-    hst32<COH>(pair_row, 4 * (size_t)tid, (uint32_t)row);
-    if (eq_before == 0) splan[first_lt] = make_int4(e, lt, n_eq, 0);
+  return *s_n;
+}
+
+// offsets[x] for x = 0..E from the n active experts in splan (ascending): the
+// first row of the first active expert >= x (binary search), or P past the last.
+template <int NT>
+__device__ void small_offsets(const int4* splan, int n, int P, int E, int32_t* __restrict__ offsets) {
+  for (int x = threadIdx.x; x <= E; x += NT) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (splan[mid].x < x) lo = mid + 1;
+      else hi = mid;
+    }
+    offsets[x] = lo < n ? splan[lo].y : P;
   }
-  for (int x = tid; x <= E; x += NT) {
-    int below = 0;
-    for (int q = 0; q < P; ++q) below += pid[q] < x;
-    offsets[x] = below;
-  }
-  int n = 0;
-  for (int q = 0; q < P; ++q) n += pfirst[q];
-  __syncthreads();   // splan complete
-  return n;
 }
 
 // ------------------------------------------------------------------ A: routing
@@ -155,7 +165,7 @@ __global__ void __launch_bounds__(kPermThreads)
   __shared__ int wcnt[kPermWaves][kMaxExperts];
   __shared__ int wave_tot[kPermWaves];
   __shared__ int pid[kSmallP];
-  __shared__ int pfirst[kSmallP];
+  __shared__ int s_n;
   __shared__ int4 splan[kSmallP];
   __shared__ int s_last;
   const int tid = threadIdx.x, wave = tid / kWave;
@@ -176,7 +186,8 @@ __global__ void __launch_bounds__(kPermThreads)
     topk_wave<S, true>(logits, t, E, k, ids, tw, P <= kSmallP ? pid : nullptr);
   __syncthreads();   // ids are written (same workgroup)
   if (P <= kSmallP) {
-    const int n_act = rank_small<kPermThreads, false>(pid, pfirst, splan, P, E, offsets, sorted_pairs, pair_row);
+    const int n_act = rank_small<false>(pid, splan, &s_n, P, sorted_pairs, pair_row);
+    small_offsets<kPermThreads>(splan, n_act, P, E, offsets);
     for (int i = tid; i < n_act; i += kPermThreads) st->plan[i] = splan[i];
     if (tid == 0) st->n_active = n_act;
   } else {
@@ -304,7 +315,7 @@ __global__ void __launch_bounds__(kTileThreads)
                    uint16_t* __restrict__ out, uint32_t epoch) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int pid[kSmallP];
-  __shared__ int pfirst[kSmallP];
+  __shared__ int s_n;
   __shared__ int4 splan[kSmallP];
   __shared__ int4 s_pl;
   __shared__ int s_last;
@@ -326,9 +337,7 @@ __global__ void __launch_bounds__(kTileThreads)
     if (!s_last) return;
     for (int t = wave; t < T; t += kTileWaves) topk_wave<S, true>(logits, t, E, k, ids, tw, pid);
     __syncthreads();
-    const int n_act = rank_small<kTileThreads, true>(pid, pfirst, splan, P, E,
-                                                     const_cast<int32_t*>(a.offsets),
-                                                     const_cast<int32_t*>(a.sorted_pairs), pair_row);
+    const int n_act = rank_small<true>(pid, splan, &s_n, P, const_cast<int32_t*>(a.sorted_pairs), pair_row);
     // the expert half's counters (left by the previous call) back to zero
     const int nrb_dn = (H + kDnRows - 1) / kDnRows;
     for (int i = tid; i < max_slots; i += kTileThreads)
@@ -347,6 +356,8 @@ __global__ void __launch_bounds__(kTileThreads)
                          pack_pub(epoch, (uint32_t)pl.x, (uint32_t)pl.z, (uint32_t)pl.y, (uint32_t)n_act),
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    // the expert offsets are an output only: after the publication
+    small_offsets<kTileThreads>(splan, n_act, P, E, const_cast<int32_t*>(a.offsets));
     return;
   }
   expert_tiles<MODE, GL, GC, DL, DC>(

@@ -13,10 +13,11 @@
 // f16 matrix rate is ample.
 //
 // Work.  The plan lists chunks of at most 32 tokens of one expert; each
-// workgroup computes one chunk against 64 weight rows, so hot experts spread
-// over many workgroups and every workgroup streams its weight rows once.  A
-// wave owns 16 weight rows (gate/up: waves 0-3 gate rows, 4-7 the matching up
-// rows; down: 4 waves of output rows) and up to two 16-token MFMA column tiles.
+// workgroup computes one chunk against a block of weight rows (gate/up: 64 h
+// rows, down: kDownRows output rows), so hot experts spread over many
+// workgroups and every workgroup streams its weight rows once.  A wave owns 16
+// weight rows (gate/up: waves 0-3 gate rows, 4-7 the matching up rows; down:
+// kDownWaves waves of output rows) and up to two 16-token MFMA column tiles.
 //
 // K loop.  Steps of 128: per step a lane loads 16 bytes of codes (32 values)
 // and their two E4M3 scales for its weight row, and the same for its token of
@@ -33,7 +34,12 @@
 namespace moe {
 
 constexpr int kXcds = 8;                     // XCDs of the chip, each with its own L2
-constexpr int kWideRows = 64;                // weight rows per workgroup
+constexpr int kWideRows = 64;                // weight rows per gate/up workgroup
+// Down: K is only I, so a workgroup's fixed costs (plan, staging the chunk's
+// activations, pipeline fill) weigh more; it takes 16 output rows per wave
+// over kDownWaves waves to spread them over more weight bytes.
+constexpr int kDownWaves = 8;
+constexpr int kDownRows = 16 * kDownWaves;
 constexpr int kWideTok = 32;                 // tokens per chunk
 constexpr int kWideTiles = kWideTok / 16;    // MFMA column tiles per chunk
 constexpr int kKStep = 128;                  // K per step
@@ -320,11 +326,11 @@ __device__ __forceinline__ Stager make_stager(int np, int ntt, int K) {
   sg.sm = threadIdx.x / (kWideTok * 8);
   sg.sn = (threadIdx.x / 8) % kWideTok;
   sg.sq = threadIdx.x % 8;
-  const int row = min(sg.sn, np - 1) * NM + sg.sm;
+  const int row = min(sg.sn, np - 1) * NM + min(sg.sm, NM - 1);
   sg.vc = row * (K / 2);
   sg.vs = row * (K / 16);
   sg.K = K;
-  sg.on = sg.sn < 16 * ntt;
+  sg.on = sg.sn < 16 * ntt && sg.sm < NM;   // threads past NM planes only wait at the barriers
   return sg;
 }
 
@@ -395,17 +401,21 @@ __global__ void __launch_bounds__(512) k_gateup_wide_a4(FfnArgs a, const int4* _
 }
 
 // ------------------------------------------------------------------ down
-// Workgroup: one chunk, 64 output rows (wave w: rows o0 = 64 rb + 16w .. +15).
-__global__ void __launch_bounds__(256) k_down_wide_a4(FfnArgs a, const int4* __restrict__ plan,
-                                                      int slots) {
+// Workgroup: one chunk, 16 NW output rows (wave w: rows o0 = 16 NW rb + 16w .. +15).
+// Waves past the first four only wait at the staging barriers (the chunk's
+// activations need 256 staging threads).
+template <int NW>
+__global__ void __launch_bounds__(NW * kWave) k_down_wide_a4(FfnArgs a, const int4* __restrict__ plan,
+                                                            int slots) {
+  constexpr int kRows = 16 * NW;   // output rows of the workgroup: 16 per wave
   __shared__ WideLds<1> lds;
-  const Job job = wide_job(plan, (a.H + kWideRows - 1) / kWideRows, slots);
+  const Job job = wide_job(plan, (a.H + kRows - 1) / kRows, slots);
   if (job.e < 0) return;
   const int e = job.e, row0 = job.row0, np = job.ne;
   const int H = a.H, I = a.I;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
-  const int o0 = job.rb * kWideRows + wave * 16;
+  const int o0 = job.rb * kRows + wave * 16;
   const bool on = o0 < H;
   const size_t row16 = (size_t)e * H + (on ? o0 : H - 16);
   const Rows w = make_rows(a.dn_codes + row16 * (I / 2), a.dn_scales + row16 * (I / 16), 16, I);
@@ -454,8 +464,9 @@ moe_status launch_ffn_wide_a4(const FfnArgs& a, int stage_mask, void* plan_ws, h
     if (st != MOE_OK) return st;
   }
   if (stage_mask & 4) {
-    const int nrb = (a.H + kWideRows - 1) / kWideRows;
-    hipLaunchKernelGGL(k_down_wide_a4, dim3(wide_grid(n, nrb)), dim3(256), 0, s, a, plan, n);
+    const int nrb = (a.H + kDownRows - 1) / kDownRows;
+    hipLaunchKernelGGL(k_down_wide_a4<kDownWaves>, dim3(wide_grid(n, nrb)), dim3(kDownWaves * kWave), 0, s,
+                       a, plan, n);
     return check_launch("nvfp4_expert_ffn (wide down)");
   }
   return MOE_OK;

@@ -63,52 +63,84 @@ __device__ __forceinline__ void router_logits_wave(const uint16_t* __restrict__ 
   }
 }
 
-// One wave per token.  Lane L holds the S contiguous experts L*S .. L*S+S-1, so
-// among lanes tied on the maximum the lowest lane holds the lowest index.
-// Each round: every lane's best free slot (strict >, so a lane keeps its lowest
-// index among equal values), the wave maximum, the lowest lane holding it;
-// that expert is marked taken.  No branches depend on the data.
+// Order-preserving int keys of finite floats (-0 taken as +0): a > b as floats
+// exactly when key(a) > key(b), equal floats give equal keys.
+__device__ __forceinline__ int order_key(float f) {
+  const int b = __float_as_int(f + 0.0f);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float key_value(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// Wave maximum of int keys: DPP steps within rows of 16, then the four rows'
+// maxima on the scalar unit.
+__device__ __forceinline__ int wave_max_key(int v) {
+  v = max(v, dpp_i32<kDppXor1>(v));
+  v = max(v, dpp_i32<kDppXor2>(v));
+  v = max(v, dpp_i32<kDppHalfMirror>(v));
+  v = max(v, dpp_i32<kDppMirror>(v));
+  const int r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const int r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// One wave per token.  Lane L holds the S contiguous experts L*S .. L*S+S-1 and
+// first sorts them by (value descending, index ascending), as 64-bit composites
+// (order key << 32 | S-1-slot).  Each round then takes the wave maximum of the
+// lanes' heads; among lanes tied on it the lowest holds the lowest index, so
+// the lowest such lane wins, and it moves its next expert to the head.  The
+// round's critical path is one wave reduction; no branches depend on the data.
+//
 // With lds_ids, the chosen experts also go to LDS (same [t][k] layout), for a
 // caller that works on them within the workgroup.
 template <int S, bool COH = false>
 __device__ __forceinline__ void topk_wave(const float* __restrict__ logits, int t, int E, int k,
                                           int32_t* __restrict__ ids, float* __restrict__ w,
                                           int* lds_ids = nullptr) {
+  constexpr int kNone = (int)0x80000000;   // below every key of a finite value
   const int lane = lane_id();
   const float* row = logits + (size_t)t * E;
-  const float ninf = -__builtin_huge_valf();
-  float v[S];
-  uint32_t taken = 0u;
+  long long c[S];
 #pragma unroll
   for (int i = 0; i < S; ++i) {
     const int e = lane * S + i;
     const float x = __builtin_bit_cast(float, hld32<COH>(row, 4 * (size_t)(e < E ? e : E - 1)));   // masked below
-    v[i] = e < E ? x : ninf;
-    taken |= (e < E ? 0u : 1u) << i;
+    const int key = e < E ? order_key(x) : kNone;
+    c[i] = (long long)((unsigned long long)(unsigned)key << 32 | (unsigned)(S - 1 - i));
   }
-  float sel_v = 0.0f, first_v = 0.0f;
-  int sel_i = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = ninf;
-    int bs = S;                                   // no free slot
+  // odd-even transposition sort, descending (composites are distinct)
 #pragma unroll
-    for (int i = S - 1; i >= 0; --i) {            // descending: ties end on the lowest slot
-      const bool better = !((taken >> i) & 1u) && v[i] >= bv;
-      bv = better ? v[i] : bv;
-      bs = better ? i : bs;
+  for (int r = 0; r < S; ++r) {
+#pragma unroll
+    for (int i = r & 1; i + 1 < S; i += 2) {
+      const long long a = c[i], b = c[i + 1];
+      const bool sw = b > a;
+      c[i] = sw ? b : a;
+      c[i + 1] = sw ? a : b;
     }
-    const float m = wave_max(bs < S ? bv : ninf);
-    const unsigned long long hit = __ballot(bs < S && bv == m);
-    const int win_lane = __ffsll((long long)hit) - 1;
-    const int win_slot = __builtin_amdgcn_readlane(bs, win_lane);
-    const int win = win_lane * S + win_slot;
-    if (lane == win_lane) taken |= 1u << win_slot;
-    if (j == 0) first_v = m;
-    sel_v = lane == j ? m : sel_v;
-    sel_i = lane == j ? win : sel_i;
+  }
+  int sel_k = 0, sel_i = 0, first_k = 0;
+  for (int j = 0; j < k; ++j) {
+    const int hk = (int)(c[0] >> 32);
+    const int m = wave_max_key(hk);
+    const unsigned long long hit = __ballot(hk == m);
+    const int wl = __ffsll((long long)hit) - 1;
+    const int slot = S - 1 - __builtin_amdgcn_readlane((int)(unsigned)c[0], wl);
+    if (lane == wl) {
+#pragma unroll
+      for (int i = 0; i + 1 < S; ++i) c[i] = c[i + 1];
+      c[S - 1] = (long long)((unsigned long long)(unsigned)kNone << 32);
+    }
+    if (j == 0) first_k = m;
+    sel_k = lane == j ? m : sel_k;
+    sel_i = lane == j ? wl * S + slot : sel_i;
   }
   // renormalised softmax over the chosen logits: exp(l_j - l_max) / sum
-  const float ex = lane < k ? expf(sel_v - first_v) : 0.0f;
+  const float ex = lane < k ? expf(key_value(sel_k) - key_value(first_k)) : 0.0f;
   const float sum = wave_sum(ex);
   if (lane < k) {
     hst32<COH>(ids, 4 * ((size_t)t * k + lane), (uint32_t)sel_i);
