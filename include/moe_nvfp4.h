@@ -25,7 +25,8 @@
  *  - Packed NVFP4 rows hold element 2i in the low nibble of byte i.
  *  - Identical inputs give bitwise-identical outputs (no floating-point
  *    atomics).  Calls are re-entrant; calls on different streams may overlap.
- *  - Shapes: H and I are multiples of 32 and at most 4096; 1 <= k <= E <= 1024.
+ *  - Shapes: H and I are multiples of 32 and at most 4096; 1 <= k <= E <= 1024
+ *    and k <= 64 (routing and the whole layer).
  */
 #ifndef MOE_NVFP4_H
 #define MOE_NVFP4_H

@@ -37,6 +37,7 @@ inline moe_status check_launch(const char* what) {
   } while (0)
 
 constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 64;   // experts per token: one wave lane each in the top-k
 constexpr int kMaxDim = 4096;
 
 inline bool dim_ok(int d) { return d >= 32 && d <= kMaxDim && d % 32 == 0; }

@@ -235,6 +235,9 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
                                              uint16_t* __restrict__ out, uint8_t* lds,
                                              PlanOf&& plan_of) {
   __shared__ int s_flag;
+  __shared__ int s_prow[kDecMaxSlots];            // the combine's pair rows, weights and residual,
+  __shared__ float s_tw[kDecMaxSlots];            // loaded while the tile waits for gate/up
+  __shared__ __align__(8) uint16_t s_res[kNarrowT][kDnRows];
   const int tid = threadIdx.x;
   const int nrb_gu = a.I / kGuRows, nrb_dn = (a.H + kDnRows - 1) / kDnRows;
   const int G = max_slots * nrb_gu;
@@ -252,6 +255,17 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
     const int4 pl = plan_of(slot, 1);
     if (pl.x < 0) return;
     down_tile<MODE, DL, DC, true>(a, pl.x, pl.y, pl.z, rb, cols_dn, lds, [&] {
+      // (the weight loads are out) what a combine of this row block needs, in
+      // case this tile turns out to be the block's last
+      const int P = a.T * a.k;
+      for (int i = tid; i < P; i += kTileThreads) {
+        s_prow[i] = (int)hld32<true>(pair_row, 4 * (size_t)i);
+        s_tw[i] = __builtin_bit_cast(float, hld32<true>(tw, 4 * (size_t)i));
+      }
+      for (int i = tid; i < a.T * kDnRows; i += kTileThreads) {
+        const int t = i / kDnRows, o = rb * kDnRows + i % kDnRows;
+        s_res[t][i % kDnRows] = residual && o < a.H ? residual[(size_t)t * a.H + o] : (uint16_t)0;
+      }
       wait_at_least(&st->gu_done[slot].v, (uint32_t)nrb_gu, &st->timeouts.v);
     });
     wait_vmem();   // this wave's y has reached the device-coherent level
@@ -266,9 +280,16 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
       const int n4 = kDnRows / 4, c0 = rb * n4;
       for (int i = tid; i < a.T * n4; i += kTileThreads) {
         const int t = i / n4, c = c0 + i % n4;
-        if (4 * c < a.H)
+        if (4 * c < a.H) {
+          const float4 acc = combine_acc4(
+              [&](int r) {
+                return __builtin_bit_cast(float4, hld128<true>(a.y, 4 * ((size_t)r * a.H) + 16 * (size_t)c));
+              },
+              s_prow, s_tw, t, a.k);
+          const uint2 rr = *reinterpret_cast<const uint2*>(&s_res[t][4 * (c - c0)]);
           *reinterpret_cast<uint2*>(out + (size_t)t * a.H + (size_t)c * 4) =
-              combine4<true>(a.y, pair_row, tw, t, a.k, a.H, c, residual);
+              combine_round4(acc, residual != nullptr, rr);
+        }
       }
     }
   }

@@ -26,7 +26,7 @@ struct LayerLayout {
 };
 
 static bool layer_layout(moe_act_mode mode, int T, int k, int E, int H, int I, LayerLayout& L) {
-  if (T < 1 || k < 1 || E < 1 || E > kMaxExperts || k > E || !dim_ok(H) || !dim_ok(I) ||
+  if (T < 1 || k < 1 || k > kMaxTopK || E < 1 || E > kMaxExperts || k > E || !dim_ok(H) || !dim_ok(I) ||
       (int64_t)T * k > (1 << 24))
     return false;
   if (mode != MOE_A16 && mode != MOE_A8 && mode != MOE_A4) return false;

@@ -156,7 +156,7 @@ extern "C" moe_status moe_route_topk(const uint16_t* x, const uint16_t* w_router
   MOE_REQUIRE(x && w_router && topk_ids && topk_w && ws, MOE_E_ARG,
               "moe_route_topk: null pointer argument");
   MOE_REQUIRE(T >= 1 && moe::dim_ok(H) && E >= 1 && E <= moe::kMaxExperts && k >= 1 && k <= E &&
-                  k <= moe::kWave,
+                  k <= moe::kMaxTopK,
               MOE_E_SHAPE, "moe_route_topk: bad shape T=%d H=%d E=%d k=%d", T, H, E, k);
   MOE_REQUIRE(moe::aligned(x, 16) && moe::aligned(w_router, 16) && moe::aligned(ws, 16) &&
                   moe::aligned(topk_ids, 4) && moe::aligned(topk_w, 4) &&

@@ -41,6 +41,7 @@ def test_workspace_sizes():
     assert L.nvfp4_expert_ffn_workspace_bytes(moe.MOE_A16, 1, 10, H, I) == 10 * I * 2
     assert L.nvfp4_expert_ffn_workspace_bytes(7, 1, 10, H, I) == 0
     assert L.moe_layer_workspace_bytes(moe.MOE_A16, 1, 10, 512, 3072, 500) == 0   # I % 32 != 0
+    assert L.moe_layer_workspace_bytes(moe.MOE_A16, 1, 65, 512, 3072, 512) == 0   # k <= 64
     lay = moe.layer_workspace_layout("A4", 1024, 10, 512, 3072, 512)
     # a counter block of the fused decode path comes first, at a fixed place
     assert 0 < lay["topk_ids"] <= 128 * 1024 and all(v % 256 == 0 for v in lay.values())
