@@ -206,3 +206,74 @@ def test_stack_layers(dev, mode):
     assert checked >= 1
     _LAYERS.clear()
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ decode edges
+# Shapes at the corners of the fused decode paths (single launch: 16-bit
+# activations, up to 64 pairs; two launches otherwise): a router grid that does
+# not fill its last workgroup, one pair, exactly 64 pairs with shared experts,
+# 1024 experts (16 logits per top-k lane), the widest fused tiles (H=4096,
+# I=1024), and 8-bit activations.  Seeds follow the workload index.
+EDGES = [
+    synth.Workload(20, "edge: E=33", E=33, k=4, H=1056, I=160, T=1, modes=("A16",)),
+    synth.Workload(21, "edge: one pair", E=64, k=1, H=1056, I=160, T=1, modes=("A16",)),
+    synth.Workload(22, "edge: 64 pairs", E=64, k=8, H=1056, I=160, T=8, modes=("A16",)),
+    synth.Workload(23, "edge: E=1024", E=1024, k=6, H=1056, I=160, T=3, modes=("A16",)),
+    synth.Workload(24, "edge: H=4096 I=1024", E=64, k=4, H=4096, I=1024, T=2, modes=("A16",)),
+    synth.Workload(25, "edge: A8", E=40, k=5, H=1056, I=160, T=5, modes=("A8",)),
+]
+
+
+@pytest.mark.parametrize("w", EDGES, ids=[w.name for w in EDGES])
+def test_decode_edges(dev, w):
+    """Full oracle parity of the fused forward on edge shapes, its equality with the
+    per-stage entry points bit for bit, over three token batches on one workspace."""
+    mode = w.modes[0]
+    single = mode == "A16" and w.T * w.k <= 64
+    assert moe.layer_launches(mode, w.T, w.k, w.H, w.I) == (1 if single else (2 if mode == "A16" else 3))
+    ex, router, bias = gpu_layer(w, 0, mode, dev)
+    ws = torch.zeros(moe.layer_workspace_bytes(mode, w.T, w.k, w.E, w.H, w.I), dtype=torch.uint8, device=dev)
+    for batch in range(3):
+        say("edge", w.name, "batch", batch)
+        xg = bench.token_batch(w, batch, dev, w.T)
+        out, _ = moe.moe_layer_forward(ex, mode, xg, router, w.k, bias=bias, residual=xg, ws=ws)
+        ids, tw = moe.moe_route_topk(xg, router, w.k, bias)
+        off, sp, pr = moe.moe_permute(ids, w.E)
+        y, _ = moe.nvfp4_expert_ffn(ex, mode, xg, w.k, off, sp)
+        ref = moe.moe_combine(y, pr, tw, residual=xg)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+        if batch == 0:   # the oracle, on the call without residual
+            out0, ws0 = moe.moe_layer_forward(ex, mode, xg, router, w.k, bias=bias)
+            torch.cuda.synchronize()
+            check_call(w, mode, 0, synth.tokens(w, batch=batch, T=w.T), out0, ws0)
+    assert moe.layer_wait_timeouts(ws) == 0
+
+
+def test_decode_graph_replay(dev):
+    """Under stream capture the layer takes its two-launch form (a replay would
+    repeat the single-launch form's epoch).  Three replays, each with eager
+    single-launch calls and a synchronisation before it, all equal the eager
+    result bit for bit."""
+    w = synth.CONFIGS[1]
+    ex, router, bias = gpu_layer(w, 0, "A16", dev)
+    nws = moe.layer_workspace_bytes("A16", w.T, w.k, w.E, w.H, w.I)
+    ws_g = torch.zeros(nws, dtype=torch.uint8, device=dev)
+    ws_e = torch.zeros(nws, dtype=torch.uint8, device=dev)
+    x_g = bench.token_batch(w, 0, dev).clone()
+    out_g = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev)
+    moe.moe_layer_forward(ex, "A16", x_g, router, w.k, ws=ws_g, out=out_g)   # warm up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_layer_forward(ex, "A16", x_g, router, w.k, ws=ws_g, out=out_g)
+    for rep, batch in enumerate((1, 2, 3)):
+        say("graph replay", rep, "batch", batch)
+        x_new = bench.token_batch(w, batch, dev)
+        ref, _ = moe.moe_layer_forward(ex, "A16", x_new, router, w.k, ws=ws_e)   # eager, one launch
+        x_g.copy_(x_new)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int16), ref.view(torch.int16)), rep
+    assert moe.layer_wait_timeouts(ws_g) == 0 and moe.layer_wait_timeouts(ws_e) == 0
