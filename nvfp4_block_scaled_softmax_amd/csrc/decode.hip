@@ -66,6 +66,9 @@ struct DecodeState {
   // single-launch layer: every slot's plan packed with the call's epoch (see
   // pack_pub); one copy polled by gate/up tiles, one by down tiles
   uint64_t pub[2][kDecMaxSlots];
+  // single-launch layer: the router logits of the call, each tagged with its
+  // epoch ((logit bits << 32) | epoch), [T][E]; the routing tail polls them
+  uint64_t logit_tag[kNarrowT * kMaxExperts];
 };
 
 size_t decode_state_bytes() { return sizeof(DecodeState); }
@@ -339,24 +342,46 @@ __global__ void __launch_bounds__(kTileThreads)
   __shared__ int s_n;
   __shared__ int4 splan[kSmallP];
   __shared__ int4 s_pl;
-  __shared__ int s_last;
   const int tid = threadIdx.x, wave = tid / kWave;
   const int T = a.T, H = a.H, E = a.E, k = a.k, P = T * k;
   const int R = (E + kTileWaves - 1) / kTileWaves;
   const int wg = blockIdx.x;
   if (wg < R) {
-    router_logits_wave<kTileThreads, true>(x, wr, bias, T, H, E, wg * kTileWaves + wave,
-                                           reinterpret_cast<uint4*>(lds), logits);
-    wait_vmem();
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t done =
-          __hip_atomic_fetch_add(&st->route_done.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = done == (uint32_t)R - 1;
+    router_logits_wave<kTileThreads, true, true>(x, wr, bias, T, H, E, wg * kTileWaves + wave,
+                                                 reinterpret_cast<uint4*>(lds), logits,
+                                                 st->logit_tag, epoch);
+    if (wg != R - 1) return;   // the last routing workgroup runs the tail
+    // one wave per token polls the token's E tagged logits until every one
+    // carries this call's epoch (the words are this call's only once they
+    // match), then selects from the values it holds
+    for (int t = wave; t < T; t += kTileWaves) {
+      const uint64_t* row = st->logit_tag + (size_t)t * E;
+      const int lane = lane_id();
+      uint64_t v[S];
+      uint32_t it = 0;
+      while (true) {
+        bool mine = true;
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+          const int e = lane * S + i;
+          v[i] = e < E ? __hip_atomic_load(&row[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : (uint64_t)epoch;
+          mine = mine && (uint32_t)v[i] == epoch;
+        }
+        if (__all(mine)) break;
+        if (++it >= kSpinCap) {
+          if (lane == 0)
+            __hip_atomic_fetch_add(&st->timeouts.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      int key[S];
+#pragma unroll
+      for (int i = 0; i < S; ++i)
+        key[i] = lane * S + i < E ? order_key(__builtin_bit_cast(float, (uint32_t)(v[i] >> 32))) : kNoKey;
+      topk_keys<S, true>(key, t, k, ids, tw, pid);
     }
-    __syncthreads();
-    if (!s_last) return;
-    for (int t = wave; t < T; t += kTileWaves) topk_wave<S, true>(logits, t, E, k, ids, tw, pid);
     __syncthreads();
     const int n_act = rank_small<true>(pid, splan, &s_n, P, const_cast<int32_t*>(a.sorted_pairs), pair_row);
     // the expert half's counters (left by the previous call) back to zero
@@ -365,7 +390,6 @@ __global__ void __launch_bounds__(kTileThreads)
       __hip_atomic_store(&st->gu_done[i].v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int i = tid; i < nrb_dn; i += kTileThreads)
       __hip_atomic_store(&st->dn_done[i].v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid == 0) __hip_atomic_store(&st->route_done.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     wait_vmem();
     __syncthreads();   // every result above is at the device-coherent level
     // every entry, also those this call does not poll, so that each holds the

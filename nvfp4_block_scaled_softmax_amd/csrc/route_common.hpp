@@ -11,12 +11,18 @@ constexpr int kNarrowT = 8;
 // Logits of expert e (this wave) for all T <= 8 tokens.  Every thread of the
 // workgroup calls it (x is staged into xs by all of them); waves with e >= E
 // only help with the staging.
-template <int NT, bool COH = false>
+//
+// With TAG, a logit is not stored as a float but published as one 64-bit word
+// tagged[t * E + e] = (logit bits << 32) | epoch, written as one atomic store, so
+// that a reader polling the words knows when every logit of a call is there.
+template <int NT, bool COH = false, bool TAG = false>
 __device__ __forceinline__ void router_logits_wave(const uint16_t* __restrict__ x,
                                                    const uint16_t* __restrict__ wr,
                                                    const float* __restrict__ bias, int T, int H,
                                                    int E, int e, uint4* xs,
-                                                   float* __restrict__ logits) {
+                                                   float* __restrict__ logits,
+                                                   uint64_t* __restrict__ tagged = nullptr,
+                                                   uint32_t epoch = 0u) {
   const int nch = H / 8;
   const int lane = lane_id();
   // this lane's chunks of the router row go out first (H <= 4096: <= 8 chunks),
@@ -58,7 +64,14 @@ __device__ __forceinline__ void router_logits_wave(const uint16_t* __restrict__ 
   for (int t = 0; t < kNarrowT; ++t) {
     if (t < T) {
       const float v = group_sum<kWave>(acc[t]);
-      if (lane == 0) hst32<COH>(logits, 4 * ((size_t)t * E + e), __builtin_bit_cast(uint32_t, v + b));
+      if constexpr (TAG) {
+        if (lane == 0)
+          __hip_atomic_store(&tagged[(size_t)t * E + e],
+                             (uint64_t)__builtin_bit_cast(uint32_t, v + b) << 32 | epoch,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        if (lane == 0) hst32<COH>(logits, 4 * ((size_t)t * E + e), __builtin_bit_cast(uint32_t, v + b));
+      }
     }
   }
 }
@@ -88,30 +101,25 @@ __device__ __forceinline__ int wave_max_key(int v) {
   return max(max(r0, r1), max(r2, r3));
 }
 
-// One wave per token.  Lane L holds the S contiguous experts L*S .. L*S+S-1 and
-// first sorts them by (value descending, index ascending), as 64-bit composites
-// (order key << 32 | S-1-slot).  Each round then takes the wave maximum of the
-// lanes' heads; among lanes tied on it the lowest holds the lowest index, so
-// the lowest such lane wins, and it moves its next expert to the head.  The
-// round's critical path is one wave reduction; no branches depend on the data.
+// One wave per token.  Lane L holds the S contiguous experts L*S .. L*S+S-1
+// (their order keys in key[], kNoKey past E) and first sorts them by (value
+// descending, index ascending), as 64-bit composites (order key << 32 |
+// S-1-slot).  Each round then takes the wave maximum of the lanes' heads; among
+// lanes tied on it the lowest holds the lowest index, so the lowest such lane
+// wins, and it moves its next expert to the head.  The round's critical path is
+// one wave reduction; no branches depend on the data.
 //
 // With lds_ids, the chosen experts also go to LDS (same [t][k] layout), for a
 // caller that works on them within the workgroup.
+constexpr int kNoKey = (int)0x80000000;   // below every key of a finite value
 template <int S, bool COH = false>
-__device__ __forceinline__ void topk_wave(const float* __restrict__ logits, int t, int E, int k,
-                                          int32_t* __restrict__ ids, float* __restrict__ w,
-                                          int* lds_ids = nullptr) {
-  constexpr int kNone = (int)0x80000000;   // below every key of a finite value
+__device__ __forceinline__ void topk_keys(const int* key, int t, int k, int32_t* __restrict__ ids,
+                                          float* __restrict__ w, int* lds_ids = nullptr) {
   const int lane = lane_id();
-  const float* row = logits + (size_t)t * E;
   long long c[S];
 #pragma unroll
-  for (int i = 0; i < S; ++i) {
-    const int e = lane * S + i;
-    const float x = __builtin_bit_cast(float, hld32<COH>(row, 4 * (size_t)(e < E ? e : E - 1)));   // masked below
-    const int key = e < E ? order_key(x) : kNone;
-    c[i] = (long long)((unsigned long long)(unsigned)key << 32 | (unsigned)(S - 1 - i));
-  }
+  for (int i = 0; i < S; ++i)
+    c[i] = (long long)((unsigned long long)(unsigned)key[i] << 32 | (unsigned)(S - 1 - i));
   // odd-even transposition sort, descending (composites are distinct)
 #pragma unroll
   for (int r = 0; r < S; ++r) {
@@ -133,7 +141,7 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ logits, int 
     if (lane == wl) {
 #pragma unroll
       for (int i = 0; i + 1 < S; ++i) c[i] = c[i + 1];
-      c[S - 1] = (long long)((unsigned long long)(unsigned)kNone << 32);
+      c[S - 1] = (long long)((unsigned long long)(unsigned)kNoKey << 32);
     }
     if (j == 0) first_k = m;
     sel_k = lane == j ? m : sel_k;
@@ -147,6 +155,23 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ logits, int 
     hst32<COH>(w, 4 * ((size_t)t * k + lane), __builtin_bit_cast(uint32_t, __fdiv_rn(ex, sum)));
     if (lds_ids) lds_ids[t * k + lane] = sel_i;
   }
+}
+
+// topk_keys over token t's row of fp32 logits [T][E] in memory.
+template <int S, bool COH = false>
+__device__ __forceinline__ void topk_wave(const float* __restrict__ logits, int t, int E, int k,
+                                          int32_t* __restrict__ ids, float* __restrict__ w,
+                                          int* lds_ids = nullptr) {
+  const int lane = lane_id();
+  const float* row = logits + (size_t)t * E;
+  int key[S];
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const int e = lane * S + i;
+    const float x = __builtin_bit_cast(float, hld32<COH>(row, 4 * (size_t)(e < E ? e : E - 1)));   // masked below
+    key[i] = e < E ? order_key(x) : kNoKey;
+  }
+  topk_keys<S, COH>(key, t, k, ids, w, lds_ids);
 }
 
 }  // namespace moe
