@@ -49,9 +49,12 @@ moe_status launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offs
                           int32_t* sorted_pairs, int32_t* pair_row, void* ws, hipStream_t s);
 size_t permute_workspace(int P, int E);
 // stage_mask: bit 0 activation quantization, bit 1 gate/up + SwiGLU, bit 2 down.
+// pair_row and ids (the permutation's inverse and the top-k ids, both [T*k];
+// nullable together) let the 4-bit x quantization work per token.
 moe_status launch_expert_ffn(const moe_nvfp4_experts& w, moe_act_mode mode, const uint16_t* x,
                              int T, int k, const int32_t* offsets, const int32_t* sorted_pairs,
-                             float* y_pairs, void* ws, int stage_mask, hipStream_t s);
+                             float* y_pairs, void* ws, int stage_mask, hipStream_t s,
+                             const int32_t* pair_row = nullptr, const int32_t* ids = nullptr);
 moe_status launch_combine(const float* y_pairs, const int32_t* pair_row, const float* topk_w,
                           int T, int k, int H, const uint16_t* residual, uint16_t* out,
                           hipStream_t s);

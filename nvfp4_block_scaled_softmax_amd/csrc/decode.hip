@@ -571,7 +571,7 @@ moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, in
     r = check_launch("moe_layer_forward (decode routing)");
     if (r != MOE_OK) return r;
     if (mode != MOE_A16) {   // needs the permutation (4-bit: per pair)
-      r = launch_expert_ffn(w, mode, x, T, k, offsets, sorted, y, ffn_ws, 1, s);
+      r = launch_expert_ffn(w, mode, x, T, k, offsets, sorted, y, ffn_ws, 1, s, prow, ids);
       if (r != MOE_OK) return r;
     }
   }

@@ -38,6 +38,69 @@ __global__ void __launch_bounds__(256) k_quant_x_a4_rows(FfnArgs a) {
   static_cast<uint8_t*>(const_cast<void*>(a.xq_scales))[row * nb + b] = (uint8_t)s;
 }
 
+// 4-bit mode inside the whole layer, where the permutation's pair rows and the
+// top-k ids are at hand: one workgroup per token, one thread per 16-block of H.
+// The token's x block is quantized under the gate and up input scales of each
+// of its pairs' experts and stored to that pair's sorted row (pairs with
+// pair_row < 0 are skipped); a scale equal (bitwise) to the one just used
+// reuses its codes, so a token whose pairs share their input scales is
+// quantized once.  The codes are the same function of (x block, scale) as in
+// k_quant_x_a4_rows.
+__global__ void __launch_bounds__(256) k_quant_x_a4_tokens(FfnArgs a, const int32_t* __restrict__ pair_row,
+                                                           const int32_t* __restrict__ ids) {
+  __shared__ int s_row[kMaxTopK];
+  __shared__ float s_g[kMaxTopK][2];
+  const int t = blockIdx.x, k = a.k, nb = a.H / 16;
+  const uint4* xrow = reinterpret_cast<const uint4*>(a.x + (size_t)t * a.H);
+  const int b0 = threadIdx.x;
+  uint4 u0 = make_uint4(0u, 0u, 0u, 0u), u1 = u0;
+  if (b0 < nb) {   // this thread's first block is on its way while the pairs are staged
+    u0 = xrow[2 * b0];
+    u1 = xrow[2 * b0 + 1];
+  }
+  for (int j = threadIdx.x; j < k; j += blockDim.x) {
+    const size_t p = (size_t)t * k + j;
+    const int r = pair_row[p], e = ids[p];
+    const bool ok = r >= 0 && e >= 0 && e < a.E;
+    s_row[j] = ok ? r : -1;
+    s_g[j][0] = ok ? a.gu_inscale[2 * e] : 0.0f;
+    s_g[j][1] = ok ? a.gu_inscale[2 * e + 1] : 0.0f;
+  }
+  __syncthreads();
+  for (int b = b0; b < nb; b += blockDim.x) {
+    if (b != b0) {
+      u0 = xrow[2 * b];
+      u1 = xrow[2 * b + 1];
+    }
+    float v[16];
+    const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+      v[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+    }
+    uint32_t last_g = 0u, lo = 0u, hi = 0u, sc = 0u;
+    bool have = false;
+    for (int j = 0; j < k; ++j) {
+      const int r = s_row[j];
+      if (r < 0) continue;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const float g = s_g[j][m];
+        if (!have || __float_as_uint(g) != last_g) {
+          sc = nvfp4_quant16(v, g, lo, hi);
+          last_g = __float_as_uint(g);
+          have = true;
+        }
+        const size_t row = (size_t)r * 2 + m;
+        *reinterpret_cast<uint2*>(const_cast<uint8_t*>(a.xq_codes) + row * (a.H / 2) + (size_t)b * 8) =
+            make_uint2(lo, hi);
+        static_cast<uint8_t*>(const_cast<void*>(a.xq_scales))[row * nb + b] = (uint8_t)sc;
+      }
+    }
+  }
+}
+
 size_t expert_ffn_workspace(moe_act_mode mode, int T, int k, int H, int I) {
   return ffn_layout(mode, T, k, H, I).total;
 }
@@ -74,7 +137,8 @@ FfnArgs make_ffn_args(const moe_nvfp4_experts& w, moe_act_mode mode, const uint1
 
 moe_status launch_expert_ffn(const moe_nvfp4_experts& w, moe_act_mode mode, const uint16_t* x,
                              int T, int k, const int32_t* offsets, const int32_t* sorted_pairs,
-                             float* y_pairs, void* ws, int stage_mask, hipStream_t s) {
+                             float* y_pairs, void* ws, int stage_mask, hipStream_t s,
+                             const int32_t* pair_row, const int32_t* ids) {
   const FfnLayout L = ffn_layout(mode, T, k, w.H, w.I);
   uint8_t* base = static_cast<uint8_t*>(ws);
   const FfnArgs a = make_ffn_args(w, mode, x, T, k, offsets, sorted_pairs, y_pairs, ws);
@@ -86,8 +150,14 @@ moe_status launch_expert_ffn(const moe_nvfp4_experts& w, moe_act_mode mode, cons
                                   reinterpret_cast<float*>(base + L.xq_scales), s);
     if (st != MOE_OK) return st;
   } else if (mode == MOE_A4 && (stage_mask & 1)) {
-    const int64_t n = (int64_t)P * 2 * (w.H / 16);
-    hipLaunchKernelGGL(k_quant_x_a4_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    if (pair_row && ids) {
+      const int nb = w.H / 16;
+      hipLaunchKernelGGL(k_quant_x_a4_tokens, dim3(T), dim3(nb < 256 ? (nb + 63) / 64 * 64 : 256), 0, s, a,
+                         pair_row, ids);
+    } else {
+      const int64_t n = (int64_t)P * 2 * (w.H / 16);
+      hipLaunchKernelGGL(k_quant_x_a4_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    }
     moe_status st = check_launch("nvfp4_expert_ffn (x quantization)");
     if (st != MOE_OK) return st;
   }

@@ -121,7 +121,7 @@ static moe_status layer_call(const char* name, const moe_nvfp4_experts* w, moe_a
       return st;
     if ((st = moe::launch_permute(ids, T, k, w->E, offs, sorted, prow, b + L.route, s)) != MOE_OK)
       return st;
-    if ((st = moe::launch_expert_ffn(*w, mode, x, T, k, offs, sorted, y, b + L.ffn, 1, s)) != MOE_OK)
+    if ((st = moe::launch_expert_ffn(*w, mode, x, T, k, offs, sorted, y, b + L.ffn, 1, s, prow, ids)) != MOE_OK)
       return st;
   }
   if (stage_mask & 2) {

@@ -33,12 +33,10 @@ def test_workspace_sizes():
     L = moe.lib()
     assert L.moe_route_workspace_bytes(8, 512) == 8 * 512 * 4
     assert L.moe_route_workspace_bytes(0, 512) == 0
-    # 4-bit mode: x codes/scales per pair and matrix, h codes/scales per pair, work plan,
-    # each pair's (sorted row, expert)
+    # 4-bit mode: x codes/scales per pair and matrix, h codes/scales per pair, work plan
     P, H, I = 80, 3072, 512
     want = sum((n + 255) // 256 * 256
-               for n in (P * 2 * H // 2, P * 2 * H // 16, P * I // 2, P * I // 16, (min(P, 1024) + P // 32) * 16,
-                         P * 8))
+               for n in (P * 2 * H // 2, P * 2 * H // 16, P * I // 2, P * I // 16, (min(P, 1024) + P // 32) * 16))
     assert L.nvfp4_expert_ffn_workspace_bytes(moe.MOE_A4, 8, 10, H, I) == want
     assert L.nvfp4_expert_ffn_workspace_bytes(moe.MOE_A16, 1, 10, H, I) == 10 * I * 2
     assert L.nvfp4_expert_ffn_workspace_bytes(7, 1, 10, H, I) == 0
