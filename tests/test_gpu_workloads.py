@@ -250,6 +250,48 @@ def test_decode_edges(dev, w):
     assert moe.layer_wait_timeouts(ws) == 0
 
 
+# Tied router logits in the single-launch routing tail: an all-zero router
+# (every logit 0: ids 0..k-1, weights 1/k) at E=512 (8 logits per top-k lane)
+# and E=40 (one per lane, lanes past E empty), and router rows repeated in groups
+# of 4, which puts equal logits within a lane and across lanes.
+TIED = [
+    (synth.Workload(26, "ties: zero router, E=512", E=512, k=10, H=1056, I=160, T=1, modes=("A16",)), 0),
+    (synth.Workload(27, "ties: rows in groups of 4, E=512", E=512, k=10, H=1056, I=160, T=4, modes=("A16",)), 4),
+    (synth.Workload(28, "ties: zero router, E=40", E=40, k=5, H=1056, I=160, T=3, modes=("A16",)), 0),
+]
+
+
+@pytest.mark.parametrize("w,group", TIED, ids=[w.name for w, _ in TIED])
+def test_decode_tied_logits(dev, w, group):
+    """Routing of the single-launch layer with exactly tied logits: the oracle's
+    ids (ties to the lower expert), and the output equal to the per-stage entry
+    points' bit for bit."""
+    assert moe.layer_launches("A16", w.T, w.k, w.H, w.I) == 1
+    ex, _, _ = gpu_layer(w, 0, "A16", dev)
+    wr = synth.router_weight(w, 0)
+    wr = np.zeros_like(wr) if group == 0 else np.ascontiguousarray(np.repeat(wr[::group], group, axis=0)[:w.E])
+    router = torch.from_numpy(wr.view(np.int16)).to(dev).view(torch.bfloat16)
+    ws = torch.zeros(moe.layer_workspace_bytes("A16", w.T, w.k, w.E, w.H, w.I), dtype=torch.uint8, device=dev)
+    for batch in range(2):
+        say("tied", w.name, "batch", batch)
+        xg = bench.token_batch(w, batch, dev, w.T)
+        out, _ = moe.moe_layer_forward(ex, "A16", xg, router, w.k, ws=ws)
+        ids, tw = moe.moe_route_topk(xg, router, w.k)
+        off, sp, pr = moe.moe_permute(ids, w.E)
+        y, _ = moe.nvfp4_expert_ffn(ex, "A16", xg, w.k, off, sp)
+        ref = moe.moe_combine(y, pr, tw)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+        v = moe.workspace_views(ws, "A16", w.T, w.k, w.E, w.H, w.I)
+        ids_h, w_h = host(v["topk_ids"]), host(v["topk_w"])
+        r, flipped = parity.check_route(synth.tokens(w, batch=batch, T=w.T), wr, None, w.k, ids_h, w_h)
+        assert np.array_equal(ids_h, r.ids) and not flipped
+        if group == 0:
+            assert np.array_equal(ids_h, np.tile(np.arange(w.k), (w.T, 1)))
+            assert np.all(w_h == np.float32(1.0) / np.float32(w.k))
+    assert moe.layer_wait_timeouts(ws) == 0
+
+
 def test_decode_graph_replay(dev):
     """Under stream capture the layer takes its two-launch form (a replay would
     repeat the single-launch form's epoch).  Three replays, each with eager
