@@ -59,6 +59,8 @@ struct alignas(128) Counter {
 struct DecodeState {
   Counter route_done;                  // A: workgroups finished
   Counter timeouts;                    // waits that reached the spin cap (stays 0)
+  Counter outs_epoch;                  // single launch: epoch of the call whose routing outputs
+                                       // (ids, weights, sorted pairs, pair rows) are complete
   int32_t n_active;                    // active experts (written by A)
   Counter gu_done[kDecMaxSlots];       // B: gate/up tiles finished, per active expert
   Counter dn_done[kDecMaxRowBlocks];   // B: down tiles finished, per output-row block
@@ -75,14 +77,24 @@ size_t decode_state_bytes() { return sizeof(DecodeState); }
 
 // A published plan entry in one 64-bit word (read and written as one atomic
 // access): bits 0-31 the call's epoch, 32-42 the expert (kNoExpert: the slot
-// is past the active count), 43-46 its rows, 47-53 its first sorted row, 54-61
-// the active count.  Holds for E <= 1024 and up to kSmallP pairs.
+// is past the active count), 43-50 the mask of its tokens (an expert's sorted
+// rows are its tokens in ascending order, so the mask gives the rows and their
+// tokens), 51-56 the active count - 1, 57-62 its first sorted row.  Holds for
+// E <= 1024, T <= 8 and up to kSmallP pairs.
 constexpr uint32_t kNoExpert = 0x7FF;
-__device__ __forceinline__ uint64_t pack_pub(uint32_t epoch, uint32_t e, uint32_t rows, uint32_t row0,
+__device__ __forceinline__ uint64_t pack_pub(uint32_t epoch, uint32_t e, uint32_t tmask, uint32_t row0,
                                              uint32_t n_active) {
-  return (uint64_t)epoch | ((uint64_t)e << 32) | ((uint64_t)rows << 43) | ((uint64_t)row0 << 47) |
-         ((uint64_t)n_active << 54);
+  return (uint64_t)epoch | ((uint64_t)e << 32) | ((uint64_t)tmask << 43) | ((uint64_t)(n_active - 1) << 51) |
+         ((uint64_t)row0 << 57);
 }
+
+// One slot of the expert half: its expert (< 0: no work), first sorted row,
+// rows, the call's active experts, the mask of its tokens (-1: read them from
+// sorted_pairs), and the epoch a combine waits for in outs_epoch (0: none).
+struct SlotPlan {
+  int e, row0, rows, n_active, tmask;
+  uint32_t outs_epoch;
+};
 size_t decode_timeouts_offset() { return offsetof(DecodeState, timeouts); }
 
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
@@ -100,26 +112,34 @@ __device__ __forceinline__ void wait_at_least(const uint32_t* p, uint32_t want, 
   __syncthreads();
 }
 
-// The stable permutation of P <= kSmallP pairs whose experts are in pid (LDS),
-// by all NT threads: a pair's sorted row is (#pairs with a smaller expert) +
-// (#earlier pairs with its expert).  Wave 0 holds one pair per lane and
-// compares through lane reads (no memory round trips); splan gets the active
-// experts in ascending order (expert, first row, rows), *s_n their count, which
-// is returned.  With COH the results are stored device-coherently (read back in
-// the same launch).  The expert offsets are small_offsets' part.
+// The stable permutation of P <= kSmallP pairs (of T <= 8 tokens) whose experts
+// are in pid (LDS), by all NT threads: a pair's sorted row is (#pairs with a
+// smaller expert) + (#earlier pairs with its expert).  Wave 0 holds one pair per
+// lane and compares through lane reads (no memory round trips); splan gets the
+// active experts in ascending order (expert, first row, rows, mask of their
+// tokens), *s_n their count, which is returned.  The sorted pairs and pair rows
+// go to memory (device-coherently with COH: read back in the same launch), or,
+// with null pointers, to LDS only (lds_sorted / lds_prow).  The expert offsets
+// are small_offsets' part.
 template <bool COH>
-__device__ int rank_small(const int* pid, int4* splan, int* s_n, int P,
-                          int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_row) {
+__device__ int rank_small(const int* pid, int4* splan, int* s_n, int P, int k,
+                          int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_row,
+                          int* lds_sorted = nullptr, int* lds_prow = nullptr) {
   const int tid = threadIdx.x, lane = lane_id();
   if (tid < kWave) {
     const bool mine = lane < P;
     const int e = mine ? pid[lane] : 0x7FFFFFFF;
-    int lt = 0, eq_before = 0, n_eq = 0;
-    for (int q = 0; q < P; ++q) {
+    int lt = 0, eq_before = 0, n_eq = 0, tmask = 0;
+    for (int q = 0, tq = 0, jq = 0; q < P; ++q) {   // pair q is token tq's jq-th
       const int f = __builtin_amdgcn_readlane(e, q);
       lt += f < e;
       eq_before += f == e && q < lane;
       n_eq += f == e;
+      tmask |= (int)(f == e) << tq;
+      if (++jq == k) {
+        jq = 0;
+        ++tq;
+      }
     }
     const unsigned long long first = __ballot(mine && eq_before == 0);   // each expert's first pair
     int first_lt = 0;                                                    // distinct experts below e
@@ -127,9 +147,14 @@ __device__ int rank_small(const int* pid, int4* splan, int* s_n, int P,
       if ((first >> q) & 1ull) first_lt += __builtin_amdgcn_readlane(e, q) < e;
     if (mine) {
       const int row = lt + eq_before;
-      hst32<COH>(sorted_pairs, 4 * (size_t)row, (uint32_t)lane);
-      hst32<COH>(pair_row, 4 * (size_t)lane, (uint32_t)row);
-      if (eq_before == 0) splan[first_lt] = make_int4(e, lt, n_eq, 0);
+      if (sorted_pairs) {
+        hst32<COH>(sorted_pairs, 4 * (size_t)row, (uint32_t)lane);
+        hst32<COH>(pair_row, 4 * (size_t)lane, (uint32_t)row);
+      } else {
+        lds_sorted[row] = lane;
+        lds_prow[lane] = row;
+      }
+      if (eq_before == 0) splan[first_lt] = make_int4(e, lt, n_eq, tmask);
     }
     if (lane == 0) *s_n = __popcll(first);
   }
@@ -189,7 +214,7 @@ __global__ void __launch_bounds__(kPermThreads)
     topk_wave<S, true>(logits, t, E, k, ids, tw, P <= kSmallP ? pid : nullptr);
   __syncthreads();   // ids are written (same workgroup)
   if (P <= kSmallP) {
-    const int n_act = rank_small<false>(pid, splan, &s_n, P, sorted_pairs, pair_row);
+    const int n_act = rank_small<false>(pid, splan, &s_n, P, k, sorted_pairs, pair_row);
     small_offsets<kPermThreads>(splan, n_act, P, E, offsets);
     for (int i = tid; i < n_act; i += kPermThreads) st->plan[i] = splan[i];
     if (tid == 0) st->n_active = n_act;
@@ -227,8 +252,8 @@ __global__ void __launch_bounds__(kPermThreads)
 // The expert tiles of one call, wg counted from the first expert workgroup:
 // [0, G) gate/up tile (slot, rb) = (wg / nrb_gu, wg % nrb_gu); [G, G + D) down
 // tile of (slot, rb) likewise with nrb_dn.  plan_of(slot, role) gives the
-// slot's (expert, first sorted row, rows, active experts), expert < 0 for a
-// slot past the active count (its tiles exit at once).
+// slot's SlotPlan, expert < 0 for a slot past the active count (its tiles exit
+// at once).
 template <int MODE, int GL, int GC, int DL, int DC, typename PlanOf>
 __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __restrict__ st, int wg,
                                              int max_slots, int cols_gu, int cols_dn,
@@ -246,20 +271,30 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
   const int G = max_slots * nrb_gu;
   if (wg < G) {
     const int slot = wg / nrb_gu, rb = wg % nrb_gu;
-    const int4 pl = plan_of(slot, 0);
-    if (pl.x < 0) return;
-    gateup_tile<MODE, GL, GC, true>(a, pl.x, pl.y, pl.z, rb, cols_gu, lds);
+    const SlotPlan pl = plan_of(slot, 0);
+    if (pl.e < 0) return;
+    gateup_tile<MODE, GL, GC, true>(a, pl.e, pl.row0, pl.rows, rb, cols_gu, lds, pl.tmask);
     wait_vmem();   // this wave's h has reached the device-coherent level
     __syncthreads();
     if (tid == 0)
       __hip_atomic_fetch_add(&st->gu_done[slot].v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
     const int d = wg - G, slot = d / nrb_dn, rb = d % nrb_dn;
-    const int4 pl = plan_of(slot, 1);
-    if (pl.x < 0) return;
-    down_tile<MODE, DL, DC, true>(a, pl.x, pl.y, pl.z, rb, cols_dn, lds, [&] {
+    const SlotPlan pl = plan_of(slot, 1);
+    if (pl.e < 0) return;
+    down_tile<MODE, DL, DC, true>(a, pl.e, pl.row0, pl.rows, rb, cols_dn, lds, [&] {
       // (the weight loads are out) what a combine of this row block needs, in
-      // case this tile turns out to be the block's last
+      // case this tile turns out to be the block's last; in the single launch
+      // the routing outputs are complete once outs_epoch holds the call's epoch
+      if (pl.outs_epoch != 0u) {
+        if (tid == 0) {
+          uint32_t it = 0;
+          while (ld_relaxed(&st->outs_epoch.v) != pl.outs_epoch && ++it < kSpinCap) __builtin_amdgcn_s_sleep(2);
+          if (it >= kSpinCap)
+            __hip_atomic_fetch_add(&st->timeouts.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+      }
       const int P = a.T * a.k;
       for (int i = tid; i < P; i += kTileThreads) {
         s_prow[i] = (int)hld32<true>(pair_row, 4 * (size_t)i);
@@ -276,7 +311,7 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
     if (tid == 0) {
       const uint32_t c =
           __hip_atomic_fetch_add(&st->dn_done[rb].v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_flag = c == (uint32_t)pl.w - 1;
+      s_flag = c == (uint32_t)pl.n_active - 1;
     }
     __syncthreads();
     if (s_flag) {   // every expert's rows of this block are in: combine them
@@ -311,9 +346,9 @@ __global__ void __launch_bounds__(kTileThreads)
   expert_tiles<MODE, GL, GC, DL, DC>(
       a, st, blockIdx.x, max_slots, cols_gu, cols_dn, pair_row, tw, residual, out, lds,
       [&](int slot, int) {
-        if (slot >= n_active) return make_int4(-1, 0, 0, 0);
+        if (slot >= n_active) return SlotPlan{-1, 0, 0, 0, -1, 0u};
         const int4 pl = st->plan[slot];
-        return make_int4(pl.x, pl.y, pl.z, n_active);
+        return SlotPlan{pl.x, pl.y, pl.z, n_active, -1, 0u};
       });
 }
 
@@ -322,13 +357,21 @@ __global__ void __launch_bounds__(kTileThreads)
 // per wave) and the last of them runs top-k and the permutation; the expert
 // tiles follow.  The last routing workgroup publishes each slot's plan entry
 // stamped with this call's epoch (a number the host does not reuse, never 0); expert
-// tiles poll their slot's entry until the stamp matches.  Everything they read
-// from the routing tail (sorted pairs, pair rows, weights) is stored
-// device-coherently and complete before any entry is written; an entry and its
-// stamp are one 64-bit word, written and polled as one atomic access.  Every
+// tiles poll their slot's entry until the stamp matches.  An entry and its
+// stamp are one 64-bit word, written and polled as one atomic access; every
 // entry is rewritten each call, so a stale one holds the previous call's epoch.
-// The counters of the expert half are cleared by the routing tail before it
-// publishes, as the two-launch path clears them in the routing kernel.
+//
+// The tail keeps top-k, weights and the permutation in LDS until the entries
+// are out: a workgroup barrier waits for the wave's outstanding stores, so a
+// device-coherent store before any barrier of the tail would put its round trip
+// on the critical path.  An entry is all a gate/up tile needs (it carries the
+// expert's tokens); the routing outputs (ids, weights, sorted pairs, pair rows,
+// offsets) are stored after the entries, and outs_epoch announces them once
+// complete, which a down tile checks before it reads pair rows and weights for
+// the combine.  The counters of the expert half are cleared by the tail's first
+// wave before it polls the logits, and it waits for those stores there (while
+// the other workgroups' logits are on their way), so they are complete before
+// any entry goes out.
 template <int S, int MODE, int GL, int GC, int DL, int DC>
 __global__ void __launch_bounds__(kTileThreads)
     k_layer_decode(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
@@ -341,7 +384,9 @@ __global__ void __launch_bounds__(kTileThreads)
   __shared__ int pid[kSmallP];
   __shared__ int s_n;
   __shared__ int4 splan[kSmallP];
-  __shared__ int4 s_pl;
+  __shared__ SlotPlan s_pl;
+  __shared__ float s_tw[kSmallP];
+  __shared__ int s_sorted[kSmallP], s_prow[kSmallP];
   const int tid = threadIdx.x, wave = tid / kWave;
   const int T = a.T, H = a.H, E = a.E, k = a.k, P = T * k;
   const int R = (E + kTileWaves - 1) / kTileWaves;
@@ -351,6 +396,14 @@ __global__ void __launch_bounds__(kTileThreads)
                                                  reinterpret_cast<uint4*>(lds), logits,
                                                  st->logit_tag, epoch);
     if (wg != R - 1) return;   // the last routing workgroup runs the tail
+    if (wave == 0) {   // the expert half's counters (left by the previous call) back to zero
+      const int nrb_dn = (H + kDnRows - 1) / kDnRows;
+      for (int i = lane_id(); i < max_slots; i += kWave)
+        __hip_atomic_store(&st->gu_done[i].v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = lane_id(); i < nrb_dn; i += kWave)
+        __hip_atomic_store(&st->dn_done[i].v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_vmem();
+    }
     // one wave per token polls the token's E tagged logits until every one
     // carries this call's epoch (the words are this call's only once they
     // match), then selects from the values it holds
@@ -380,29 +433,30 @@ __global__ void __launch_bounds__(kTileThreads)
 #pragma unroll
       for (int i = 0; i < S; ++i)
         key[i] = lane * S + i < E ? order_key(__builtin_bit_cast(float, (uint32_t)(v[i] >> 32))) : kNoKey;
-      topk_keys<S, true>(key, t, k, ids, tw, pid);
+      topk_keys<S, true>(key, t, k, nullptr, nullptr, pid, s_tw);
     }
     __syncthreads();
-    const int n_act = rank_small<true>(pid, splan, &s_n, P, const_cast<int32_t*>(a.sorted_pairs), pair_row);
-    // the expert half's counters (left by the previous call) back to zero
-    const int nrb_dn = (H + kDnRows - 1) / kDnRows;
-    for (int i = tid; i < max_slots; i += kTileThreads)
-      __hip_atomic_store(&st->gu_done[i].v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int i = tid; i < nrb_dn; i += kTileThreads)
-      __hip_atomic_store(&st->dn_done[i].v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    wait_vmem();
-    __syncthreads();   // every result above is at the device-coherent level
+    const int n_act = rank_small<true>(pid, splan, &s_n, P, k, nullptr, nullptr, s_sorted, s_prow);
     // every entry, also those this call does not poll, so that each holds the
     // previous call's epoch at most
     for (int i = tid; i < 2 * kDecMaxSlots; i += kTileThreads) {
       const int slot = i % kDecMaxSlots;
       const int4 pl = slot < n_act ? splan[slot] : make_int4((int)kNoExpert, 0, 0, 0);
       __hip_atomic_store(&st->pub[i / kDecMaxSlots][slot],
-                         pack_pub(epoch, (uint32_t)pl.x, (uint32_t)pl.z, (uint32_t)pl.y, (uint32_t)n_act),
+                         pack_pub(epoch, (uint32_t)pl.x, (uint32_t)pl.w, (uint32_t)pl.y, (uint32_t)n_act),
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    // the expert offsets are an output only: after the publication
+    // the routing outputs, after the entries
+    for (int i = tid; i < P; i += kTileThreads) {
+      hst32<true>(ids, 4 * (size_t)i, (uint32_t)pid[i]);
+      hst32<true>(tw, 4 * (size_t)i, __builtin_bit_cast(uint32_t, s_tw[i]));
+      hst32<true>(const_cast<int32_t*>(a.sorted_pairs), 4 * (size_t)i, (uint32_t)s_sorted[i]);
+      hst32<true>(pair_row, 4 * (size_t)i, (uint32_t)s_prow[i]);
+    }
     small_offsets<kTileThreads>(splan, n_act, P, E, const_cast<int32_t*>(a.offsets));
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(&st->outs_epoch.v, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
   expert_tiles<MODE, GL, GC, DL, DC>(
@@ -420,11 +474,12 @@ __global__ void __launch_bounds__(kTileThreads)
           const uint32_t ex = (uint32_t)(v >> 32) & 0x7FFu;
           if ((uint32_t)v != epoch) {
             __hip_atomic_fetch_add(&st->timeouts.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_pl = make_int4(-1, 0, 0, 0);   // give up on this tile
+            s_pl = SlotPlan{-1, 0, 0, 0, -1, 0u};   // give up on this tile
           } else {
-            s_pl = ex == kNoExpert ? make_int4(-1, 0, 0, 0)
-                                   : make_int4((int)ex, (int)((v >> 47) & 0x7Fu), (int)((v >> 43) & 0xFu),
-                                               (int)((v >> 54) & 0xFFu));
+            const int tmask = (int)((v >> 43) & 0xFFu);
+            s_pl = ex == kNoExpert ? SlotPlan{-1, 0, 0, 0, -1, 0u}
+                                   : SlotPlan{(int)ex, (int)((v >> 57) & 0x3Fu), (int)__popc((unsigned)tmask),
+                                              (int)((v >> 51) & 0x3Fu) + 1, tmask, epoch};
           }
         }
         __syncthreads();

@@ -158,9 +158,11 @@ struct NoHook {
   __device__ void operator()() const {}
 };
 
+// tmask >= 0: the tile's sorted rows are the tokens of this mask in ascending
+// order (so sorted_pairs is not read); -1: the tokens come from sorted_pairs.
 template <int MODE, int LPR, int CPL, bool COH = false>
 __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, int ne, int rb,
-                                            int max_cols, uint8_t* lds) {
+                                            int max_cols, uint8_t* lds, int tmask = -1) {
   __shared__ float part[8][kGuRows][2];
   __shared__ float hbuf[8][kGuRows];
   __shared__ int s_tok[8];
@@ -176,9 +178,13 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, i
   // the x loads (issued after the weights) need not wait for the weights
   auto col_pair = [&](int c0) {   // the pair of column lane; its token is pair / k
     const int l = lane_id();
-    return MODE != MOE_A4 && l < min(max_cols, ne - c0)
-               ? (int)hld32<COH>(a.sorted_pairs, 4 * (size_t)(row0 + c0 + l))
-               : 0;
+    if (MODE == MOE_A4 || l >= min(max_cols, ne - c0)) return 0;
+    if (tmask >= 0) {   // column c0 + l is the mask's (c0 + l)-th token
+      uint32_t m = (uint32_t)tmask;
+      for (int i = 0; i < c0 + l && m != 0u; ++i) m &= m - 1u;
+      return m != 0u ? (__ffs((int)m) - 1) * a.k : 0;
+    }
+    return (int)hld32<COH>(a.sorted_pairs, 4 * (size_t)(row0 + c0 + l));
   };
   int pair = col_pair(0);
   __builtin_amdgcn_sched_barrier(0);

@@ -109,12 +109,14 @@ __device__ __forceinline__ int wave_max_key(int v) {
 // wins, and it moves its next expert to the head.  The round's critical path is
 // one wave reduction; no branches depend on the data.
 //
-// With lds_ids, the chosen experts also go to LDS (same [t][k] layout), for a
-// caller that works on them within the workgroup.
+// With lds_ids / lds_w, the chosen experts / weights also go to LDS (same
+// [t][k] layout), for a caller that works on them within the workgroup; with
+// ids and w null they go to LDS only.
 constexpr int kNoKey = (int)0x80000000;   // below every key of a finite value
 template <int S, bool COH = false>
 __device__ __forceinline__ void topk_keys(const int* key, int t, int k, int32_t* __restrict__ ids,
-                                          float* __restrict__ w, int* lds_ids = nullptr) {
+                                          float* __restrict__ w, int* lds_ids = nullptr,
+                                          float* lds_w = nullptr) {
   const int lane = lane_id();
   long long c[S];
 #pragma unroll
@@ -151,9 +153,11 @@ __device__ __forceinline__ void topk_keys(const int* key, int t, int k, int32_t*
   const float ex = lane < k ? expf(key_value(sel_k) - key_value(first_k)) : 0.0f;
   const float sum = wave_sum(ex);
   if (lane < k) {
-    hst32<COH>(ids, 4 * ((size_t)t * k + lane), (uint32_t)sel_i);
-    hst32<COH>(w, 4 * ((size_t)t * k + lane), __builtin_bit_cast(uint32_t, __fdiv_rn(ex, sum)));
+    const float wt = __fdiv_rn(ex, sum);
+    if (ids) hst32<COH>(ids, 4 * ((size_t)t * k + lane), (uint32_t)sel_i);
+    if (w) hst32<COH>(w, 4 * ((size_t)t * k + lane), __builtin_bit_cast(uint32_t, wt));
     if (lds_ids) lds_ids[t * k + lane] = sel_i;
+    if (lds_w) lds_w[t * k + lane] = wt;
   }
 }
 
