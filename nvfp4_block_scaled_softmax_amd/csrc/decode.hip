@@ -36,6 +36,9 @@
 // its own, so every call finds them at zero.
 #include <algorithm>
 #include <atomic>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "combine_common.hpp"
 #include "ffn_narrow.hpp"
@@ -256,7 +259,7 @@ __global__ void __launch_bounds__(kPermThreads)
 // at once).
 template <int MODE, int GL, int GC, int DL, int DC, typename PlanOf>
 __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __restrict__ st, int wg,
-                                             int max_slots, int cols_gu, int cols_dn,
+                                             uint32_t dn_hold, int max_slots, int cols_gu, int cols_dn,
                                              const int32_t* __restrict__ pair_row,
                                              const float* __restrict__ tw,
                                              const uint16_t* __restrict__ residual,
@@ -282,6 +285,11 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
     const int d = wg - G, slot = d / nrb_dn, rb = d % nrb_dn;
     const SlotPlan pl = plan_of(slot, 1);
     if (pl.e < 0) return;
+    if (dn_hold != 0u) {   // let the gate/up weights stream first (see launch_one3)
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      const uint64_t hold = (uint64_t)dn_hold * (uint64_t)pl.n_active;
+      while (__builtin_amdgcn_s_memrealtime() - t0 < hold) __builtin_amdgcn_s_sleep(1);
+    }
     down_tile<MODE, DL, DC, true>(a, pl.e, pl.row0, pl.rows, rb, cols_dn, lds, [&] {
       // (the weight loads are out) what a combine of this row block needs, in
       // case this tile turns out to be the block's last; in the single launch
@@ -344,7 +352,7 @@ __global__ void __launch_bounds__(kTileThreads)
   extern __shared__ __align__(16) uint8_t lds[];
   const int n_active = st->n_active;
   expert_tiles<MODE, GL, GC, DL, DC>(
-      a, st, blockIdx.x, max_slots, cols_gu, cols_dn, pair_row, tw, residual, out, lds,
+      a, st, blockIdx.x, 0u, max_slots, cols_gu, cols_dn, pair_row, tw, residual, out, lds,
       [&](int slot, int) {
         if (slot >= n_active) return SlotPlan{-1, 0, 0, 0, -1, 0u};
         const int4 pl = st->plan[slot];
@@ -379,7 +387,7 @@ __global__ void __launch_bounds__(kTileThreads)
                    int32_t* __restrict__ ids, float* __restrict__ tw, FfnArgs a,
                    DecodeState* __restrict__ st, int max_slots, int cols_gu, int cols_dn,
                    int32_t* __restrict__ pair_row, const uint16_t* __restrict__ residual,
-                   uint16_t* __restrict__ out, uint32_t epoch) {
+                   uint16_t* __restrict__ out, uint32_t epoch, uint32_t dn_hold) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int pid[kSmallP];
   __shared__ int s_n;
@@ -460,7 +468,7 @@ __global__ void __launch_bounds__(kTileThreads)
     return;
   }
   expert_tiles<MODE, GL, GC, DL, DC>(
-      a, st, wg - R, max_slots, cols_gu, cols_dn, pair_row, tw, residual, out, lds,
+      a, st, wg - R, dn_hold, max_slots, cols_gu, cols_dn, pair_row, tw, residual, out, lds,
       [&](int slot, int role) {
         if (tid == 0) {
           const uint64_t* e = &st->pub[role][slot];
@@ -488,6 +496,36 @@ __global__ void __launch_bounds__(kTileThreads)
 }
 
 // ------------------------------------------------------------------ launch
+// Workgroups of `kernel` (kTileThreads threads, `lds` bytes of dynamic LDS) that
+// are resident at once on the current device, cached per (device, kernel, LDS);
+// 0 when the runtime does not say.
+static int resident_groups(const void* kernel, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, size_t>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_tuple(dev, kernel, lds);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kTileThreads, lds) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cache[key] = per_cu * cus;
+}
+
+// Hold-back of the down tiles' weight loads in the single launch, per active
+// expert, in ticks of the 100 MHz real-time counter: 300 ns, the time to stream
+// one expert's gate/up weights (1.77 MB at H=3072, I=512) at the ~6 TB/s the
+// expert loads reach.  When every workgroup of the call is resident at once,
+// gate/up and down tiles see the plan together and their loads would share the
+// bandwidth, while gate/up is on the critical path and the down weights are
+// needed only after it (measured at T=1: 23.8 -> 23.15 us per call).  When the
+// grid is not resident at once, down tiles start late anyway and holding them
+// back only delays them (measured at T=2: +3.5 us), so there is no hold-back.
+constexpr uint32_t kDnHoldTicksPerExpert = 30;
+
 template <int S>
 static void launch_a(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E,
                      int k, float* logits, int32_t* ids, float* tw, int32_t* offsets,
@@ -562,9 +600,11 @@ static void launch_one3(const FfnArgs& a, const uint16_t* x, const uint16_t* wr,
   size_t lds = (size_t)a.T * a.H * 2;
   lds = std::max(lds, (size_t)cols * (a.H / 32) * ChunkLds<MOE_A16>::kStride);
   lds = std::max(lds, (size_t)cols_dn * (a.I / 32) * ChunkLds<MOE_A16>::kStride);
+  const int cap = resident_groups(reinterpret_cast<const void*>(&k_layer_decode<S, MOE_A16, 32, GC, DL, 1>), lds);
+  const uint32_t dn_hold = cap > 0 && grid <= cap ? kDnHoldTicksPerExpert : 0u;
   hipLaunchKernelGGL((k_layer_decode<S, MOE_A16, 32, GC, DL, 1>), dim3(grid), dim3(kTileThreads), lds, s,
                      x, wr, bias, logits, ids, tw, a, st, max_slots, cols, cols_dn, prow, residual, out,
-                     (uint32_t)epoch);
+                     (uint32_t)epoch, dn_hold);
 }
 
 template <int S, int GC>
