@@ -74,6 +74,9 @@ struct DecodeState {
   // single-launch layer: the router logits of the call, each tagged with its
   // epoch ((logit bits << 32) | epoch), [T][E]; the routing tail polls them
   uint64_t logit_tag[kNarrowT * kMaxExperts];
+  // single-launch layer: the down outputs y of the call, tagged the same way,
+  // [sorted row][H]; each row block's combining tile polls them
+  uint64_t y_tag[kSmallP * kMaxDim];
 };
 
 size_t decode_state_bytes() { return sizeof(DecodeState); }
@@ -313,7 +316,47 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
         s_res[t][i % kDnRows] = residual && o < a.H ? residual[(size_t)t * a.H + o] : (uint16_t)0;
       }
       wait_at_least(&st->gu_done[slot].v, (uint32_t)nrb_gu, &st->timeouts.v);
-    });
+    }, pl.outs_epoch != 0u ? st->y_tag : nullptr, pl.outs_epoch);
+    if (pl.outs_epoch != 0u) {
+      // single launch: the tile of slot 0 (always active) combines its row block
+      // by polling the tagged outputs of every pair's row; the others are done
+      if (slot != 0) return;
+      const uint32_t epoch = pl.outs_epoch;
+      for (int i = tid; i < a.T * kDnRows; i += kTileThreads) {
+        const int t = i / kDnRows, ol = i % kDnRows, o = rb * kDnRows + ol;
+        if (o >= a.H) continue;
+        float acc = 0.0f;
+        for (int j0 = 0; j0 < a.k; j0 += 16) {   // as combine_acc4: j ascending, one fma each
+          uint64_t v[16];
+          uint32_t it = 0;
+          while (true) {
+            bool ready = true;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+              const int j = j0 + u, r = j < a.k ? s_prow[t * a.k + j] : -1;
+              v[u] = r >= 0 ? __hip_atomic_load(&st->y_tag[(size_t)r * a.H + o], __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)
+                            : (uint64_t)epoch;   // value 0
+              ready = ready && (uint32_t)v[u] == epoch;
+            }
+            if (ready) break;
+            if (++it >= kSpinCap) {
+              __hip_atomic_fetch_add(&st->timeouts.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            if (j0 + u < a.k)
+              acc = __builtin_fmaf(s_tw[t * a.k + j0 + u], __builtin_bit_cast(float, (uint32_t)(v[u] >> 32)), acc);
+        }
+        uint32_t ob = f32_to_bf16(acc);   // as combine_round4, one element
+        if (residual) ob = f32_to_bf16(bf16_to_f32(s_res[t][ol]) + bf16_to_f32(ob));
+        out[(size_t)t * a.H + o] = (uint16_t)ob;
+      }
+      return;
+    }
     wait_vmem();   // this wave's y has reached the device-coherent level
     __syncthreads();
     if (tid == 0) {

@@ -284,8 +284,12 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, i
 // wait() runs after the weight loads are issued and before the intermediate is
 // read: the fused decode kernel waits there for its expert's gate/up tiles.
 template <int MODE, int LPR, int CPL, bool COH, typename Wait>
+// With ytag, every output value is also published as one 64-bit word
+// ytag[row * H + o] = (value bits << 32) | epoch (one atomic store), for a
+// consumer that polls the words instead of waiting on a counter.
 __device__ __forceinline__ void down_tile(const FfnArgs& a, int e, int row0, int ne, int rb,
-                                          int max_cols, uint8_t* lds, Wait&& wait) {
+                                          int max_cols, uint8_t* lds, Wait&& wait,
+                                          uint64_t* ytag = nullptr, uint32_t epoch = 0u) {
   __shared__ float outb[8][kDnRows];
   constexpr int S = ChunkLds<MODE>::kStride;
   constexpr int SLOTS = 64 / LPR;
@@ -344,8 +348,12 @@ __device__ __forceinline__ void down_tile(const FfnArgs& a, int e, int row0, int
     __syncthreads();
     for (int t = threadIdx.x; t < ncol * kDnRows; t += kTileThreads) {
       const int col = t / kDnRows, o = t % kDnRows;
-      if (o0 + o < H)
-        hst32<COH>(a.y, 4 * ((size_t)(row0 + c0 + col) * H + o0 + o), __builtin_bit_cast(uint32_t, outb[col][o]));
+      if (o0 + o < H) {
+        const size_t at = (size_t)(row0 + c0 + col) * H + o0 + o;
+        const uint32_t bits = __builtin_bit_cast(uint32_t, outb[col][o]);
+        if (ytag) __hip_atomic_store(&ytag[at], (uint64_t)bits << 32 | epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        hst32<COH>(a.y, 4 * at, bits);
+      }
     }
   }
 }
