@@ -77,6 +77,9 @@ struct DecodeState {
   // single-launch layer: the down outputs y of the call, tagged the same way,
   // [sorted row][H]; each row block's combining tile polls them
   uint64_t y_tag[kSmallP * kMaxDim];
+  // single-launch layer: the intermediate h, two bf16 values per tagged word,
+  // [sorted row][I/2]; the down tiles poll them
+  uint64_t h_tag[kSmallP * kMaxDim / 2];
 };
 
 size_t decode_state_bytes() { return sizeof(DecodeState); }
@@ -279,6 +282,11 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
     const int slot = wg / nrb_gu, rb = wg % nrb_gu;
     const SlotPlan pl = plan_of(slot, 0);
     if (pl.e < 0) return;
+    if (MODE == MOE_A16 && pl.outs_epoch != 0u) {   // single launch: h goes out as tagged words
+      gateup_tile<MODE, GL, GC, true>(a, pl.e, pl.row0, pl.rows, rb, cols_gu, lds, pl.tmask, st->h_tag,
+                                      pl.outs_epoch);
+      return;
+    }
     gateup_tile<MODE, GL, GC, true>(a, pl.e, pl.row0, pl.rows, rb, cols_gu, lds, pl.tmask);
     wait_vmem();   // this wave's h has reached the device-coherent level
     __syncthreads();
@@ -315,8 +323,10 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
         const int t = i / kDnRows, o = rb * kDnRows + i % kDnRows;
         s_res[t][i % kDnRows] = residual && o < a.H ? residual[(size_t)t * a.H + o] : (uint16_t)0;
       }
-      wait_at_least(&st->gu_done[slot].v, (uint32_t)nrb_gu, &st->timeouts.v);
-    }, pl.outs_epoch != 0u ? st->y_tag : nullptr, pl.outs_epoch);
+      if (!(MODE == MOE_A16 && pl.outs_epoch != 0u))   // (single launch: h words are polled instead)
+        wait_at_least(&st->gu_done[slot].v, (uint32_t)nrb_gu, &st->timeouts.v);
+    }, pl.outs_epoch != 0u ? st->y_tag : nullptr, pl.outs_epoch,
+       MODE == MOE_A16 && pl.outs_epoch != 0u ? st->h_tag : nullptr, &st->timeouts.v);
     if (pl.outs_epoch != 0u) {
       // single launch: the tile of slot 0 (always active) combines its row block
       // by polling the tagged outputs of every pair's row; the others are done

@@ -160,9 +160,13 @@ struct NoHook {
 
 // tmask >= 0: the tile's sorted rows are the tokens of this mask in ascending
 // order (so sorted_pairs is not read); -1: the tokens come from sorted_pairs.
+// htag (16-bit activations only): every pair of h values (2i, 2i+1) of a row is
+// also published as one 64-bit word htag[row * I/2 + i] = (their bf16 bits <<
+// 32) | epoch, written as one atomic store, for consumers that poll the words.
 template <int MODE, int LPR, int CPL, bool COH = false>
 __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, int ne, int rb,
-                                            int max_cols, uint8_t* lds, int tmask = -1) {
+                                            int max_cols, uint8_t* lds, int tmask = -1,
+                                            uint64_t* htag = nullptr, uint32_t epoch = 0u) {
   __shared__ float part[8][kGuRows][2];
   __shared__ float hbuf[8][kGuRows];
   __shared__ int s_tok[8];
@@ -248,13 +252,25 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, i
     }
     __syncthreads();
     // SwiGLU and the intermediate in the mode's precision
-    for (int t = threadIdx.x; t < ncol * kGuRows; t += kTileThreads) {
-      const int col = t / kGuRows, hr = t % kGuRows;
-      const float h = swiglu(part[col][hr][0], part[col][hr][1]);
-      if (MODE == MOE_A16) {
-        hst16<COH>(a.h_codes, 2 * ((size_t)(row0 + c0 + col) * I + i0 + hr), (uint16_t)f32_to_bf16(h));
-      } else {
-        hbuf[col][hr] = h;
+    if (MODE == MOE_A16 && htag) {   // two h values per thread, as one tagged word
+      for (int t = threadIdx.x; t < ncol * (kGuRows / 2); t += kTileThreads) {
+        const int col = t / (kGuRows / 2), hr = 2 * (t % (kGuRows / 2));
+        const uint32_t b0 = f32_to_bf16(swiglu(part[col][hr][0], part[col][hr][1]));
+        const uint32_t b1 = f32_to_bf16(swiglu(part[col][hr + 1][0], part[col][hr + 1][1]));
+        const size_t at = (size_t)(row0 + c0 + col) * I + i0 + hr;
+        __hip_atomic_store(&htag[at / 2], (uint64_t)(b0 | b1 << 16) << 32 | epoch, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        hst32<COH>(a.h_codes, 2 * at, b0 | b1 << 16);
+      }
+    } else {
+      for (int t = threadIdx.x; t < ncol * kGuRows; t += kTileThreads) {
+        const int col = t / kGuRows, hr = t % kGuRows;
+        const float h = swiglu(part[col][hr][0], part[col][hr][1]);
+        if (MODE == MOE_A16) {
+          hst16<COH>(a.h_codes, 2 * ((size_t)(row0 + c0 + col) * I + i0 + hr), (uint16_t)f32_to_bf16(h));
+        } else {
+          hbuf[col][hr] = h;
+        }
       }
     }
     if (MODE != MOE_A16) {
@@ -287,9 +303,12 @@ template <int MODE, int LPR, int CPL, bool COH, typename Wait>
 // With ytag, every output value is also published as one 64-bit word
 // ytag[row * H + o] = (value bits << 32) | epoch (one atomic store), for a
 // consumer that polls the words instead of waiting on a counter.
+// With htag (16-bit activations), h is read from the tagged words that
+// gateup_tile publishes, each polled until it carries epoch.
 __device__ __forceinline__ void down_tile(const FfnArgs& a, int e, int row0, int ne, int rb,
                                           int max_cols, uint8_t* lds, Wait&& wait,
-                                          uint64_t* ytag = nullptr, uint32_t epoch = 0u) {
+                                          uint64_t* ytag = nullptr, uint32_t epoch = 0u,
+                                          const uint64_t* htag = nullptr, uint32_t* timeouts = nullptr) {
   __shared__ float outb[8][kDnRows];
   constexpr int S = ChunkLds<MODE>::kStride;
   constexpr int SLOTS = 64 / LPR;
@@ -323,7 +342,26 @@ __device__ __forceinline__ void down_tile(const FfnArgs& a, int e, int row0, int
   for (int c0 = 0; c0 < ne; c0 += max_cols) {
     const int ncol = min(max_cols, ne - c0);
     __syncthreads();
-    stage_down_cols<MODE, COH>(a, row0, c0, ncol, lds);
+    if (MODE == MOE_A16 && htag) {
+      // word p of a row holds h 2p, 2p+1: chunk p / 16, bytes 4 (p % 16) of it
+      const int half = I / 2;
+      for (int i = threadIdx.x; i < ncol * half; i += kTileThreads) {
+        const int col = i / half, p = i % half;
+        const uint64_t* w = htag + (size_t)(row0 + c0 + col) * half + p;
+        uint64_t v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (uint32_t it = 0; (uint32_t)v != epoch; ++it) {
+          if (it >= (1u << 22)) {
+            __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+          v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        *reinterpret_cast<uint32_t*>(lds + ((size_t)col * NC + p / 16) * S + 4 * (p % 16)) = (uint32_t)(v >> 32);
+      }
+    } else {
+      stage_down_cols<MODE, COH>(a, row0, c0, ncol, lds);
+    }
     __syncthreads();
     for (int col = 0; col < ncol; ++col) {
       const uint8_t* xc = lds + (size_t)col * NC * S;
