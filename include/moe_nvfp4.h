@@ -219,8 +219,9 @@ int moe_layer_is_fused(int T, int H, int I);
 
 /* Kernel launches of one moe_layer_forward call on a stream that is not being
  * captured into a graph: 1 for the single-launch decode layer (fused sizes,
- * MOE_A16, T*k <= 64), 2 or 3 for the fused two-kernel path (routing, the
- * 8/4-bit activation quantizer, experts + combine), 0 when the per-stage
+ * MOE_A16, T*k <= 64), 2 or 3 for the fused two-kernel path (routing, for
+ * MOE_A8 the activation quantizer, experts + combine; MOE_A4 quantizes x in
+ * the expert kernel's gate/up tiles), 0 when the per-stage
  * kernels run.  Under capture the single-launch case takes the two-kernel path:
  * its launch carries a per-call number that a graph replay would repeat. */
 int moe_layer_launches(moe_act_mode mode, int T, int k, int H, int I);

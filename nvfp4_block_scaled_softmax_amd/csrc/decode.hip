@@ -287,7 +287,7 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
                                       pl.outs_epoch);
       return;
     }
-    gateup_tile<MODE, GL, GC, true>(a, pl.e, pl.row0, pl.rows, rb, cols_gu, lds, pl.tmask);
+    gateup_tile<MODE, GL, GC, true, MODE == MOE_A4>(a, pl.e, pl.row0, pl.rows, rb, cols_gu, lds, pl.tmask);
     wait_vmem();   // this wave's h has reached the device-coherent level
     __syncthreads();
     if (tid == 0)
@@ -602,7 +602,7 @@ static bool single_launch(moe_act_mode mode, int T, int k) { return mode == MOE_
 
 int decode_launches(moe_act_mode mode, int T, int k, int H, int I) {
   if (T < 1 || k < 1 || !decode_fusable(T, H, I)) return 0;
-  return single_launch(mode, T, k) ? 1 : (mode == MOE_A16 ? 2 : 3);
+  return single_launch(mode, T, k) ? 1 : (mode == MOE_A8 ? 3 : 2);   // A8: the activation quantizer between
 }
 
 template <int MODE, int GC, int DL>
@@ -718,7 +718,7 @@ moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, in
     else launch_a<16>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
     r = check_launch("moe_layer_forward (decode routing)");
     if (r != MOE_OK) return r;
-    if (mode != MOE_A16) {   // needs the permutation (4-bit: per pair)
+    if (mode == MOE_A8) {   // x per token; 4-bit x is quantized in the gate/up tiles
       r = launch_expert_ffn(w, mode, x, T, k, offsets, sorted, y, ffn_ws, 1, s, prow, ids);
       if (r != MOE_OK) return r;
     }

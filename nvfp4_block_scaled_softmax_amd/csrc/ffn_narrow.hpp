@@ -160,10 +160,57 @@ struct NoHook {
 
 // tmask >= 0: the tile's sorted rows are the tokens of this mask in ascending
 // order (so sorted_pairs is not read); -1: the tokens come from sorted_pairs.
+// 4-bit mode, quantizing in the tile: x of the tokens in tok (one per column)
+// quantized per 16 under the expert's gate and up input scales straight into
+// the A4 chunk layout (the arithmetic of the stand-alone quantizers, so the
+// codes are the same); with write_ws the codes and scales also go to the
+// workspace rows row0 + c0 + col, as the stand-alone quantizer writes them.
+__device__ void stage_gateup_quant_a4(const FfnArgs& a, int e, int row0, int c0, int ncol, const int* tok,
+                                      uint8_t* lds, bool write_ws) {
+  constexpr int S = ChunkLds<MOE_A4>::kStride;
+  const int H = a.H, nb = H / 16, NC = H / 32;
+  const float g0 = a.gu_inscale[2 * e], g1 = a.gu_inscale[2 * e + 1];
+  const bool same = __float_as_uint(g0) == __float_as_uint(g1);
+  for (int i = threadIdx.x; i < ncol * nb; i += kTileThreads) {
+    const int col = i / nb, b = i % nb, hb = b % 2;
+    const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)tok[col] * H + (size_t)b * 16);
+    const uint4 u0 = src[0], u1 = src[1];
+    const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+      v[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+    }
+    uint32_t lo0, hi0, lo1, hi1;
+    const uint32_t s0 = nvfp4_quant16(v, g0, lo0, hi0);
+    uint32_t s1 = s0;
+    lo1 = lo0;
+    hi1 = hi0;
+    if (!same) s1 = nvfp4_quant16(v, g1, lo1, hi1);
+    uint8_t* c = lds + ((size_t)col * NC + b / 2) * S;
+    *reinterpret_cast<uint2*>(c + 8 * hb) = make_uint2(lo0, hi0);
+    *reinterpret_cast<uint2*>(c + 16 + 8 * hb) = make_uint2(lo1, hi1);
+    c[32 + hb] = (uint8_t)s0;
+    c[34 + hb] = (uint8_t)s1;
+    if (write_ws) {
+      const size_t r = (size_t)(row0 + c0 + col);
+      uint8_t* xc = const_cast<uint8_t*>(a.xq_codes);
+      uint8_t* xs = static_cast<uint8_t*>(const_cast<void*>(a.xq_scales));
+      *reinterpret_cast<uint2*>(xc + (r * 2 + 0) * (H / 2) + (size_t)b * 8) = make_uint2(lo0, hi0);
+      *reinterpret_cast<uint2*>(xc + (r * 2 + 1) * (H / 2) + (size_t)b * 8) = make_uint2(lo1, hi1);
+      xs[(r * 2 + 0) * nb + b] = (uint8_t)s0;
+      xs[(r * 2 + 1) * nb + b] = (uint8_t)s1;
+    }
+  }
+}
+
 // htag (16-bit activations only): every pair of h values (2i, 2i+1) of a row is
 // also published as one 64-bit word htag[row * I/2 + i] = (their bf16 bits <<
 // 32) | epoch, written as one atomic store, for consumers that poll the words.
-template <int MODE, int LPR, int CPL, bool COH = false>
+// QX (4-bit mode): x is quantized in the tile (stage_gateup_quant_a4) instead of
+// read quantized from the workspace; row block 0's tile also writes it there.
+template <int MODE, int LPR, int CPL, bool COH = false, bool QX = false>
 __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, int ne, int rb,
                                             int max_cols, uint8_t* lds, int tmask = -1,
                                             uint64_t* htag = nullptr, uint32_t epoch = 0u) {
@@ -182,7 +229,7 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, i
   // the x loads (issued after the weights) need not wait for the weights
   auto col_pair = [&](int c0) {   // the pair of column lane; its token is pair / k
     const int l = lane_id();
-    if (MODE == MOE_A4 || l >= min(max_cols, ne - c0)) return 0;
+    if ((MODE == MOE_A4 && !QX) || l >= min(max_cols, ne - c0)) return 0;
     if (tmask >= 0) {   // column c0 + l is the mask's (c0 + l)-th token
       uint32_t m = (uint32_t)tmask;
       for (int i = 0; i < c0 + l && m != 0u; ++i) m &= m - 1u;
@@ -225,7 +272,8 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, i
     const int ncol = min(max_cols, ne - c0);
     if (threadIdx.x < ncol) s_tok[threadIdx.x] = pair / a.k;
     __syncthreads();
-    if (!by_token) stage_gateup_cols<MODE>(a, e, row0, c0, ncol, s_tok, lds);
+    if constexpr (MODE == MOE_A4 && QX) stage_gateup_quant_a4(a, e, row0, c0, ncol, s_tok, lds, rb == 0);
+    else if (!by_token) stage_gateup_cols<MODE>(a, e, row0, c0, ncol, s_tok, lds);
     __syncthreads();
     for (int col = 0; col < ncol; ++col) {
       const uint8_t* xc = lds + (size_t)(by_token ? s_tok[col] : col) * NC * S;
