@@ -222,8 +222,9 @@ int moe_layer_is_fused(int T, int H, int I);
  * MOE_A16, T*k <= 64), 2 or 3 for the fused two-kernel path (routing, for
  * MOE_A8 the activation quantizer, experts + combine; MOE_A4 quantizes x in
  * the expert kernel's gate/up tiles), 0 when the per-stage
- * kernels run.  Under capture the single-launch case takes the two-kernel path:
- * its launch carries a per-call number that a graph replay would repeat. */
+ * kernels run.  Under capture the single-launch case is preceded by a
+ * one-thread kernel that advances the call's number in the workspace (a number
+ * baked into the launch would repeat on every replay): 2 launches. */
 int moe_layer_launches(moe_act_mode mode, int T, int k, int H, int I);
 size_t moe_layer_workspace_bytes(moe_act_mode mode, int T, int k, int E, int H, int I);
 moe_status moe_layer_forward(const moe_nvfp4_experts* w, moe_act_mode mode, const uint16_t* x,

@@ -62,6 +62,8 @@ struct alignas(128) Counter {
 struct DecodeState {
   Counter route_done;                  // A: workgroups finished
   Counter timeouts;                    // waits that reached the spin cap (stays 0)
+  Counter dev_epoch;                   // single launch under graph capture: the call's epoch,
+                                       // advanced by k_epoch_bump before each call
   Counter outs_epoch;                  // single launch: epoch of the call whose routing outputs
                                        // (ids, weights, sorted pairs, pair rows) are complete
   int32_t n_active;                    // active experts (written by A)
@@ -440,8 +442,13 @@ __global__ void __launch_bounds__(kTileThreads)
                    int32_t* __restrict__ ids, float* __restrict__ tw, FfnArgs a,
                    DecodeState* __restrict__ st, int max_slots, int cols_gu, int cols_dn,
                    int32_t* __restrict__ pair_row, const uint16_t* __restrict__ residual,
-                   uint16_t* __restrict__ out, uint32_t epoch, uint32_t dn_hold) {
+                   uint16_t* __restrict__ out, uint32_t epoch_arg, uint32_t dn_hold) {
   extern __shared__ __align__(16) uint8_t lds[];
+  // epoch_arg 0: the epoch is in the workspace, advanced by k_epoch_bump just
+  // before this kernel (complete at the kernel boundary, the same for every
+  // workgroup)
+  const uint32_t epoch = epoch_arg != 0u ? epoch_arg
+                                         : __hip_atomic_load(&st->dev_epoch.v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __shared__ int pid[kSmallP];
   __shared__ int s_n;
   __shared__ int4 splan[kSmallP];
@@ -546,6 +553,19 @@ __global__ void __launch_bounds__(kTileThreads)
         __syncthreads();
         return s_pl;
       });
+}
+
+// The epoch of a single-launch call made under graph capture, where a number
+// baked into the launch would repeat on every replay: one thread advances the
+// workspace's device epoch (top bit set, so it never equals a host epoch, which
+// keeps the top bit clear; never 0), and the layer kernel that follows reads it.
+__global__ void __launch_bounds__(kWave) k_epoch_bump(DecodeState* __restrict__ st) {
+  if (threadIdx.x == 0) {
+    const uint32_t v = __hip_atomic_load(&st->dev_epoch.v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t c = (v & 0x7FFFFFFFu) + 1u;
+    __hip_atomic_store(&st->dev_epoch.v, 0x80000000u | (c > 0x7FFFFFFFu ? 1u : c), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ------------------------------------------------------------------ launch
@@ -680,8 +700,9 @@ static void launch_one(const FfnArgs& a, const uint16_t* x, const uint16_t* wr, 
   else launch_one2<S, 4>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
 }
 
-// Epochs of single-launch calls: never reused within the process (the
-// workspace starts at zero, so 0 is never one).
+// Epochs of eager single-launch calls: 31 bits, not reused within 2^31 calls
+// of the process, never 0 (the workspace starts at zero); device epochs (graph
+// capture) have the top bit set.
 static std::atomic<uint64_t> g_epoch{0};
 
 moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, int stage_mask,
@@ -694,14 +715,20 @@ moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, in
   const int E = w.E, H = w.H;
   moe_status r;
   if (stage_mask == 3 && single_launch(mode, T, k)) {
-    // one launch, unless the stream is being captured into a graph: a replay
-    // would repeat the epoch baked into the launch, so graphs get two launches
+    // one launch; under graph capture, where a replay would repeat an epoch baked
+    // into the launch, a one-thread kernel first advances a device-side epoch
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cs) != hipSuccess) return check_launch("moe_layer_forward (capture query)");
-    if (cs == hipStreamCaptureStatusNone) {
+    {
       const FfnArgs a = make_ffn_args(w, mode, x, T, k, offsets, sorted, y, ffn_ws);
-      uint64_t epoch;
-      do epoch = ++g_epoch; while ((uint32_t)epoch == 0u);   // 0: a never-written entry
+      uint64_t epoch = 0;   // 0: read the device epoch
+      if (cs == hipStreamCaptureStatusNone) {
+        do epoch = ++g_epoch & 0x7FFFFFFFu; while (epoch == 0u);   // 0: a never-written entry
+      } else {
+        hipLaunchKernelGGL(k_epoch_bump, dim3(1), dim3(kWave), 0, s, st);
+        moe_status rb = check_launch("moe_layer_forward (epoch)");
+        if (rb != MOE_OK) return rb;
+      }
       if (E <= 64) launch_one<1>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
       else if (E <= 128) launch_one<2>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
       else if (E <= 256) launch_one<4>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, s);

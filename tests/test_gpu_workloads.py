@@ -293,10 +293,11 @@ def test_decode_tied_logits(dev, w, group):
 
 
 def test_decode_graph_replay(dev):
-    """Under stream capture the layer takes its two-launch form (a replay would
-    repeat the single-launch form's epoch).  Three replays, each with eager
-    single-launch calls and a synchronisation before it, all equal the eager
-    result bit for bit."""
+    """Under stream capture the single-launch layer is recorded behind a
+    one-thread kernel that advances the call's epoch in the workspace (an epoch
+    baked into the launch would repeat on replay).  Three replays, each with
+    eager single-launch calls and a synchronisation before it, all equal the
+    eager result bit for bit."""
     w = synth.CONFIGS[1]
     ex, router, bias = gpu_layer(w, 0, "A16", dev)
     nws = moe.layer_workspace_bytes("A16", w.T, w.k, w.E, w.H, w.I)
