@@ -208,7 +208,11 @@ def run_gpu(w, mode, steps, warmup, n_layers, n_batches):
         kern_bytes = float(np.mean([per_layer[s % n_layers][3] for s in range(steps)])) * gu_bytes_e
         kernel = ("k_gateup_wide_a4" if (mode == "A4" and T > 8) else "k_gateup_narrow") + " (gate/up + SwiGLU)"
     achieved = kern_bytes / (kern_us * 1e-6) / 1e9
+    stack = None
+    if w.index == 3:
+        stack = stack_step(w, mode, layers, xs[0], ws, steps=max(5, steps // 20), warmup=2)
     return {
+        "stack_step": stack,
         "ms_per_step": ms,
         "gbs": total_bytes / steps / (ms * 1e-3) / 1e9,
         "bytes_per_step": total_bytes / steps,
@@ -219,6 +223,52 @@ def run_gpu(w, mode, steps, warmup, n_layers, n_batches):
         "route_us": None if split else route_us,
         "split": split,
     }
+
+
+def stack_step(w, mode, layers, x0, ws, steps, warmup, depth=48):
+    """One decode step through `depth` stacked layers (the layer copies cycled),
+    each layer's output plus its input feeding the next, timed eagerly and as a
+    replayed HIP graph of the whole step (the layer calls are single-launch
+    kernels in both; under capture each is preceded by its epoch kernel)."""
+    import torch
+    import nvfp4_block_scaled_softmax_amd as moe
+    bufs = [torch.empty_like(x0) for _ in range(2)]
+    x_in = x0.clone()
+
+    def calls():
+        cur = x_in
+        for l in range(depth):
+            ex, router, bias = layers[l % len(layers)]
+            moe.moe_layer_forward(ex, mode, cur, router, w.k, bias=bias, residual=cur, ws=ws, out=bufs[l % 2])
+            cur = bufs[l % 2]
+        return cur
+
+    for _ in range(warmup):
+        calls()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        calls()
+    ev1.record()
+    torch.cuda.synchronize()
+    eager_us = ev0.elapsed_time(ev1) / steps * 1e3
+    eager_out = calls().clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(steps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    graph_us = ev0.elapsed_time(ev1) / steps * 1e3
+    same = bool(torch.equal(bufs[(depth - 1) % 2].view(torch.int16), eager_out.view(torch.int16)))
+    return {"layers": depth, "T": w.T, "eager_us": round(eager_us, 1), "graph_us": round(graph_us, 1),
+            "tokens_per_s_graph": round(w.T / (graph_us * 1e-6), 1), "graph_equals_eager": same}
 
 
 # --------------------------------------------------------------------------- CPU baseline
@@ -365,6 +415,8 @@ def main(argv=None):
                      "traffic": stored_traffic(w.index)},
         "cpu_baseline": cpu,
     }
+    if r["stack_step"] is not None:
+        line["stack_step"] = r["stack_step"]
     print(json.dumps(line), flush=True)
     return 0
 
