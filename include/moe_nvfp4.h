@@ -197,9 +197,11 @@ moe_status moe_combine(const float* y_pairs, const int32_t* pair_row, const floa
  *   out [T][H] bf16 = the layer output, or bf16(residual + output) when
  *   residual is not NULL (residual may equal x; out must not alias x).
  *   ws: moe_layer_workspace_bytes(mode, T, k, E, H, I) bytes, 256-byte aligned,
- *   zero-filled before its first use: up to 8 tokens the layer runs fused (the
- *   routing in one launch, the experts with the combine in another) and keeps
- *   inter-workgroup counters in the workspace, which every call leaves at zero.
+ *   zero-filled before its first use: up to 8 tokens the layer runs fused (one
+ *   launch for 16-bit activations and up to 64 pairs, else the routing in one
+ *   launch and the experts with the combine in another) and keeps
+ *   inter-workgroup state in the workspace: counters, which every call leaves at
+ *   zero, and words stamped with a per-call number, which need no reset.
  *   Calls sharing a workspace must not overlap.
  *   moe_layer_workspace_layout fills offsets[7] (bytes into ws) of topk_ids
  *   [T][k] int32, topk_w [T][k] fp32, expert_offsets [E+1] int32, sorted_pairs
