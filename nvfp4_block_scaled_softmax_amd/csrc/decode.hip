@@ -1,5 +1,5 @@
-// Fused decode layer (T <= 8 tokens): the routed-expert layer in two launches
-// instead of six.
+// Fused decode layer (T <= 8 tokens): the routed-expert layer in one launch
+// (16-bit activations, up to 64 pairs: k_layer_decode, below) or two:
 //
 //   A  k_route_decode:   router logits (one wave per expert row); the last
 //                        workgroup to finish runs top-k, the stable
@@ -15,25 +15,33 @@
 // the fused layer is bit-identical to moe_route_topk + moe_permute +
 // nvfp4_expert_ffn + moe_combine.
 //
-// Ordering between workgroups.  In B, gate/up tiles have the lower workgroup
-// indices and down tiles the higher ones.  Workgroups are dispatched in index
-// order (round-robin over the XCDs, in order within each), so every gate/up
-// tile is resident or done before a down tile that could wait for it takes a
-// slot: the waits cannot starve the tiles they wait for.  (A ticket from one
-// shared atomic counter would not need that order, but 800 workgroups
-// serialised on one counter cost more than the whole expert pass.)  Waits are
-// bounded by a spin cap, so every wave exits whatever happens; a wait that
-// reaches the cap is counted in the state block, where tests check it.  The data handed between
-// workgroups (logits, h, y) crosses XCDs, whose L2s are not coherent with
-// each other: it is written and read with device-coherent (sc1) buffer
-// accesses that pass the XCD-local caches; a producer waits for its stores to
-// complete before its workgroup bumps the counter, and consumers poll the
-// counter with relaxed device-scope loads.  No L2 write-back or invalidate is
-// needed.
+// Ordering between workgroups.  Gate/up tiles have lower workgroup indices
+// than down tiles, and waits are only on lower-indexed workgroups, except a
+// combining tile's wait for the other down tiles of its row block, which
+// themselves wait only on gate/up tiles.  Workgroups are dispatched in index
+// order (round-robin over the XCDs, in order within each), so every workgroup
+// waited for is resident, done, or gets a slot from a workgroup that finishes
+// without waiting: the waits cannot starve.  (A ticket from one shared atomic
+// counter would not need that order, but 800 workgroups serialised on one
+// counter cost more than the whole expert pass.)  Waits are bounded by a spin
+// cap, so every wave exits whatever happens; a wait that reaches the cap is
+// counted in the state block, where tests check it.
 //
-// The counters live in a small state block of the layer workspace.  It must be
-// zero before the first call; A's last workgroup clears B's counters and then
-// its own, so every call finds them at zero.
+// The data handed between workgroups (logits, h, y, the plan) crosses XCDs,
+// whose L2s are not coherent with each other: it is written and read with
+// device-coherent (sc1) accesses that pass the XCD-local caches.  In the two
+// launches a producer waits for its stores to complete before its workgroup
+// bumps a counter, and consumers poll the counter with relaxed device-scope
+// loads.  In the single launch the values themselves carry the call's epoch
+// (one 64-bit atomic store per value: logits, plan words, h pairs, y), and
+// consumers poll the values, with no store-completion wait and no counter.  No
+// L2 write-back or invalidate is needed.
+//
+// The counters and tagged words live in a state block at the start of the
+// layer workspace.  It must be zero before the first call; every call leaves
+// the counters at zero (A's last workgroup clears B's, the single launch's tail
+// clears them before it publishes), and tagged words need no reset: a stale
+// word carries another call's epoch.
 #include <algorithm>
 #include <atomic>
 #include <map>
@@ -417,12 +425,15 @@ __global__ void __launch_bounds__(kTileThreads)
 
 // ------------------------------------------------------------------ A + B in one launch
 // Up to kSmallP pairs: workgroups [0, R) compute the router logits (one expert
-// per wave) and the last of them runs top-k and the permutation; the expert
-// tiles follow.  The last routing workgroup publishes each slot's plan entry
-// stamped with this call's epoch (a number the host does not reuse, never 0); expert
-// tiles poll their slot's entry until the stamp matches.  An entry and its
-// stamp are one 64-bit word, written and polled as one atomic access; every
-// entry is rewritten each call, so a stale one holds the previous call's epoch.
+// per wave), each published as a word stamped with this call's epoch (a number
+// not reused, never 0: from the host, or under graph capture from the device,
+// see k_epoch_bump); the last routing workgroup polls them and runs top-k and
+// the permutation; the expert tiles follow.  It publishes each slot's plan
+// entry stamped with the epoch; expert tiles poll their slot's entry until the
+// stamp matches.  An entry and its stamp are one 64-bit word, written and
+// polled as one atomic access; every entry is rewritten each call.  Gate/up
+// tiles publish h, and down tiles y, the same way, so each consumer polls the
+// values it needs (slot 0's down tile of each output-row block combines).
 //
 // The tail keeps top-k, weights and the permutation in LDS until the entries
 // are out: a workgroup barrier waits for the wave's outstanding stores, so a
