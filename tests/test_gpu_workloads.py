@@ -43,6 +43,15 @@ def say(*a):
 _LAYERS = {}
 
 
+def gpu_layer_pair(w, layer, mode, dev):
+    """Like gpu_layer, but two layers of one workload may be held at once."""
+    key = ("pair", w.index, layer, mode)
+    if key not in _LAYERS:
+        say("building layer", key)
+        _LAYERS[key] = bench.build_layer(w, layer, dev, mode)
+    return _LAYERS[key]
+
+
 def gpu_layer(w, layer, mode, dev):
     key = (w.index, layer, mode)
     if key not in _LAYERS:
@@ -320,3 +329,44 @@ def test_decode_graph_replay(dev):
         torch.cuda.synchronize()
         assert torch.equal(out_g.view(torch.int16), ref.view(torch.int16)), rep
     assert moe.layer_wait_timeouts(ws_g) == 0 and moe.layer_wait_timeouts(ws_e) == 0
+
+
+def test_decode_graph_chain(dev):
+    """Six chained single-launch layers (each output plus its input feeds the
+    next; two seeded layer copies alternate) captured as one graph on one
+    workspace, the epoch kernel ahead of each: three replays on fresh inputs,
+    each equal bit for bit to the same chain run eagerly on another workspace."""
+    w = synth.CONFIGS[3]
+    mode = "A16"
+    layers = [gpu_layer_pair(w, l, mode, dev) for l in range(2)]
+    nws = moe.layer_workspace_bytes(mode, w.T, w.k, w.E, w.H, w.I)
+    ws_g = torch.zeros(nws, dtype=torch.uint8, device=dev)
+    ws_e = torch.zeros(nws, dtype=torch.uint8, device=dev)
+    x_g = bench.token_batch(w, 0, dev).clone()
+    bufs = [torch.empty_like(x_g) for _ in range(2)]
+
+    def chain(x_in, ws, outs):
+        cur = x_in
+        for l in range(6):
+            ex, router, bias = layers[l % 2]
+            moe.moe_layer_forward(ex, mode, cur, router, w.k, bias=bias, residual=cur, ws=ws, out=outs[l % 2])
+            cur = outs[l % 2]
+        return cur
+
+    chain(x_g, ws_g, bufs)   # warm up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chain(x_g, ws_g, bufs)
+    for rep, batch in enumerate((1, 2, 3)):
+        say("graph chain replay", rep, "batch", batch)
+        x_new = bench.token_batch(w, batch, dev)
+        ref = chain(x_new, ws_e, [torch.empty_like(x_new) for _ in range(2)]).clone()
+        x_g.copy_(x_new)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bufs[1].view(torch.int16), ref.view(torch.int16)), rep
+    assert moe.layer_wait_timeouts(ws_g) == 0 and moe.layer_wait_timeouts(ws_e) == 0
+    _LAYERS.clear()
+    torch.cuda.empty_cache()
