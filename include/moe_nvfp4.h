@@ -46,7 +46,8 @@ typedef enum {
   MOE_E_SHAPE = -3,        /* size out of the documented range */
   MOE_E_UNSUPPORTED = -4,  /* valid but not implemented combination */
   MOE_E_WORKSPACE = -5,    /* workspace smaller than the *_workspace_bytes() figure */
-  MOE_E_HIP = -6           /* a HIP call or kernel launch failed */
+  MOE_E_HIP = -6,          /* a HIP call or kernel launch failed */
+  MOE_E_STALLED = -7       /* moe_layer_status: a wait inside a fused decode call gave up */
 } moe_status;
 
 /* Expert activation precision (page "Infernix", section "Activation precision"). */
@@ -211,9 +212,21 @@ moe_status moe_combine(const float* y_pairs, const int32_t* pair_row, const floa
 moe_status moe_layer_workspace_layout(moe_act_mode mode, int T, int k, int E, int H, int I,
                                       size_t offsets[7]);
 /* Byte offset in a layer workspace of a uint32 that counts waits of the fused
- * decode path which reached their bound (a stalled producer); it stays 0 in
- * correct operation and is meant for tests and health checks. */
+ * decode path which gave up (a stalled producer); it stays 0 in correct
+ * operation.  Workgroups of one fused launch wait for each other; the waits are
+ * bounded (about 0.7 s each) and the first to give up makes every other wait of
+ * the launch give up at once, so a stalled launch still ends.  Its combine then
+ * writes bf16 NaN for the outputs whose inputs it gave up on.  A non-zero count
+ * makes every later fused call on the workspace give up at once (NaN outputs)
+ * until the caller zero-fills the workspace again. */
 size_t moe_layer_wait_timeouts_offset(void);
+
+/* moe_layer_status: MOE_OK when no wait of a fused decode call on this layer
+ * workspace has given up since it was zero-filled, else MOE_E_STALLED (the
+ * outputs of those calls are unreliable).  It reads 4 bytes of ws after the
+ * work already enqueued on s, and therefore SYNCHRONISES stream s: a health
+ * check, not for a hot loop. */
+moe_status moe_layer_status(const void* ws, hipStream_t s);
 
 /* 1 when moe_layer_forward runs the fused decode path for these sizes (up
  * to 8 tokens, H/32 in 33..128, I/32 in 5..32), else 0 (per-stage kernels). */
@@ -245,6 +258,32 @@ moe_status moe_layer_forward_stage(const moe_nvfp4_experts* w, moe_act_mode mode
                                    const float* router_bias, int T, int k,
                                    const uint16_t* residual, uint16_t* out, void* ws,
                                    size_t ws_bytes, hipStream_t s);
+
+/* ------------------------------------------------------------------ test only
+ * moe_debug_nvfp4_matmul: the expert kernels' product core without the
+ * routing, the SwiGLU or the intermediate's rounding, for pinning it.  For one
+ * NVFP4 matrix W (codes [N][K/2], E4M3 scales [N][K/16], fp32 multiplier
+ * *wscale) and cols activation columns x:
+ *   out[c][n] = wscale (* inscale, MOE_A4) * sum_k dec(W[n][k]) * x[c][k]
+ * in fp32 accumulation, with x in the mode's stored form:
+ *   MOE_A16  x bf16 [cols][K], x_scales NULL;
+ *   MOE_A8   x E4M3 codes [cols][K], x_scales fp32 [cols][K/16];
+ *   MOE_A4   x E2M1 codes [cols][K/2], x_scales E4M3 [cols][K/16], *inscale
+ *            the fp32 input scale (a device pointer, as wscale).
+ * core 0 runs the narrow path's tile (the one the down projection of calls of
+ * up to 8 tokens uses; any K % 32 == 0 up to 4096, any N); core 1 the wide
+ * path's matrix-core loop (MOE_A4; N % 16 == 0, K % 128 == 0) and needs
+ * moe_debug_nvfp4_matmul_workspace_bytes(1, cols) bytes of ws (16-byte
+ * aligned) for its chunk list; core 0 needs none (ws may be NULL).
+ * Products of E2M1 weights with E2M1 (or small-integer) activations are exact,
+ * so with unit scales the result is the exact integer row sum, bit for bit,
+ * in any summation order (page "Infernix releases", release 2026.10.11,
+ * "Highlights": FP4 products and their row sums stay exact). */
+size_t moe_debug_nvfp4_matmul_workspace_bytes(int core, int cols);
+moe_status moe_debug_nvfp4_matmul(int core, moe_act_mode mode, const uint8_t* codes, const uint8_t* scales,
+                                  const float* wscale, int N, int K, const void* x, const void* x_scales,
+                                  const float* inscale, int cols, float* out, void* ws, size_t ws_bytes,
+                                  hipStream_t s);
 
 #ifdef __cplusplus
 }

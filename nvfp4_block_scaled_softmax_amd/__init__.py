@@ -21,7 +21,7 @@ MOE_A16, MOE_A8, MOE_A4 = 0, 1, 2
 MODES = {"A16": MOE_A16, "A8": MOE_A8, "A4": MOE_A4}
 DT_BF16, DT_F32 = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_E_ARG", -2: "MOE_E_ALIGN", -3: "MOE_E_SHAPE",
-          -4: "MOE_E_UNSUPPORTED", -5: "MOE_E_WORKSPACE", -6: "MOE_E_HIP"}
+          -4: "MOE_E_UNSUPPORTED", -5: "MOE_E_WORKSPACE", -6: "MOE_E_HIP", -7: "MOE_E_STALLED"}
 
 EXPORTS = ("moe_last_error", "moe_route_workspace_bytes", "moe_route_topk",
            "moe_permute_workspace_bytes", "moe_permute",
@@ -29,7 +29,8 @@ EXPORTS = ("moe_last_error", "moe_route_workspace_bytes", "moe_route_topk",
            "nvfp4_expert_ffn_workspace_bytes", "nvfp4_expert_ffn", "nvfp4_expert_ffn_stage",
            "moe_combine",
            "moe_layer_workspace_bytes", "moe_layer_workspace_layout", "moe_layer_wait_timeouts_offset",
-           "moe_layer_forward", "moe_layer_forward_stage", "moe_layer_is_fused", "moe_layer_launches")
+           "moe_layer_forward", "moe_layer_forward_stage", "moe_layer_is_fused", "moe_layer_launches",
+           "moe_layer_status", "moe_debug_nvfp4_matmul_workspace_bytes", "moe_debug_nvfp4_matmul")
 
 
 class MoeError(RuntimeError):
@@ -78,6 +79,9 @@ def lib():
             "moe_layer_launches": ([_I, _I, _I, _I, _I], _I),
             "moe_layer_forward_stage": ([ctypes.POINTER(_Experts), _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _Z, _P], _I),
             "moe_layer_forward": ([ctypes.POINTER(_Experts), _I, _P, _P, _P, _I, _I, _P, _P, _P, _Z, _P], _I),
+            "moe_layer_status": ([_P, _P], _I),
+            "moe_debug_nvfp4_matmul_workspace_bytes": ([_I, _I], _Z),
+            "moe_debug_nvfp4_matmul": ([_I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _I, _P, _P, _Z, _P], _I),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -373,9 +377,52 @@ def layer_launches(mode, T, k, H, I):
 
 
 def layer_wait_timeouts(ws):
-    """Waits of the fused decode path that reached their bound (0 in correct operation)."""
+    """Waits of the fused decode path that gave up (0 in correct operation)."""
     o = lib().moe_layer_wait_timeouts_offset()
     return int(ws[o:o + 4].view(torch.int32).item())
+
+
+def moe_layer_status(ws):
+    """Raises MoeError (MOE_E_STALLED) when a fused decode wait on this workspace gave
+    up since it was zero-filled.  Synchronises the current stream."""
+    _need(ws, "ws", torch.uint8)
+    _check("moe_layer_status", lib().moe_layer_status(_ptr(ws), _stream()))
+
+
+def debug_nvfp4_matmul(core, mode, codes, scales, wscale, x, x_scales=None, inscale=None, out=None):
+    """Test-only: the expert kernels' product core, out [cols, N] fp32 =
+    wscale (* inscale) * x . dequant(W)^T (see moe_debug_nvfp4_matmul in the C header).
+    core 0 narrow tile, 1 wide matrix-core loop.  codes uint8 [N, K/2], scales uint8
+    [N, K/16], wscale / inscale fp32 [1] device tensors; x per mode: bf16 [cols, K],
+    uint8 E4M3 [cols, K] (+ fp32 x_scales [cols, K/16]) or uint8 E2M1 [cols, K/2]
+    (+ uint8 x_scales [cols, K/16])."""
+    m = _mode(mode)
+    N, K2 = codes.shape
+    K = 2 * K2
+    _need(codes, "codes", torch.uint8, (N, K // 2))
+    _need(scales, "scales", torch.uint8, (N, K // 16))
+    _need(wscale, "wscale", torch.float32)
+    cols = x.shape[0]
+    if m == MOE_A16:
+        x = _bf16(x, "x")
+        _need(x, "x", shape=(cols, K))
+    elif m == MOE_A8:
+        _need(x, "x", torch.uint8, (cols, K))
+        _need(x_scales, "x_scales", torch.float32, (cols, K // 16))
+    else:
+        _need(x, "x", torch.uint8, (cols, K // 2))
+        _need(x_scales, "x_scales", torch.uint8, (cols, K // 16))
+        _need(inscale, "inscale", torch.float32)
+    if out is None:
+        out = torch.empty(cols, N, dtype=torch.float32, device=codes.device)
+    _need(out, "out", torch.float32, (cols, N))
+    nws = lib().moe_debug_nvfp4_matmul_workspace_bytes(core, cols)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=codes.device)
+    _check("moe_debug_nvfp4_matmul",
+           lib().moe_debug_nvfp4_matmul(core, m, _ptr(codes), _ptr(scales), _ptr(wscale), N, K, _ptr(x),
+                                        _ptr(x_scales), _ptr(inscale), cols, _ptr(out), _ptr(ws), ws.numel(),
+                                        _stream()))
+    return out
 
 
 def workspace_views(ws, mode, T, k, E, H, I):

@@ -23,9 +23,12 @@
 // waited for is resident, done, or gets a slot from a workgroup that finishes
 // without waiting: the waits cannot starve.  (A ticket from one shared atomic
 // counter would not need that order, but 800 workgroups serialised on one
-// counter cost more than the whole expert pass.)  Waits are bounded by a spin
-// cap, so every wave exits whatever happens; a wait that reaches the cap is
-// counted in the state block, where tests check it.
+// counter cost more than the whole expert pass.)  HIP does not promise that
+// dispatch order, so every wait is bounded (Patience: a deadline, and an abort
+// word that the first wait to give up sets, which ends every other wait of the
+// launch at its next check); the call then completes with the combine writing
+// NaN where it gave up, and the abort word (the `timeouts` counter of the state
+// block) stays non-zero for moe_layer_status to report.
 //
 // The data handed between workgroups (logits, h, y, the plan) crosses XCDs,
 // whose L2s are not coherent with each other: it is written and read with
@@ -57,7 +60,6 @@ namespace moe {
 
 constexpr int kDecMaxSlots = 512;     // active experts of a call: at most T * k <= 8 * 64
 constexpr int kDecMaxRowBlocks = kMaxDim / kDnRows;
-constexpr uint32_t kSpinCap = 1u << 22;
 constexpr int kSmallP = 64;           // up to this many pairs the routing tail ranks them directly
 
 // Each counter sits on its own 128-byte line: many workgroups poll or bump them
@@ -69,7 +71,7 @@ struct alignas(128) Counter {
 
 struct DecodeState {
   Counter route_done;                  // A: workgroups finished
-  Counter timeouts;                    // waits that reached the spin cap (stays 0)
+  Counter timeouts;                    // waits that gave up: the abort word (stays 0)
   Counter dev_epoch;                   // single launch under graph capture: the call's epoch,
                                        // advanced by k_epoch_bump before each call
   Counter outs_epoch;                  // single launch: epoch of the call whose routing outputs
@@ -120,13 +122,12 @@ __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Thread 0 waits (bounded) until *p >= want; the data behind the count is
-// then read with device-coherent loads.
-__device__ __forceinline__ void wait_at_least(const uint32_t* p, uint32_t want, uint32_t* timeouts) {
+// Thread 0 waits (bounded, see Patience) until *p >= want; the data behind the
+// count is then read with device-coherent loads.
+__device__ __forceinline__ void wait_at_least(const uint32_t* p, uint32_t want, uint32_t* abort_word) {
   if (threadIdx.x == 0) {
-    uint32_t it = 0;
-    while (ld_relaxed(p) < want && ++it < kSpinCap) __builtin_amdgcn_s_sleep(8);
-    if (it >= kSpinCap) __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    Patience pat;
+    while (ld_relaxed(p) < want && !pat.expired(abort_word)) __builtin_amdgcn_s_sleep(8);
   }
   __syncthreads();
 }
@@ -317,10 +318,9 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
       // the routing outputs are complete once outs_epoch holds the call's epoch
       if (pl.outs_epoch != 0u) {
         if (tid == 0) {
-          uint32_t it = 0;
-          while (ld_relaxed(&st->outs_epoch.v) != pl.outs_epoch && ++it < kSpinCap) __builtin_amdgcn_s_sleep(2);
-          if (it >= kSpinCap)
-            __hip_atomic_fetch_add(&st->timeouts.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          Patience pat;
+          while (ld_relaxed(&st->outs_epoch.v) != pl.outs_epoch && !pat.expired(&st->timeouts.v))
+            __builtin_amdgcn_s_sleep(2);
         }
         __syncthreads();
       }
@@ -346,9 +346,12 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
         const int t = i / kDnRows, ol = i % kDnRows, o = rb * kDnRows + ol;
         if (o >= a.H) continue;
         float acc = 0.0f;
+        // the abort word travels with every poll (no round trip of its own): an
+        // output whose inputs were given up on, here or by a producer, is NaN
+        uint32_t aborted = 0u;
+        Patience pat;
         for (int j0 = 0; j0 < a.k; j0 += 16) {   // as combine_acc4: j ascending, one fma each
           uint64_t v[16];
-          uint32_t it = 0;
           while (true) {
             bool ready = true;
 #pragma unroll
@@ -359,9 +362,10 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
                             : (uint64_t)epoch;   // value 0
               ready = ready && (uint32_t)v[u] == epoch;
             }
+            aborted |= ld_relaxed(&st->timeouts.v);
             if (ready) break;
-            if (++it >= kSpinCap) {
-              __hip_atomic_fetch_add(&st->timeouts.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (pat.expired(&st->timeouts.v)) {
+              aborted = 1u;
               break;
             }
             __builtin_amdgcn_s_sleep(1);
@@ -373,19 +377,26 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
         }
         uint32_t ob = f32_to_bf16(acc);   // as combine_round4, one element
         if (residual) ob = f32_to_bf16(bf16_to_f32(s_res[t][ol]) + bf16_to_f32(ob));
-        out[(size_t)t * a.H + o] = (uint16_t)ob;
+        out[(size_t)t * a.H + o] = aborted != 0u ? kBf16NaN : (uint16_t)ob;
       }
       return;
     }
     wait_vmem();   // this wave's y has reached the device-coherent level
     __syncthreads();
     if (tid == 0) {
+      // the abort word is read beside the counter bump (no round trip of its own)
+      const uint32_t ab = ld_relaxed(&st->timeouts.v);
       const uint32_t c =
           __hip_atomic_fetch_add(&st->dn_done[rb].v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_flag = c == (uint32_t)pl.n_active - 1;
+      s_flag = c == (uint32_t)pl.n_active - 1 ? (ab != 0u ? 2 : 1) : 0;
     }
     __syncthreads();
-    if (s_flag) {   // every expert's rows of this block are in: combine them
+    if (s_flag == 2) {   // a wait of this call gave up: the block's outputs are NaN
+      for (int i = tid; i < a.T * kDnRows; i += kTileThreads) {
+        const int t = i / kDnRows, o = rb * kDnRows + i % kDnRows;
+        if (o < a.H) out[(size_t)t * a.H + o] = kBf16NaN;
+      }
+    } else if (s_flag) {   // every expert's rows of this block are in: combine them
       const int n4 = kDnRows / 4, c0 = rb * n4;
       for (int i = tid; i < a.T * n4; i += kTileThreads) {
         const int t = i / n4, c = c0 + i % n4;
@@ -490,7 +501,7 @@ __global__ void __launch_bounds__(kTileThreads)
       const uint64_t* row = st->logit_tag + (size_t)t * E;
       const int lane = lane_id();
       uint64_t v[S];
-      uint32_t it = 0;
+      Patience pat;
       while (true) {
         bool mine = true;
 #pragma unroll
@@ -501,11 +512,9 @@ __global__ void __launch_bounds__(kTileThreads)
           mine = mine && (uint32_t)v[i] == epoch;
         }
         if (__all(mine)) break;
-        if (++it >= kSpinCap) {
-          if (lane == 0)
-            __hip_atomic_fetch_add(&st->timeouts.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
+        // every lane polls in step, so the wave gives up as one (stale logits
+        // still give valid expert ids: each key's slot is its expert)
+        if (pat.expired(&st->timeouts.v)) break;
         __builtin_amdgcn_s_sleep(2);
       }
       int key[S];
@@ -543,17 +552,16 @@ __global__ void __launch_bounds__(kTileThreads)
       [&](int slot, int role) {
         if (tid == 0) {
           const uint64_t* e = &st->pub[role][slot];
-          uint32_t it = 0;
+          Patience pat;
           uint64_t v;
           while (true) {
             v = __hip_atomic_load(e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if ((uint32_t)v == epoch || ++it >= kSpinCap) break;
+            if ((uint32_t)v == epoch || pat.expired(&st->timeouts.v)) break;
             __builtin_amdgcn_s_sleep(4);
           }
           const uint32_t ex = (uint32_t)(v >> 32) & 0x7FFu;
           if ((uint32_t)v != epoch) {
-            __hip_atomic_fetch_add(&st->timeouts.v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_pl = SlotPlan{-1, 0, 0, 0, -1, 0u};   // give up on this tile
+            s_pl = SlotPlan{-1, 0, 0, 0, -1, 0u};   // gave up on this tile
           } else {
             const int tmask = (int)((v >> 43) & 0xFFu);
             s_pl = ex == kNoExpert ? SlotPlan{-1, 0, 0, 0, -1, 0u}

@@ -341,4 +341,30 @@ __device__ __forceinline__ uint4 hld128(const void* base, size_t off) {
 // (s_waitcnt vmcnt(0); the other counters untouched).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// A bounded wait between workgroups of one launch.  It gives up when the abort
+// word (a counter in the caller's workspace) is non-zero, which means another
+// wait of the call, or of an earlier call on the same workspace, has given up;
+// or when kWaitTicks of the 100 MHz real-time counter have passed since it
+// began, and then it bumps the abort word itself.  So one stalled producer ends
+// every wait of the launch within one check, and the count stays non-zero (the
+// workspace must be zero-filled again) for the host to see.  The word and the
+// clock are checked every 32nd poll; a poll loop calls expired() once per poll.
+constexpr uint64_t kWaitTicks = 1ull << 26;   // ~0.67 s; a correct call waits microseconds
+
+struct Patience {
+  uint64_t t0;
+  uint32_t polls;
+  __device__ __forceinline__ Patience() : t0(__builtin_amdgcn_s_memrealtime()), polls(0u) {}
+  __device__ __forceinline__ bool expired(uint32_t* abort_word) {
+    if ((++polls & 31u) != 0u) return false;
+    if (__hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) return true;
+    if (__builtin_amdgcn_s_memrealtime() - t0 < kWaitTicks) return false;
+    __hip_atomic_fetch_add(abort_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+  }
+};
+
+// bf16 NaN: what a combine writes for an output whose inputs it gave up on.
+constexpr uint16_t kBf16NaN = 0x7FC0;
+
 }  // namespace moe

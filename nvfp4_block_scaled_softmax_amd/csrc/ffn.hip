@@ -236,3 +236,51 @@ extern "C" moe_status nvfp4_expert_ffn_stage(const moe_nvfp4_experts* w, moe_act
   return ffn_entry("nvfp4_expert_ffn_stage", w, mode, 1 << stage, x, T, k, expert_offsets,
                    sorted_pairs, y_pairs, ws, ws_bytes, s);
 }
+
+// ------------------------------------------------------------------ debug core
+extern "C" size_t moe_debug_nvfp4_matmul_workspace_bytes(int core, int cols) {
+  if (cols < 1 || (core != 0 && core != 1)) return 0;
+  return core == 1 ? moe::debug_wide_plan_bytes(cols) : 0;
+}
+
+extern "C" moe_status moe_debug_nvfp4_matmul(int core, moe_act_mode mode, const uint8_t* codes,
+                                             const uint8_t* scales, const float* wscale, int N, int K,
+                                             const void* x, const void* x_scales, const float* inscale,
+                                             int cols, float* out, void* ws, size_t ws_bytes,
+                                             hipStream_t s) {
+  const char* name = "moe_debug_nvfp4_matmul";
+  moe::clear_error();
+  MOE_REQUIRE(core == 0 || core == 1, MOE_E_ARG, "%s: core %d is not 0 (narrow) or 1 (wide)", name, core);
+  MOE_REQUIRE(mode == MOE_A16 || mode == MOE_A8 || mode == MOE_A4, MOE_E_ARG, "%s: bad mode %d", name,
+              (int)mode);
+  MOE_REQUIRE(codes && scales && wscale && x && out, MOE_E_ARG, "%s: null pointer argument", name);
+  MOE_REQUIRE(mode == MOE_A16 || x_scales, MOE_E_ARG, "%s: 8/4-bit x needs x_scales", name);
+  MOE_REQUIRE(mode != MOE_A4 || inscale, MOE_E_ARG, "%s: 4-bit x needs inscale", name);
+  MOE_REQUIRE(N >= 1 && N <= (1 << 20) && moe::dim_ok(K) && cols >= 1 && cols <= (1 << 16), MOE_E_SHAPE,
+              "%s: bad shape N=%d K=%d cols=%d", name, N, K, cols);
+  MOE_REQUIRE(moe::aligned(codes, 16) && moe::aligned(scales, 16) && moe::aligned(x, 16) &&
+                  moe::aligned(out, 16) && moe::aligned(wscale, 4) && (!inscale || moe::aligned(inscale, 4)) &&
+                  (!x_scales || moe::aligned(x_scales, 16)),
+              MOE_E_ALIGN, "%s: misaligned pointer", name);
+  if (core == 1) {
+    MOE_REQUIRE(mode == MOE_A4, MOE_E_UNSUPPORTED, "%s: the wide core takes 4-bit x", name);
+    MOE_REQUIRE(N % 16 == 0 && K % 128 == 0, MOE_E_SHAPE, "%s: the wide core needs N %% 16 == 0, K %% 128 == 0",
+                name);
+    MOE_REQUIRE(ws && moe::aligned(ws, 16) && ws_bytes >= moe::debug_wide_plan_bytes(cols), MOE_E_WORKSPACE,
+                "%s: workspace %zu < %zu bytes", name, ws_bytes, moe::debug_wide_plan_bytes(cols));
+  }
+  moe::FfnArgs a{};
+  a.dn_codes = codes;
+  a.dn_scales = scales;
+  a.dn_wscale = wscale;
+  a.dn_inscale = inscale;
+  a.E = 1;
+  a.H = N;
+  a.I = K;
+  a.T = cols;
+  a.k = 1;
+  a.h_codes = const_cast<uint8_t*>(static_cast<const uint8_t*>(x));
+  a.h_scales = const_cast<void*>(x_scales);
+  a.y = out;
+  return core == 1 ? moe::launch_debug_wide(a, ws, s) : moe::launch_debug_narrow(a, mode, s);
+}

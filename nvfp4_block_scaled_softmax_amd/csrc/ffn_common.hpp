@@ -161,6 +161,12 @@ FfnArgs make_ffn_args(const moe_nvfp4_experts& w, moe_act_mode mode, const uint1
 moe_status launch_ffn_wide_a4(const FfnArgs& a, int stage_mask, void* plan_ws, hipStream_t s);
 // Entries of the wide path's work plan for P sorted rows of E experts.
 int wide_plan_entries(int P, int E);
+// The product cores alone (moe_debug_nvfp4_matmul), on an argument block whose
+// expert 0 down matrix is the N x K operand (H = N, I = K) and whose
+// intermediate slots (h_codes, h_scales) hold the T columns.
+moe_status launch_debug_narrow(const FfnArgs& a, moe_act_mode mode, hipStream_t s);
+moe_status launch_debug_wide(const FfnArgs& a, void* plan_ws, hipStream_t s);
+size_t debug_wide_plan_bytes(int cols);
 
 // Calls with more than this many tokens take the MFMA path (4-bit mode).
 constexpr int kNarrowMaxT = 8;

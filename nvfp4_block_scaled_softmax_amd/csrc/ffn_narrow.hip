@@ -56,6 +56,15 @@ __global__ void __launch_bounds__(kTileThreads) k_down_narrow(FfnArgs a, int max
                                    NoHook{});
 }
 
+// The product core alone (moe_debug_nvfp4_matmul): the down tile over one
+// matrix of N = a.H rows and K = a.I, its T columns from the intermediate's
+// workspace slots (h_codes / h_scales), no plan and no SwiGLU.
+template <int MODE, int LPR, int CPL>
+__global__ void __launch_bounds__(kTileThreads) k_debug_narrow(FfnArgs a, int max_cols) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  down_tile<MODE, LPR, CPL, false>(a, 0, 0, a.T, blockIdx.x, max_cols, lds, NoHook{});
+}
+
 // ------------------------------------------------------------------ launch
 template <int MODE, int LPR, int CPL>
 static void launch_gu(const FfnArgs& a, int slots, int max_cols, hipStream_t s) {
@@ -103,6 +112,37 @@ static moe_status run(const FfnArgs& a, int slots, int stage_mask, hipStream_t s
     return check_launch("nvfp4_expert_ffn (down)");
   }
   return MOE_OK;
+}
+
+template <int MODE, int LPR, int CPL>
+static void launch_dbg(const FfnArgs& a, int max_cols, hipStream_t s) {
+  const size_t lds = (size_t)max_cols * (a.I / 32) * ChunkLds<MODE>::kStride;
+  hipLaunchKernelGGL((k_debug_narrow<MODE, LPR, CPL>), dim3((a.H + kDnRows - 1) / kDnRows), dim3(kTileThreads),
+                     lds, s, a, max_cols);
+}
+
+template <int MODE>
+static moe_status run_debug(const FfnArgs& a, hipStream_t s) {
+  const int per_col = (a.I / 32) * ChunkLds<MODE>::kStride;
+  const int cols = max(1, min(min(8, a.T), kLdsBudget / per_col));
+  const int NC = a.I / 32;
+  // the lanes-per-row / chunks-per-lane choice of the per-stage kernels
+  if (NC <= 4) launch_dbg<MODE, 4, 1>(a, cols, s);
+  else if (NC <= 8) launch_dbg<MODE, 8, 1>(a, cols, s);
+  else if (NC <= 16) launch_dbg<MODE, 16, 1>(a, cols, s);
+  else if (NC <= 32) launch_dbg<MODE, 32, 1>(a, cols, s);
+  else if (NC <= 64) launch_dbg<MODE, 32, 2>(a, cols, s);
+  else if (NC <= 96) launch_dbg<MODE, 32, 3>(a, cols, s);
+  else launch_dbg<MODE, 32, 4>(a, cols, s);
+  return check_launch("moe_debug_nvfp4_matmul (narrow)");
+}
+
+moe_status launch_debug_narrow(const FfnArgs& a, moe_act_mode mode, hipStream_t s) {
+  switch (mode) {
+    case MOE_A16: return run_debug<MOE_A16>(a, s);
+    case MOE_A8: return run_debug<MOE_A8>(a, s);
+    default: return run_debug<MOE_A4>(a, s);
+  }
 }
 
 moe_status launch_ffn_narrow(const FfnArgs& a, moe_act_mode mode, int slots, int stage_mask,

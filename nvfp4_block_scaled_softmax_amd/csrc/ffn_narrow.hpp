@@ -352,11 +352,12 @@ template <int MODE, int LPR, int CPL, bool COH, typename Wait>
 // ytag[row * H + o] = (value bits << 32) | epoch (one atomic store), for a
 // consumer that polls the words instead of waiting on a counter.
 // With htag (16-bit activations), h is read from the tagged words that
-// gateup_tile publishes, each polled until it carries epoch.
+// gateup_tile publishes, each polled until it carries epoch (a bounded wait on
+// abort_word, see Patience; a thread that gives up uses whatever it read).
 __device__ __forceinline__ void down_tile(const FfnArgs& a, int e, int row0, int ne, int rb,
                                           int max_cols, uint8_t* lds, Wait&& wait,
                                           uint64_t* ytag = nullptr, uint32_t epoch = 0u,
-                                          const uint64_t* htag = nullptr, uint32_t* timeouts = nullptr) {
+                                          const uint64_t* htag = nullptr, uint32_t* abort_word = nullptr) {
   __shared__ float outb[8][kDnRows];
   constexpr int S = ChunkLds<MODE>::kStride;
   constexpr int SLOTS = 64 / LPR;
@@ -393,13 +394,15 @@ __device__ __forceinline__ void down_tile(const FfnArgs& a, int e, int row0, int
     if (MODE == MOE_A16 && htag) {
       // word p of a row holds h 2p, 2p+1: chunk p / 16, bytes 4 (p % 16) of it
       const int half = I / 2;
+      Patience pat;   // one budget for all of this thread's words
+      bool gave_up = false;
       for (int i = threadIdx.x; i < ncol * half; i += kTileThreads) {
         const int col = i / half, p = i % half;
         const uint64_t* w = htag + (size_t)(row0 + c0 + col) * half + p;
         uint64_t v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (uint32_t it = 0; (uint32_t)v != epoch; ++it) {
-          if (it >= (1u << 22)) {
-            __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        while ((uint32_t)v != epoch && !gave_up) {
+          if (pat.expired(abort_word)) {
+            gave_up = true;
             break;
           }
           __builtin_amdgcn_s_sleep(1);

@@ -449,6 +449,29 @@ static unsigned wide_grid(int entries, int nrb) {
   return (unsigned)(((entries + kXcds - 1) / kXcds) * kXcds * nrb);
 }
 
+// The product core alone (moe_debug_nvfp4_matmul): one matrix of N = a.H rows
+// and K = a.I as expert 0's down matrix, its a.T columns cut into chunks of 32.
+__global__ void __launch_bounds__(256) k_debug_plan(int cols, int n_entries, int4* __restrict__ plan) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j < n_entries)
+    plan[j] = j * kWideTok < cols ? make_int4(0, j * kWideTok, min(kWideTok, cols - j * kWideTok), 0)
+                                  : make_int4(-1, 0, 0, 0);
+}
+
+size_t debug_wide_plan_bytes(int cols) { return (size_t)((cols + kWideTok - 1) / kWideTok) * sizeof(int4); }
+
+moe_status launch_debug_wide(const FfnArgs& a, void* plan_ws, hipStream_t s) {
+  int4* plan = static_cast<int4*>(plan_ws);
+  const int n = (a.T + kWideTok - 1) / kWideTok;
+  hipLaunchKernelGGL(k_debug_plan, dim3((n + 255) / 256), dim3(256), 0, s, a.T, n, plan);
+  moe_status st = check_launch("moe_debug_nvfp4_matmul (plan)");
+  if (st != MOE_OK) return st;
+  const int nrb = (a.H + kDownRows - 1) / kDownRows;
+  hipLaunchKernelGGL(k_down_wide_a4<kDownWaves>, dim3(wide_grid(n, nrb)), dim3(kDownWaves * kWave), 0, s, a,
+                     plan, n);
+  return check_launch("moe_debug_nvfp4_matmul (wide)");
+}
+
 moe_status launch_ffn_wide_a4(const FfnArgs& a, int stage_mask, void* plan_ws, hipStream_t s) {
   int4* plan = static_cast<int4*>(plan_ws);
   const int n = wide_plan_entries(a.T * a.k, a.E);

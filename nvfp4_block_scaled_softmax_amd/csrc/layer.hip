@@ -155,3 +155,18 @@ extern "C" moe_status moe_layer_forward_stage(const moe_nvfp4_experts* w, moe_ac
   return layer_call("moe_layer_forward_stage", w, mode, 1 << stage, x, w_router, router_bias, T,
                     k, residual, out, ws, ws_bytes, s);
 }
+
+extern "C" moe_status moe_layer_status(const void* ws, hipStream_t s) {
+  moe::clear_error();
+  MOE_REQUIRE(ws, MOE_E_ARG, "moe_layer_status: null workspace");
+  uint32_t v = 0u;
+  hipError_t e = hipMemcpyAsync(&v, static_cast<const uint8_t*>(ws) + moe::decode_timeouts_offset(), 4,
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  MOE_REQUIRE(e == hipSuccess, MOE_E_HIP, "moe_layer_status: %s", hipGetErrorString(e));
+  MOE_REQUIRE(v == 0u, MOE_E_STALLED,
+              "moe_layer_status: %u wait(s) of the fused decode path gave up on this workspace; "
+              "the outputs of the calls since it was zero-filled are unreliable (NaN where seen)",
+              v);
+  return MOE_OK;
+}

@@ -252,21 +252,6 @@ def moe_layer(x_bf16, wr_bf16, k, get_expert, mode, bias=None):
     return LayerResult(r, perm, ffn, y_sorted, acc, out)
 
 
-def moe_stack(x0_bf16, layers, k, mode):
-    """Layers chained through the residual stream: x_{l+1} = bf16(x_l + layer_l(x_l)).
-
-    ``layers`` yields (wr_bf16, get_expert, bias) per layer.  Returns the list of
-    LayerResult and the list of inputs x_0 .. x_L (bf16 bits).
-    """
-    xs = [np.asarray(x0_bf16, np.uint16)]
-    results = []
-    for wr, get_expert, bias in layers:
-        res = moe_layer(xs[-1], wr, k, get_expert, mode, bias)
-        results.append(res)
-        xs.append(residual_add(xs[-1], res.out))
-    return results, xs
-
-
 # ----------------------------------------------------------------------------- calibration
 def calibrate_input_scales(x_calib_bf16, experts):
     """Activation input scales of 4-bit mode from a calibration batch.

@@ -130,3 +130,39 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         moe.moe_permute(torch.zeros(2, 2, dtype=torch.int32), 4)
+
+
+def test_debug_matmul_validation():
+    """The test-only product core: host-side checks before anything is enqueued."""
+    L = moe.lib()
+    f = L.moe_debug_nvfp4_matmul
+    assert L.moe_debug_nvfp4_matmul_workspace_bytes(0, 40) == 0
+    assert L.moe_debug_nvfp4_matmul_workspace_bytes(1, 40) == 2 * 16     # two chunks of <= 32 columns
+    assert L.moe_debug_nvfp4_matmul_workspace_bytes(2, 40) == 0
+    ok = dict(core=0, mode=moe.MOE_A16, codes=P16, scales=P16, wscale=P16, N=256, K=3072, x=P16,
+              x_scales=None, inscale=None, cols=8, out=P16, ws=None, nws=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return _err(f(a["core"], a["mode"], a["codes"], a["scales"], a["wscale"], a["N"], a["K"], a["x"],
+                      a["x_scales"], a["inscale"], a["cols"], a["out"], a["ws"], a["nws"], None))[0]
+
+    assert call(core=2) == "MOE_E_ARG"
+    assert call(mode=5) == "MOE_E_ARG"
+    assert call(codes=None) == "MOE_E_ARG"
+    assert call(mode=moe.MOE_A8) == "MOE_E_ARG"                          # 8-bit x needs its scales
+    assert call(mode=moe.MOE_A4, x_scales=P16) == "MOE_E_ARG"            # 4-bit x needs the input scale
+    assert call(K=3000) == "MOE_E_SHAPE"
+    assert call(cols=0) == "MOE_E_SHAPE"
+    assert call(x=P4) == "MOE_E_ALIGN"
+    assert call(core=1) == "MOE_E_UNSUPPORTED"                           # wide core: 4-bit x
+    a4 = dict(mode=moe.MOE_A4, x_scales=P16, inscale=P16)
+    assert call(core=1, N=250, **a4) == "MOE_E_SHAPE"                    # N % 16
+    assert call(core=1, K=3040, **a4) == "MOE_E_SHAPE"                   # K % 128
+    assert call(core=1, **a4) == "MOE_E_WORKSPACE"                       # chunk list needed
+    assert call(core=1, ws=P16, nws=8, **a4) == "MOE_E_WORKSPACE"
+
+
+def test_layer_status_validation():
+    L = moe.lib()
+    assert _err(L.moe_layer_status(None, None))[0] == "MOE_E_ARG"

@@ -337,8 +337,9 @@ def test_tiny_layer_matches_oracle(dev, mode):
         fv = {n: host(t) for n, t in moe.ffn_workspace_views(moe.workspace_views(wsb, mode, T, k, E, H, I)["ffn"], mode, T, k, H, I).items()}
         r, flipped = parity.check_route(x, wr, None, k, v["topk_ids"], v["topk_w"])
         parity.check_permutation(v["topk_ids"], E, v["expert_offsets"], v["sorted_pairs"], v["pair_row"], r.ids)
-        y_exp, _ = parity.check_experts(w, mode, x, cache, k, v["expert_offsets"], v["sorted_pairs"], v["y_pairs"], fv)
-        parity.check_output(host(out), y_exp, v["pair_row"], r, v["topk_ids"], k)
+        y_exp, info = parity.check_experts(w, mode, x, cache, k, v["expert_offsets"], v["sorted_pairs"], v["y_pairs"], fv)
+        parity.check_output(host(out), y_exp, v["pair_row"], r, v["topk_ids"], k, mode=mode,
+                            y_nom=info["y_nominal"], row_flipped=info["row_flipped"], oracle_ids=r.ids)
 
 
 def test_layer_is_deterministic(dev):

@@ -4,9 +4,9 @@ The layer is built as bench.py builds it: expert weights drawn on the GPU by
 the seeded generator and NVFP4-packed by the library.  The oracle packs the
 same experts from the host build of the generator; the packed bytes of every
 expert a checked token touches must be identical (act_quant_nvfp4 on real
-weight matrices), and the layer output is checked token by token.  Where the
-oracle would need minutes (1024-token prefill, 48 layers) it checks a sample
-of tokens or layers; properties that hold at any size are checked on all.
+weight matrices), and the layer output is checked token by token: every token
+of every call, the 1024-token prefill chunk included, and every layer of the
+48-layer stack (each GPU layer fed the oracle chain's own input).
 """
 import numpy as np
 import pytest
@@ -44,7 +44,7 @@ _LAYERS = {}
 
 
 def gpu_layer_pair(w, layer, mode, dev):
-    """Like gpu_layer, but two layers of one workload may be held at once."""
+    """Like gpu_layer, but several layers of one workload may be held at once."""
     key = ("pair", w.index, layer, mode)
     if key not in _LAYERS:
         say("building layer", key)
@@ -74,8 +74,10 @@ def check_packed_bytes(ex_gpu, cache, experts):
         assert host(ex_gpu.dn_wscale[e]).view(np.uint32) == np.float32(o.dn_wscale).view(np.uint32), e
 
 
-def check_call(w, mode, layer, x, out, ws, sample=None):
-    """Full parity of one GPU layer call on tokens x (bf16 bits) against the oracle."""
+def check_call(w, mode, layer, x, out, ws, sample=None, ex=None, cache=None):
+    """Full parity of one GPU layer call on tokens x (bf16 bits) against the oracle.
+    ex: the GPU experts (default: the cached layer); cache: an oracle ExpertCache
+    to reuse (default: a new one)."""
     T = x.shape[0]
     wr = synth.router_weight(w, layer)
     bias_np = synth.zipf_bias(w)
@@ -84,17 +86,21 @@ def check_call(w, mode, layer, x, out, ws, sample=None):
     fv = {n: host(t) for n, t in moe.ffn_workspace_views(views["ffn"], mode, T, w.k, w.H, w.I).items()}
     r, flipped = parity.check_route(x, wr, bias_np, w.k, v["topk_ids"], v["topk_w"])
     parity.check_permutation(v["topk_ids"], w.E, v["expert_offsets"], v["sorted_pairs"], v["pair_row"], r.ids)
-    ins = synth.load_input_scales(w) if mode == "A4" else None
-    cache = oracle_cache.ExpertCache(w, layer, ins)
+    if cache is None:
+        ins = synth.load_input_scales(w) if mode == "A4" else None
+        cache = oracle_cache.ExpertCache(w, layer, ins)
     toks = np.arange(T) if sample is None else np.asarray(sample)
     touched = np.unique(v["topk_ids"][toks])
     cache.prefetch(touched)
-    ex = _LAYERS[(w.index, layer, mode)][0]
+    if ex is None:
+        ex = _LAYERS[(w.index, layer, mode)][0]
     check_packed_bytes(ex, cache, touched)
     rep = ties.TieReport()
     y_exp, info = parity.check_experts(w, mode, x, cache, w.k, v["expert_offsets"], v["sorted_pairs"],
                                        v["y_pairs"], fv, tokens=None if sample is None else toks, report=rep)
-    info.update(parity.check_output(host(out), y_exp, v["pair_row"], r, v["topk_ids"], w.k, tokens=toks))
+    y_nom, rflip = info.pop("y_nominal"), info.pop("row_flipped")
+    info.update(parity.check_output(host(out), y_exp, v["pair_row"], r, v["topk_ids"], w.k, tokens=toks,
+                                    mode=mode, y_nom=y_nom, row_flipped=rflip, oracle_ids=r.ids))
     info["router_flips"] = len(flipped)
     info["experts_touched"] = int(len(np.unique(v["topk_ids"])))
     say("ok", info)
@@ -108,6 +114,7 @@ def run_and_check(w, mode, layer, batch, dev, T=None, sample=None):
     say("layer", w.index, mode, "layer", layer, "batch", batch, "T", T)
     out, ws = moe.moe_layer_forward(ex, mode, bench.token_batch(w, batch, dev, T), router, w.k, bias=bias)
     torch.cuda.synchronize()
+    moe.moe_layer_status(ws)           # no wait of the call gave up
     info, v = check_call(w, mode, layer, x, out, ws, sample)
     return info, v, host(out)
 
@@ -128,13 +135,13 @@ def test_verify_w4a4(dev):
     run_and_check(w, "A4", 0, 1, dev)
 
 
+@pytest.mark.timeout(900)
 def test_prefill_w4a4_zipf(dev):
-    """1024-token prefill chunk with a Zipf-biased router: all tokens' routing and the
-    permutation are checked; experts and outputs on a sample of tokens."""
+    """1024-token prefill chunk with a Zipf-biased router: every token's routing, the
+    permutation, all 10,240 pairs' activation codes, intermediates and down outputs
+    (all 512 experts), and every token's output."""
     w = synth.CONFIGS[4]
-    rng = np.random.default_rng(4)
-    sample = np.sort(rng.choice(w.T, 12, replace=False))
-    info, v, out = run_and_check(w, "A4", 0, 0, dev, sample=sample)
+    info, v, out = run_and_check(w, "A4", 0, 0, dev)
     counts = np.diff(v["expert_offsets"])
     say("expert counts: max", counts.max(), "median", np.median(counts), "empty", int((counts == 0).sum()))
     assert counts.max() >= 64                     # the bias skews the load
@@ -173,46 +180,43 @@ def test_decode_fused_equals_stages(dev, wi, mode):
     assert moe.layer_wait_timeouts(ws) == 0
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("mode", ["A16", "A8"])
 def test_stack_layers(dev, mode):
-    """48-layer decode stack, T=2: each layer consumes the previous layer's residual
-    stream x_{l+1} = bf16(x_l + out_l), routing recomputed per layer.  The oracle
-    runs its own chain (its inputs never come from the GPU); while the GPU chain's
-    input is bit-identical to the oracle's, the layer call gets the full parity
-    check.  Every layer of the 48: the fused residual output equals
-    bf16(x + out) of the same call, weights sum to one, values are finite."""
+    """48-layer decode stack, T=2, routing recomputed per layer.  Every layer gets the
+    full parity check on the oracle chain's own input: the oracle runs
+    x_{l+1} = bf16(x_l + out_l) from x_0, and GPU layer l is called on the oracle's
+    x_l (its inputs never come from the GPU).  On the same input the fused residual
+    call equals bf16(x + out) of the plain call.  Beside it the GPU runs its own
+    chain from x_0; its drift from the oracle chain after 48 layers is reported."""
     w = synth.CONFIGS[3]
-    n_oracle = 3
     xo = synth.tokens(w, batch=0)
     xg = bench.token_batch(w, 0, dev)
-    checked = 0
+    worst, flips, two = 0.0, 0, 0
     for l in range(w.layers):
         ex, router, bias = gpu_layer(w, l, mode, dev)
-        out, ws = moe.moe_layer_forward(ex, mode, xg, router, w.k)
-        nxt, _ = moe.moe_layer_forward(ex, mode, xg, router, w.k, residual=xg)
+        x_or = torch.from_numpy(xo.view(np.int16)).to(dev).view(torch.bfloat16)
+        out, ws = moe.moe_layer_forward(ex, mode, x_or, router, w.k)
+        nxt, _ = moe.moe_layer_forward(ex, mode, x_or, router, w.k, residual=x_or)
+        xg, _ = moe.moe_layer_forward(ex, mode, xg, router, w.k, residual=xg)   # the GPU's own chain
         torch.cuda.synchronize()
-        xg_h, out_h, nxt_h = host(xg), host(out), host(nxt)
-        tw = host(moe.workspace_views(ws, mode, w.T, w.k, w.E, w.H, w.I)["topk_w"])
-        assert np.allclose(tw.sum(axis=1), 1.0, atol=1e-6)
-        s = (torch.from_numpy(xg_h.astype(np.uint32) << 16).view(torch.float32)
-             + torch.from_numpy(out_h.astype(np.uint32) << 16).view(torch.float32))
-        fused = s.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-        assert np.array_equal(nxt_h, fused)
-        assert np.all(np.isfinite(F.bf16_to_f64(nxt_h)))
-        if l < n_oracle:
-            cache = oracle_cache.ExpertCache(w, l)
-            res = OL.moe_layer(xo, synth.router_weight(w, l), w.k, cache, mode)
-            if np.array_equal(xg_h, xo):
-                check_call(w, mode, l, xo, out, ws)
-                checked += 1
-            else:
-                got, want = F.bf16_to_f64(out_h), F.bf16_to_f64(res.out)
-                rel = np.linalg.norm(got - want, axis=1) / np.linalg.norm(want, axis=1)
-                say("stack", mode, "layer", l, "inputs differ; output rel L2", rel)
-                assert np.all(rel <= 4 * parity.OUT_TOL), rel
-            xo = OL.residual_add(xo, res.out)
-        xg = nxt
-    assert checked >= 1
+        out_h, nxt_h = host(out), host(nxt)
+        s_ = (torch.from_numpy(xo.astype(np.uint32) << 16).view(torch.float32)
+              + torch.from_numpy(out_h.astype(np.uint32) << 16).view(torch.float32))
+        assert np.array_equal(nxt_h, s_.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+        assert moe.layer_wait_timeouts(ws) == 0
+        cache = oracle_cache.ExpertCache(w, l)
+        info, _ = check_call(w, mode, l, xo, out, ws, cache=cache)
+        worst = max(worst, info["out_worst_rel_l2"])
+        flips += info["tie_flipped"]
+        two += info["tie_two_candidate"]
+        res = OL.moe_layer(xo, synth.router_weight(w, l), w.k, cache, mode)
+        xo = OL.residual_add(xo, res.out)
+    got, want = F.bf16_to_f64(host(xg)), F.bf16_to_f64(xo)
+    drift = np.linalg.norm(got - want, axis=1) / np.linalg.norm(want, axis=1)
+    say("stack", mode, "48 layers checked; worst per-layer rel L2", worst, "flipped h codes", flips, "of", two,
+        "two-candidate; GPU chain drift after 48 layers (reported, not gated):", drift)
+    assert np.all(np.isfinite(got))
     _LAYERS.clear()
     torch.cuda.empty_cache()
 
@@ -328,6 +332,7 @@ def test_decode_graph_replay(dev):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out_g.view(torch.int16), ref.view(torch.int16)), rep
+        check_call(w, "A16", 0, synth.tokens(w, batch=batch), out_g, ws_g)   # the replay against the oracle
     assert moe.layer_wait_timeouts(ws_g) == 0 and moe.layer_wait_timeouts(ws_e) == 0
 
 
@@ -368,5 +373,53 @@ def test_decode_graph_chain(dev):
         torch.cuda.synchronize()
         assert torch.equal(bufs[1].view(torch.int16), ref.view(torch.int16)), rep
     assert moe.layer_wait_timeouts(ws_g) == 0 and moe.layer_wait_timeouts(ws_e) == 0
+    _LAYERS.clear()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+def test_decode_graph_layers_oracle(dev):
+    """Six single-launch layer calls of the 48-layer stack workload (layers 0-5, T=2)
+    captured as one graph, each with its own input, workspace and output.  Before
+    each of two replays the inputs are set to the oracle chain's x_0 .. x_5 (the
+    oracle's inputs, never the GPU's); every replayed call then gets the full
+    parity check against the oracle."""
+    w = synth.CONFIGS[3]
+    mode, n = "A16", 6
+    layers = [gpu_layer_pair(w, l, mode, dev) for l in range(n)]
+    nws = moe.layer_workspace_bytes(mode, w.T, w.k, w.E, w.H, w.I)
+    wss = [torch.zeros(nws, dtype=torch.uint8, device=dev) for _ in range(n)]
+    xins = [torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev) for _ in range(n)]
+    outs = [torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev) for _ in range(n)]
+    caches = [oracle_cache.ExpertCache(w, l) for l in range(n)]
+
+    def calls():
+        for l in range(n):
+            ex, router, bias = layers[l]
+            moe.moe_layer_forward(ex, mode, xins[l], router, w.k, bias=bias, ws=wss[l], out=outs[l])
+
+    for xi in xins:
+        xi.copy_(bench.token_batch(w, 0, dev))
+    calls()   # warm up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep_, batch in enumerate((1, 2)):
+        xo = synth.tokens(w, batch=batch)
+        chain = []
+        for l in range(n):
+            chain.append(xo)
+            res = OL.moe_layer(xo, synth.router_weight(w, l), w.k, caches[l], mode)
+            xo = OL.residual_add(xo, res.out)
+        for l in range(n):
+            xins[l].copy_(torch.from_numpy(chain[l].view(np.int16)).to(dev).view(torch.bfloat16))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for l in range(n):
+            say("graph layers replay", rep_, "layer", l)
+            check_call(w, mode, l, chain[l], outs[l], wss[l], ex=layers[l][0], cache=caches[l])
+            assert moe.layer_wait_timeouts(wss[l]) == 0
     _LAYERS.clear()
     torch.cuda.empty_cache()

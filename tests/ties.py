@@ -16,6 +16,18 @@ helpers compare "what is unique" exactly and check that "the rest is valid":
 
 All arithmetic here uses the oracle's own rounding functions; GPU data only
 selects among candidates the oracle produced and is validated first.
+
+How many choices may differ.  The window is a worst-case bound on the fp32
+sums' error, far wider than the error itself (the rounding errors of a
+few-thousand-term sum of random-sign terms are about 2^-24 sqrt(depth)
+||terms||_2, against 2^-17 ||terms||_1 here: a factor of about 10^3 at K =
+3072).  So about half of all elements are "two-candidate" (their window holds
+a rounding midpoint), yet an honest kernel flips only those whose midpoint lies
+within its actual error: a fraction of order 10^-3 .. 10^-2 of them.  A
+systematic bias or a dropped small term of the size of the window would flip
+about half.  The tests therefore bound the flips: at most FLIP_FRACTION of the
+two-candidate elements, plus FLIP_SLACK (counted in a TieReport, printed with
+every check).
 """
 from __future__ import annotations
 
@@ -29,6 +41,9 @@ from oracle import quant as Q
 SUM_WINDOW = 2.0 ** -17
 # Relative error of the fp32 SwiGLU evaluation itself (a few ulps).
 SWIGLU_WINDOW = 2.0 ** -20
+# Flip budget: flipped choices <= FLIP_FRACTION * two-candidate elements + FLIP_SLACK.
+FLIP_FRACTION = 0.1
+FLIP_SLACK = 3
 
 
 def h_error_bound(res):
@@ -44,13 +59,24 @@ def h_error_bound(res):
 class TieReport:
     def __init__(self):
         self.elements = 0
-        self.nominal = 0
-        self.flipped = 0
+        self.two_candidate = 0      # elements whose window admits a second code
+        self.flipped = 0            # GPU code != the oracle's nominal code
         self.block_scale_flips = 0
         self.bad = []
+        self.row_flips = None       # per row of the last call: any flipped element
+
+    def budget(self):
+        return FLIP_FRACTION * self.two_candidate + FLIP_SLACK
+
+    def check(self):
+        assert not self.bad, f"intermediate codes outside the tie windows: {self.bad[:5]}"
+        assert self.flipped <= self.budget(), \
+            f"{self.flipped} flipped intermediate codes exceed the budget {self.budget():.0f} ({self!r})"
 
     def __repr__(self):
-        return (f"TieReport(elements={self.elements}, flipped={self.flipped}, "
+        frac = self.flipped / self.two_candidate if self.two_candidate else 0.0
+        return (f"TieReport(elements={self.elements}, two_candidate={self.two_candidate}, "
+                f"flipped={self.flipped} ({frac:.2%} of two-candidate), "
                 f"block_scale_flips={self.block_scale_flips}, bad={len(self.bad)})")
 
 
@@ -80,7 +106,9 @@ def expected_intermediate(res, mode, gpu, dn_inscale=None, report=None):
         gv, lv, hv = F.bf16_to_f64(g), F.bf16_to_f64(lo), F.bf16_to_f64(hi)
         ok = (gv >= lv) & (gv <= hv)
         nom = res.hq[0]
+        rep.two_candidate += int(np.sum(lo != hi))
         rep.flipped += int(np.sum(g != nom))
+        rep.row_flips = np.any(g != nom, axis=1)
         for r, c in zip(*np.nonzero(~ok)):
             rep.bad.append((int(r), int(c), f"bf16 {gv[r, c]} outside [{lv[r, c]}, {hv[r, c]}]"))
         return gv
@@ -105,7 +133,18 @@ def expected_intermediate(res, mode, gpu, dn_inscale=None, report=None):
         ok = ((mg >= mlo) & (mg <= mhi) & sign_ok) | zero_block
         val = F.e4m3_decode(codes_g) * s_g[..., None]
         nom_c, nom_s = res.hq
-        rep.flipped += int(np.sum(codes_g.reshape(n, I) != nom_c))
+        # the fp32 block scale is a continuous value (validated by its window
+        # above; it differs from the oracle's in the last bits whenever the fp32
+        # block amax does), so the choice that counts is each code under the
+        # GPU's own scale: the oracle's rounding of its fp32 h by that scale
+        with np.errstate(divide="ignore", invalid="ignore"):
+            nom_g = F.e4m3_quantize(F.f32(res.h32.astype(np.float64).reshape(n, I // 16, 16) / d))
+        nom_g = np.where((s_g > 0)[..., None], nom_g, 0).astype(np.uint8)
+        rep.two_candidate += int(np.sum(mlo != mhi))
+        fl = (codes_g != nom_g).reshape(n, I)
+        rep.flipped += int(np.sum(fl))
+        rep.block_scale_flips += int(np.sum(s_g != nom_s.astype(np.float64)))
+        rep.row_flips = np.any(fl, axis=1)
     else:
         g_in = np.float64(np.float32(dn_inscale))
         codes_g = F.unpack_nibbles(np.asarray(gpu[0], np.uint8)).reshape(n, I // 16, 16)
@@ -129,7 +168,12 @@ def expected_intermediate(res, mode, gpu, dn_inscale=None, report=None):
         zero_block = ~(d > 0) & (codes_g == 0)
         ok = ((mg >= mlo) & (mg <= mhi) & sign_ok) | zero_block
         val = F.e2m1_decode(codes_g) * F.e4m3_decode(s_g)[..., None] * g_in
-        rep.flipped += int(np.sum(F.unpack_nibbles(np.asarray(gpu[0], np.uint8)) != F.unpack_nibbles(nom_c)))
+        scale_amb = np.repeat((c_lo != c_hi)[..., None], 16, axis=2)
+        rep.two_candidate += int(np.sum((mlo != mhi) | scale_amb))
+        fl = (F.unpack_nibbles(np.asarray(gpu[0], np.uint8)) != F.unpack_nibbles(nom_c)) | \
+            np.repeat(s_g != nom_s, 16, axis=1)
+        rep.flipped += int(np.sum(fl))
+        rep.row_flips = np.any(fl, axis=1)
     for r, b, i in zip(*np.nonzero(~ok)):
         rep.bad.append((int(r), int(b * 16 + i), "code outside the candidate range"))
     return val.reshape(n, I)
