@@ -259,6 +259,32 @@ moe_status moe_layer_forward_stage(const moe_nvfp4_experts* w, moe_act_mode mode
                                    const uint16_t* residual, uint16_t* out, void* ws,
                                    size_t ws_bytes, hipStream_t s);
 
+/* ------------------------------------------------------------------ no allocation
+ * moe_layer_forward_noalloc: moe_layer_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same layer, the same kernels and
+ * results, bit for bit, but the workspace is a device array inside the
+ * library (MOE_NOALLOC_SCRATCH_BYTES per GPU, held from the first call on a GPU
+ * until the process ends) instead of a caller's buffer.  The caller still
+ * passes the inputs and the output.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine).
+ *  - Calls whose moe_layer_workspace_bytes exceeds MOE_NOALLOC_SCRATCH_BYTES
+ *    return MOE_E_WORKSPACE (16 MiB holds, for example, every call of up to 64
+ *    tokens at E = 512, k = 10, H = 3072, I = 512).
+ *  - Every call on one GPU shares that GPU's array, which keeps the last call's
+ *    contents: calls that overlap on one GPU (on different streams or threads)
+ *    race and must not be made.
+ *  - The array is zero-filled (a fill kernel on stream s) at the first call on
+ *    each GPU, and again when reset is non-zero.  A fused decode call whose
+ *    waits gave up (see moe_layer_wait_timeouts_offset) leaves bf16 NaN in out
+ *    and makes every later call on the GPU give up too until a call with
+ *    reset != 0.
+ *  - Arguments and errors as moe_layer_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+moe_status moe_layer_forward_noalloc(const moe_nvfp4_experts* w, moe_act_mode mode, const uint16_t* x,
+                                     const uint16_t* w_router, const float* router_bias, int T, int k,
+                                     const uint16_t* residual, uint16_t* out, int reset, hipStream_t s);
+
 /* ------------------------------------------------------------------ test only
  * moe_debug_nvfp4_matmul: the expert kernels' product core without the
  * routing, the SwiGLU or the intermediate's rounding, for pinning it.  For one

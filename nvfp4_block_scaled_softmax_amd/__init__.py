@@ -30,7 +30,8 @@ EXPORTS = ("moe_last_error", "moe_route_workspace_bytes", "moe_route_topk",
            "moe_combine",
            "moe_layer_workspace_bytes", "moe_layer_workspace_layout", "moe_layer_wait_timeouts_offset",
            "moe_layer_forward", "moe_layer_forward_stage", "moe_layer_is_fused", "moe_layer_launches",
-           "moe_layer_status", "moe_debug_nvfp4_matmul_workspace_bytes", "moe_debug_nvfp4_matmul")
+           "moe_layer_status", "moe_debug_nvfp4_matmul_workspace_bytes", "moe_debug_nvfp4_matmul",
+           "moe_layer_forward_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -80,6 +81,7 @@ def lib():
             "moe_layer_forward_stage": ([ctypes.POINTER(_Experts), _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _Z, _P], _I),
             "moe_layer_forward": ([ctypes.POINTER(_Experts), _I, _P, _P, _P, _I, _I, _P, _P, _P, _Z, _P], _I),
             "moe_layer_status": ([_P, _P], _I),
+            "moe_layer_forward_noalloc": ([ctypes.POINTER(_Experts), _I, _P, _P, _P, _I, _I, _P, _P, _I, _P], _I),
             "moe_debug_nvfp4_matmul_workspace_bytes": ([_I, _I], _Z),
             "moe_debug_nvfp4_matmul": ([_I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _I, _P, _P, _Z, _P], _I),
         }
@@ -359,6 +361,33 @@ def moe_layer_forward(experts: Experts, mode, x, w_router, k, bias=None, residua
                                                         _ptr(bias), T, k, _ptr(residual), _ptr(out),
                                                         _ptr(ws), ws.numel(), _stream()))
     return out, ws
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def moe_layer_forward_noalloc(experts: Experts, mode, x, w_router, k, bias=None, residual=None, out=None,
+                              reset=False):
+    """moe_layer_forward on the library's own device scratch (no workspace argument;
+    the C call allocates nothing).  Calls on one GPU must not overlap.  Returns out."""
+    x = _bf16(x, "x")
+    _need(x, "x")
+    T, H = x.shape
+    s = experts.struct()
+    w_router = _bf16(w_router, "w_router")
+    _need(w_router, "w_router", shape=(experts.E, H))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (experts.E,))
+    if residual is not None:
+        residual = _bf16(residual, "residual")
+        _need(residual, "residual", shape=(T, H))
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", shape=(T, H))
+    _check("moe_layer_forward_noalloc",
+           lib().moe_layer_forward_noalloc(ctypes.byref(s), _mode(mode), _ptr(x), _ptr(w_router), _ptr(bias), T, k,
+                                           _ptr(residual), _ptr(out), 1 if reset else 0, _stream()))
+    return out
 
 
 def moe_layer_forward_stage(experts: Experts, mode, stage, x, w_router, k, bias, residual, ws, out):

@@ -1,5 +1,6 @@
 // The whole routed-expert layer on one stream (route -> permute -> experts ->
 // combine), its workspace layout, and the thread-local error text.
+#include <mutex>
 #include <string>
 
 #include "abi_common.hpp"
@@ -169,4 +170,80 @@ extern "C" moe_status moe_layer_status(const void* ws, hipStream_t s) {
               "the outputs of the calls since it was zero-filled are unreliable (NaN where seen)",
               v);
   return MOE_OK;
+}
+
+// ------------------------------------------------------------------ no allocation
+// moe_layer_forward_noalloc: moe_layer_forward with the library's own device
+// scratch array as the workspace, for callers that cannot allocate.  Each GPU
+// holds its own copy of `scratch` (a file-scope device array of kScratchBytes)
+// until the process ends.  In host code the array's name is only a stand-in for
+// the symbol: its device address on the current GPU comes from
+// hipGetSymbolAddress, taken once per device on that device's first call and
+// kept; kernels and fills get that address, never the name.
+
+namespace moe {
+
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Zero-fill of n16 16-byte words: a kernel, not hipMemsetAsync, so that a call
+// recorded into a graph replays it correctly.
+__global__ void __launch_bounds__(256) k_zero16(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+static moe_status zero_fill(void* p, size_t bytes, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero16, dim3(1024), dim3(256), 0, s, static_cast<uint4*>(p), bytes / 16);
+  return check_launch("moe_layer_forward_noalloc (scratch fill)");
+}
+
+// This device's scratch address, zero-filled on stream s at the device's first
+// call (the address is kept only once its fill is enqueued) or when asked to.
+static moe_status scratch_for_device(void** ptr, bool reset, hipStream_t s) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  MOE_REQUIRE(e == hipSuccess, MOE_E_HIP, "moe_layer_forward_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  MOE_REQUIRE(dev >= 0 && dev < kMaxDevices, MOE_E_UNSUPPORTED, "moe_layer_forward_noalloc: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  void* p = g_scratch_ptr[dev];
+  const bool first = p == nullptr;
+  if (first) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    MOE_REQUIRE(e == hipSuccess && p != nullptr, MOE_E_HIP,
+                "moe_layer_forward_noalloc: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+  }
+  if (first || reset) {   // the state block at its start must be zero before a fused call uses it
+    moe_status st = zero_fill(p, kScratchBytes, s);
+    if (st != MOE_OK) return st;
+  }
+  g_scratch_ptr[dev] = p;
+  *ptr = p;
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" moe_status moe_layer_forward_noalloc(const moe_nvfp4_experts* w, moe_act_mode mode,
+                                                const uint16_t* x, const uint16_t* w_router,
+                                                const float* router_bias, int T, int k,
+                                                const uint16_t* residual, uint16_t* out, int reset,
+                                                hipStream_t s) {
+  const char* name = "moe_layer_forward_noalloc";
+  moe::clear_error();
+  moe_status st = moe::check_experts(name, w, mode);
+  if (st != MOE_OK) return st;
+  const size_t need = moe_layer_workspace_bytes(mode, T, k, w->E, w->H, w->I);
+  MOE_REQUIRE(need > 0, MOE_E_SHAPE, "%s: bad shape T=%d k=%d", name, T, k);
+  MOE_REQUIRE(need <= moe::kScratchBytes, MOE_E_WORKSPACE,
+              "%s: the call needs a %zu-byte workspace, above the %zu-byte device scratch; "
+              "use moe_layer_forward with a workspace",
+              name, need, moe::kScratchBytes);
+  void* ws = nullptr;
+  if ((st = moe::scratch_for_device(&ws, reset != 0, s)) != MOE_OK) return st;
+  return layer_call(name, w, mode, 3, x, w_router, router_bias, T, k, residual, out, ws, moe::kScratchBytes, s);
 }
