@@ -22,6 +22,16 @@ renormalised over the k chosen; SwiGLU experts h = silu(gate) * up with
 silu(z) = z / (1 + exp(-z)); the output is the routing-weighted sum of the
 chosen experts' down projections, rounded once to bf16.
 
+Shared expert and its gate (page "Qwen3.8-Flash-Next NVIDIA NVFP4 for
+Infernix (bit-exact)", section "What is bit-exact and what is quantized": the
+shared experts and the gates are among the BF16 dense projections, stored
+BF16).  The pages print no formula; the Qwen-style reading taken here: one
+SwiGLU expert that every token runs, with BF16 gate/up [2Is, H] and down
+[H, Is] matrices, bf16 activations and a bf16 intermediate (the dense
+projections' activation precision), scaled per token by sigmoid(x . g) with g
+the BF16 gate vector [H], and added to the routed experts' weighted sum before
+the output's single rounding to bf16.
+
 Precision of the intermediate h (read from the activation modes, which
 describe "activations" at every expert matmul input): 16-bit mode rounds h to
 bf16, 8-bit mode quantizes it to E4M3 per 16, 4-bit mode to NVFP4 per 16 under
@@ -200,6 +210,58 @@ def expert_ffn(ex: Expert, x_bf16, mode):
                      np.abs(a_gate) @ np.abs(wg).T, np.abs(a_up) @ np.abs(wu).T)
 
 
+# ----------------------------------------------------------------------------- shared expert
+@dataclasses.dataclass
+class SharedExpert:
+    """The shared expert in bf16 bits: gu [2Is, H] (gate rows, then up rows),
+    dn [H, Is], gate [H] (the vector of its sigmoid gate)."""
+    gu: np.ndarray
+    dn: np.ndarray
+    gate: np.ndarray
+
+    @property
+    def Is(self):
+        return self.gu.shape[0] // 2
+
+
+@dataclasses.dataclass
+class SharedResult:
+    g: np.ndarray         # double [T, Is]
+    u: np.ndarray
+    h: np.ndarray         # double silu(g) * u
+    h32: np.ndarray       # fp32 [T, Is]
+    hq: tuple             # (bf16 bits [T, Is],): the intermediate as stored
+    hdq: np.ndarray       # double value of the stored intermediate
+    y: np.ndarray         # double [T, H]: down projection, before the gate
+    logit: np.ndarray     # double [T]: x . gate
+    sig: np.ndarray       # double [T]: sigmoid(logit)
+    gated: np.ndarray     # double [T, H]: sig * y, the term added to the output
+    gate_abs: np.ndarray  # double [T, Is]: sum_K |x_K * Wg[i, K]|
+    up_abs: np.ndarray
+
+
+def shared_expert(sh: SharedExpert, x_bf16):
+    """The shared expert on rows x [T, H] (bf16 bits), in double precision:
+    g = x Wg^T, u = x Wu^T, h = silu(g) u, stored as bf16 of its fp32 value,
+    y = h Wd^T, gated by sigmoid(x . gate)."""
+    x = bf16_to_f64(x_bf16)
+    Is = sh.Is
+    wg = bf16_to_f64(sh.gu[:Is])
+    wu = bf16_to_f64(sh.gu[Is:])
+    wd = bf16_to_f64(sh.dn)
+    g = x @ wg.T
+    u = x @ wu.T
+    h = u * (g / (1.0 + np.exp(-g)))
+    h32 = f32(h)
+    hb = f64_to_bf16(h32)
+    hdq = bf16_to_f64(hb)
+    y = hdq @ wd.T
+    logit = x @ bf16_to_f64(sh.gate)
+    sig = 1.0 / (1.0 + np.exp(-logit))
+    return SharedResult(g, u, h, h32, (hb,), hdq, y, logit, sig, sig[:, None] * y,
+                        np.abs(x) @ np.abs(wg).T, np.abs(x) @ np.abs(wu).T)
+
+
 # ----------------------------------------------------------------------------- combine
 def combine(y_sorted, pair_row, w):
     """out[t] = bf16( sum_j w[t, j] * y[pair_row[t*k + j]] ), j ascending, in double.
@@ -228,12 +290,15 @@ class LayerResult:
     y_sorted: np.ndarray  # double [T*k, H]
     out_f64: np.ndarray   # double [T, H] before the bf16 rounding
     out: np.ndarray       # bf16 bits [T, H]
+    shared: SharedResult | None = None
 
 
-def moe_layer(x_bf16, wr_bf16, k, get_expert, mode, bias=None):
+def moe_layer(x_bf16, wr_bf16, k, get_expert, mode, bias=None, shared=None):
     """The whole routed-expert layer for tokens x [T, H] (bf16 bits).
 
     get_expert(e) returns the Expert e (only the chosen experts are requested).
+    With a SharedExpert, its gated output is added to the routed experts'
+    weighted sum before the output's rounding to bf16.
     """
     x_bf16 = np.asarray(x_bf16, np.uint16)
     T, H = x_bf16.shape
@@ -249,7 +314,12 @@ def moe_layer(x_bf16, wr_bf16, k, get_expert, mode, bias=None):
         ffn[int(e)] = res
         y_sorted[rows] = res.y
     acc, out = combine(y_sorted, perm.pair_row, r.w)
-    return LayerResult(r, perm, ffn, y_sorted, acc, out)
+    sres = None
+    if shared is not None:
+        sres = shared_expert(shared, x_bf16)
+        acc = acc + sres.gated
+        out = f64_to_bf16(acc)
+    return LayerResult(r, perm, ffn, y_sorted, acc, out, sres)
 
 
 # ----------------------------------------------------------------------------- calibration

@@ -33,10 +33,12 @@ TAG_ROUTER = 2
 TAG_EXPERT = 3
 TAG_CALIB = 4
 TAG_ZIPF = 5
+TAG_SHARED = 6
 
 MAT_GATE = 0
 MAT_UP = 1
 MAT_DOWN = 2
+MAT_SHARED_GATE_VEC = 3
 
 SIGMA_X = 1.0
 SIGMA_W = 0.02
@@ -57,6 +59,7 @@ class Workload:
     layers: int = 1
     zipf_s: float | None = None
     zipf_beta: float = 0.25
+    Is: int = 0          # shared expert intermediate size (0: no shared expert)
 
     @property
     def seed(self) -> int:
@@ -79,6 +82,13 @@ CONFIGS = (
     Workload(4, "prefill chunk W4A4 Zipf-skewed", E=512, k=10, H=3072, I=512, T=1024,
              modes=("A4",), zipf_s=1.1),
 )
+
+
+def with_shared_expert(w: Workload, Is: int = 512) -> Workload:
+    """The same workload with a BF16 shared expert of intermediate size Is beside the
+    routed experts (its weights have their own stream tag, so every other input is
+    unchanged)."""
+    return dataclasses.replace(w, Is=Is, name=f"{w.name} + shared expert Is={Is}")
 
 
 # --------------------------------------------------------------------------- CPU generator
@@ -173,6 +183,17 @@ def expert_matrix(w: Workload, layer: int, expert: int, matrix: int, rows=None):
     n = (rows.stop - rows.start) * K
     return normal_f32(n, w.seed, TAG_EXPERT, layer=layer, expert=expert, matrix=matrix,
                       sigma=SIGMA_W, i0=i0).reshape(-1, K)
+
+
+def shared_expert_weights(w: Workload, layer: int = 0):
+    """The shared expert's bf16 weights (bits): gate/up [2Is, H] (gate rows first),
+    down [H, Is] and its gate vector [H], all ~N(0, 0.02)."""
+    H, Is = w.H, w.Is
+    g = normal_bf16(Is * H, w.seed, TAG_SHARED, layer=layer, matrix=MAT_GATE, sigma=SIGMA_W)
+    u = normal_bf16(Is * H, w.seed, TAG_SHARED, layer=layer, matrix=MAT_UP, sigma=SIGMA_W)
+    d = normal_bf16(H * Is, w.seed, TAG_SHARED, layer=layer, matrix=MAT_DOWN, sigma=SIGMA_W)
+    v = normal_bf16(H, w.seed, TAG_SHARED, layer=layer, matrix=MAT_SHARED_GATE_VEC, sigma=SIGMA_W)
+    return np.concatenate([g, u]).reshape(2 * Is, H), d.reshape(H, Is), v
 
 
 def zipf_bias(w: Workload):

@@ -212,6 +212,69 @@ def test_tiny_layer_against_torch_pipeline(mode):
     assert np.array_equal(res.out, F.f64_to_bf16(out.numpy()))
 
 
+# --------------------------------------------------------------------------- shared expert
+def test_shared_expert_equals_routed_expert_at_16_bits():
+    """A shared expert whose bf16 matrices hold exactly the dequantized weights of an
+    NVFP4 expert (E2M1 values times powers of two: bf16-exact) computes, before its
+    gate, exactly what that routed expert computes in the 16-bit mode (a pinned
+    function): same gate/up order, SwiGLU, bf16 intermediate and down orientation."""
+    rng = np.random.default_rng(41)
+    H, I, T = 64, 32, 5
+    ex, dg, du, dd = _pow2_expert(rng, H, I)
+    sh = L.SharedExpert(_bf16(np.concatenate([dg, du])), _bf16(dd), _bf16(np.zeros(H)))
+    assert np.array_equal(F.bf16_to_f64(sh.gu), np.concatenate([dg, du]))   # exact in bf16
+    x = _bf16(rng.standard_normal((T, H)))
+    r = L.shared_expert(sh, x)
+    e = L.expert_ffn(ex, x, "A16")
+    assert np.array_equal(r.hq[0], e.hq[0])
+    assert np.array_equal(r.y, e.y)
+    assert np.all(r.sig == 0.5) and np.array_equal(r.gated, 0.5 * r.y)   # sigmoid(0)
+
+
+def test_shared_expert_against_torch():
+    """Random bf16 weights through an independent torch float64 pipeline: silu(g) * u,
+    rounded to fp32 then bf16, the down projection, times torch.sigmoid of x . gate."""
+    rng = np.random.default_rng(42)
+    H, Is, T = 96, 48, 7
+    sh = L.SharedExpert(_bf16(rng.standard_normal((2 * Is, H)) * 0.1), _bf16(rng.standard_normal((H, Is)) * 0.1),
+                        _bf16(rng.standard_normal(H) * 0.2))
+    x = _bf16(rng.standard_normal((T, H)))
+    r = L.shared_expert(sh, x)
+    xt = torch.from_numpy(F.bf16_to_f64(x))
+    w = torch.from_numpy(F.bf16_to_f64(sh.gu))
+    g, u = xt @ w[:Is].T, xt @ w[Is:].T
+    h = torch.nn.functional.silu(g) * u
+    hb = h.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+    y = hb @ torch.from_numpy(F.bf16_to_f64(sh.dn)).T
+    sg = torch.sigmoid(xt @ torch.from_numpy(F.bf16_to_f64(sh.gate)))
+    assert torch.allclose(torch.from_numpy(r.h), h, rtol=1e-12, atol=1e-300)
+    assert np.array_equal(F.bf16_to_f64(r.hq[0]), hb.numpy())
+    assert torch.allclose(torch.from_numpy(r.gated), sg[:, None] * y, rtol=1e-12, atol=1e-300)
+    # the gate: sigmoid(-z) = 1 - sigmoid(z), and a large logit saturates at 1
+    r2 = L.shared_expert(L.SharedExpert(sh.gu, sh.dn, sh.gate ^ np.uint16(0x8000)), x)
+    assert np.allclose(r.sig + r2.sig, 1.0, rtol=0, atol=1e-15)
+    big = L.shared_expert(L.SharedExpert(sh.gu, sh.dn, _bf16(np.full(H, 64.0))), _bf16(np.ones((1, H))))
+    assert big.sig[0] == 1.0
+
+
+def test_layer_with_shared_expert_rounds_once():
+    """The gated shared term joins the routed experts' weighted sum before the single
+    bf16 rounding of the output."""
+    w = synth.CONFIGS[0]
+    x = synth.tokens(w, T=3)
+    wr = synth.router_weight(w)
+    experts = [L.pack_expert(*(synth.expert_matrix(w, 0, e, m) for m in range(3))) for e in range(w.E)]
+    ws = synth.with_shared_expert(w, 64)
+    sh = L.SharedExpert(*synth.shared_expert_weights(ws))
+    assert sh.gu.shape == (128, w.H) and sh.dn.shape == (w.H, 64) and sh.gate.shape == (w.H,)
+    base = L.moe_layer(x, wr, w.k, lambda e: experts[e], "A16")
+    res = L.moe_layer(x, wr, w.k, lambda e: experts[e], "A16", shared=sh)
+    gated = L.shared_expert(sh, x).gated
+    assert np.array_equal(res.out_f64, base.out_f64 + gated)
+    assert np.array_equal(res.out, F.f64_to_bf16(base.out_f64 + gated))
+    assert not np.array_equal(res.out, L.residual_add(base.out, F.f64_to_bf16(gated)))   # not two roundings
+
+
 # --------------------------------------------------------------------------- calibration
 def test_calibration_scales():
     rng = np.random.default_rng(27)
