@@ -83,6 +83,23 @@ typedef struct {
   int32_t E, H, I;
 } moe_nvfp4_experts;
 
+/* The shared expert of a layer and its gate, BF16 (page "Qwen3.8-Flash-Next
+ * NVIDIA NVFP4 for Infernix (bit-exact)", section "What is bit-exact and what
+ * is quantized": the shared experts and the gates are BF16 dense
+ * projections).  Read as a Qwen-style MoE block: one SwiGLU expert that every
+ * token runs, whose output is scaled by sigmoid(x . gate) and added to the
+ * routed experts' weighted sum.  Host struct of device pointers (16-byte
+ * aligned); Is a multiple of 32 up to 1024, H the layer's.
+ *   gu   [2Is][H] bf16  gate rows 0..Is-1, then up rows Is..2Is-1
+ *   dn   [H][Is]  bf16
+ *   gate [H]      bf16  the gate vector (one output) */
+typedef struct {
+  const uint16_t* gu;
+  const uint16_t* dn;
+  const uint16_t* gate;
+  int32_t H, Is;
+} moe_shared_expert;
+
 /* Text of the last error on the calling thread; valid until the next call on it. */
 const char* moe_last_error(void);
 
@@ -192,6 +209,22 @@ moe_status nvfp4_expert_ffn_stage(const moe_nvfp4_experts* w, moe_act_mode mode,
  * the result is the next layer's input bf16(x + bf16(sum)). */
 moe_status moe_combine(const float* y_pairs, const int32_t* pair_row, const float* topk_w, int T,
                        int k, int H, const uint16_t* residual, uint16_t* out, hipStream_t s);
+
+/* ------------------------------------------------------------------ shared expert
+ * moe_shared_expert_forward: y[t] = sigmoid(x_t . gate) * (h_t . Wd^T) with
+ * h_t = bf16(silu(x_t . Wg^T) * (x_t . Wu^T)), fp32 sums of bf16 products, the
+ * intermediate rounded once to bf16 (the dense projections' activation
+ * precision).  x [T][H] bf16; y [T][H] fp32 (out);
+ * ws: moe_shared_expert_workspace_bytes(T, Is) bytes (the intermediate), 16-byte aligned.
+ * moe_combine_shared: moe_combine with the shared expert's y (fp32 [T][H], not
+ * NULL) added after the routed sum and before the rounding:
+ *   out[t] = bf16( sum_j topk_w[t][j] * y_pairs[pair_row[t*k + j]] + shared_y[t] ). */
+size_t moe_shared_expert_workspace_bytes(int T, int Is);
+moe_status moe_shared_expert_forward(const moe_shared_expert* sw, const uint16_t* x, int T, float* y, void* ws,
+                                     size_t ws_bytes, hipStream_t s);
+moe_status moe_combine_shared(const float* y_pairs, const int32_t* pair_row, const float* topk_w, int T, int k,
+                              int H, const float* shared_y, const uint16_t* residual, uint16_t* out,
+                              hipStream_t s);
 
 /* ------------------------------------------------------------------ whole layer
  * moe_layer_forward: route -> permute -> experts -> combine on one stream.
@@ -310,6 +343,21 @@ moe_status moe_debug_nvfp4_matmul(int core, moe_act_mode mode, const uint8_t* co
                                   const float* wscale, int N, int K, const void* x, const void* x_scales,
                                   const float* inscale, int cols, float* out, void* ws, size_t ws_bytes,
                                   hipStream_t s);
+
+/* moe_block_forward: moe_layer_forward plus the shared expert (sw, not NULL):
+ *   out = bf16( routed weighted sum + sigmoid(x . gate) * shared expert(x) ),
+ * or with a residual bf16(residual + out), on one stream (the shared expert's
+ * two kernels first, then the layer's).  ws: moe_block_workspace_bytes(mode,
+ * T, k, E, H, I, Is) bytes, 256-byte aligned, zero-filled before its first use
+ * as for moe_layer_forward; moe_block_workspace_layout fills offsets[9]: the
+ * seven of moe_layer_workspace_layout, then the shared expert's intermediate
+ * (bf16 [T][Is]) and its gated output (fp32 [T][H]). */
+size_t moe_block_workspace_bytes(moe_act_mode mode, int T, int k, int E, int H, int I, int Is);
+moe_status moe_block_workspace_layout(moe_act_mode mode, int T, int k, int E, int H, int I, int Is,
+                                      size_t offsets[9]);
+moe_status moe_block_forward(const moe_nvfp4_experts* w, const moe_shared_expert* sw, moe_act_mode mode,
+                             const uint16_t* x, const uint16_t* w_router, const float* router_bias, int T, int k,
+                             const uint16_t* residual, uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s);
 
 #ifdef __cplusplus
 }

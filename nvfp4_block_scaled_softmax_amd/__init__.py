@@ -31,7 +31,9 @@ EXPORTS = ("moe_last_error", "moe_route_workspace_bytes", "moe_route_topk",
            "moe_layer_workspace_bytes", "moe_layer_workspace_layout", "moe_layer_wait_timeouts_offset",
            "moe_layer_forward", "moe_layer_forward_stage", "moe_layer_is_fused", "moe_layer_launches",
            "moe_layer_status", "moe_debug_nvfp4_matmul_workspace_bytes", "moe_debug_nvfp4_matmul",
-           "moe_layer_forward_noalloc")
+           "moe_layer_forward_noalloc",
+           "moe_shared_expert_workspace_bytes", "moe_shared_expert_forward", "moe_combine_shared",
+           "moe_block_workspace_bytes", "moe_block_workspace_layout", "moe_block_forward")
 
 
 class MoeError(RuntimeError):
@@ -46,6 +48,11 @@ class _Experts(ctypes.Structure):
                 ("gu_wscale", ctypes.c_void_p), ("dn_wscale", ctypes.c_void_p),
                 ("gu_inscale", ctypes.c_void_p), ("dn_inscale", ctypes.c_void_p),
                 ("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32)]
+
+
+class _Shared(ctypes.Structure):
+    _fields_ = [("gu", ctypes.c_void_p), ("dn", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+                ("H", ctypes.c_int32), ("Is", ctypes.c_int32)]
 
 
 _lib = None
@@ -81,6 +88,13 @@ def lib():
             "moe_layer_forward_stage": ([ctypes.POINTER(_Experts), _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _Z, _P], _I),
             "moe_layer_forward": ([ctypes.POINTER(_Experts), _I, _P, _P, _P, _I, _I, _P, _P, _P, _Z, _P], _I),
             "moe_layer_status": ([_P, _P], _I),
+            "moe_shared_expert_workspace_bytes": ([_I, _I], _Z),
+            "moe_shared_expert_forward": ([ctypes.POINTER(_Shared), _P, _I, _P, _P, _Z, _P], _I),
+            "moe_combine_shared": ([_P, _P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
+            "moe_block_workspace_bytes": ([_I, _I, _I, _I, _I, _I, _I], _Z),
+            "moe_block_workspace_layout": ([_I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_Z)], _I),
+            "moe_block_forward": ([ctypes.POINTER(_Experts), ctypes.POINTER(_Shared), _I, _P, _P, _P, _I, _I, _P,
+                                   _P, _P, _Z, _P], _I),
             "moe_layer_forward_noalloc": ([ctypes.POINTER(_Experts), _I, _P, _P, _P, _I, _I, _P, _P, _I, _P], _I),
             "moe_debug_nvfp4_matmul_workspace_bytes": ([_I, _I], _Z),
             "moe_debug_nvfp4_matmul": ([_I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _I, _P, _P, _Z, _P], _I),
@@ -178,6 +192,33 @@ class Experts:
                       None if self.gu_inscale is None else self.gu_inscale.data_ptr(),
                       None if self.dn_inscale is None else self.dn_inscale.data_ptr(),
                       E, H, I)
+        self.__dict__["_cstruct"] = st
+        return st
+
+
+@dataclasses.dataclass
+class SharedExpert:
+    """A layer's BF16 shared expert on the GPU (see moe_shared_expert in the C header)."""
+    gu: torch.Tensor      # bf16 [2Is, H]: gate rows, then up rows
+    dn: torch.Tensor      # bf16 [H, Is]
+    gate: torch.Tensor    # bf16 [H]
+
+    @property
+    def H(self):
+        return self.dn.shape[0]
+
+    @property
+    def Is(self):
+        return self.dn.shape[1]
+
+    def struct(self):
+        cached = self.__dict__.get("_cstruct")
+        if cached is not None:
+            return cached
+        H, Is = self.H, self.Is
+        for name, t, shape in (("gu", self.gu, (2 * Is, H)), ("dn", self.dn, (H, Is)), ("gate", self.gate, (H,))):
+            _need(_bf16(t, name), name, shape=shape)
+        st = _Shared(self.gu.data_ptr(), self.dn.data_ptr(), self.gate.data_ptr(), H, Is)
         self.__dict__["_cstruct"] = st
         return st
 
@@ -321,6 +362,83 @@ def moe_combine(y_pairs, pair_row, topk_w, residual=None, out=None):
     _check("moe_combine", lib().moe_combine(_ptr(y_pairs), _ptr(pair_row), _ptr(topk_w), T, k, H,
                                             _ptr(residual), _ptr(out), _stream()))
     return out
+
+
+def moe_shared_expert_forward(shared: SharedExpert, x, ws=None, y=None):
+    """The shared expert's gated output, fp32 [T, H].  Returns (y, workspace); the
+    workspace holds its bf16 intermediate [T, Is]."""
+    x = _bf16(x, "x")
+    _need(x, "x")
+    T, H = x.shape
+    st = shared.struct()
+    n = lib().moe_shared_expert_workspace_bytes(T, shared.Is)
+    if ws is None:
+        ws = torch.empty(max(n, 16), dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty(T, H, dtype=torch.float32, device=x.device)
+    _check("moe_shared_expert_forward",
+           lib().moe_shared_expert_forward(ctypes.byref(st), _ptr(x), T, _ptr(y), _ptr(ws), ws.numel(), _stream()))
+    return y, ws
+
+
+def moe_combine_shared(y_pairs, pair_row, topk_w, shared_y, residual=None, out=None):
+    """moe_combine with the shared expert's gated output added before the rounding."""
+    _need(y_pairs, "y_pairs", torch.float32)
+    _need(topk_w, "topk_w", torch.float32)
+    T, k = topk_w.shape
+    H = y_pairs.shape[1]
+    _need(pair_row, "pair_row", torch.int32, (T * k,))
+    _need(shared_y, "shared_y", torch.float32, (T, H))
+    if residual is not None:
+        residual = _bf16(residual, "residual")
+        _need(residual, "residual")
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=y_pairs.device)
+    _check("moe_combine_shared", lib().moe_combine_shared(_ptr(y_pairs), _ptr(pair_row), _ptr(topk_w), T, k, H,
+                                                          _ptr(shared_y), _ptr(residual), _ptr(out), _stream()))
+    return out
+
+
+def block_workspace_bytes(mode, T, k, E, H, I, Is):
+    return lib().moe_block_workspace_bytes(_mode(mode), T, k, E, H, I, Is)
+
+
+def block_workspace_views(ws, mode, T, k, E, H, I, Is):
+    """workspace_views of a block workspace plus the shared expert's intermediate and output."""
+    offs = (ctypes.c_size_t * 9)()
+    _check("moe_block_workspace_layout", lib().moe_block_workspace_layout(_mode(mode), T, k, E, H, I, Is, offs))
+    v = workspace_views(ws, mode, T, k, E, H, I)
+    v["shared_h"] = ws[offs[7]:offs[7] + T * Is * 2].view(torch.bfloat16).view(T, Is)
+    v["shared_y"] = ws[offs[8]:offs[8] + T * H * 4].view(torch.float32).view(T, H)
+    return v
+
+
+def moe_block_forward(experts: Experts, shared: SharedExpert, mode, x, w_router, k, bias=None, residual=None,
+                      ws=None, out=None):
+    """The layer with its shared expert.  Returns (out bf16 [T, H], workspace); a
+    workspace passed in must have been zero-filled before its first use."""
+    x = _bf16(x, "x")
+    _need(x, "x")
+    T, H = x.shape
+    s = experts.struct()
+    sh = shared.struct()
+    m = _mode(mode)
+    w_router = _bf16(w_router, "w_router")
+    _need(w_router, "w_router", shape=(experts.E, H))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (experts.E,))
+    if residual is not None:
+        residual = _bf16(residual, "residual")
+        _need(residual, "residual", shape=(T, H))
+    nws = block_workspace_bytes(m, T, k, experts.E, H, experts.I, shared.Is)
+    if ws is None:
+        ws = torch.zeros(max(nws, 16), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    _check("moe_block_forward", lib().moe_block_forward(ctypes.byref(s), ctypes.byref(sh), m, _ptr(x),
+                                                        _ptr(w_router), _ptr(bias), T, k, _ptr(residual), _ptr(out),
+                                                        _ptr(ws), ws.numel(), _stream()))
+    return out, ws
 
 
 def layer_workspace_bytes(mode, T, k, E, H, I):

@@ -56,8 +56,14 @@ moe_status launch_expert_ffn(const moe_nvfp4_experts& w, moe_act_mode mode, cons
                              float* y_pairs, void* ws, int stage_mask, hipStream_t s,
                              const int32_t* pair_row = nullptr, const int32_t* ids = nullptr);
 moe_status launch_combine(const float* y_pairs, const int32_t* pair_row, const float* topk_w,
-                          int T, int k, int H, const uint16_t* residual, uint16_t* out,
-                          hipStream_t s);
+                          int T, int k, int H, const float* shared_y, const uint16_t* residual,
+                          uint16_t* out, hipStream_t s);
+// The shared expert (shared.hip): validation, workspace (its bf16 intermediate
+// [T][Is]) and the two kernels writing the gated output y [T][H] fp32.
+moe_status check_shared(const char* name, const moe_shared_expert* sw, int H);
+size_t shared_workspace(int T, int Is);
+moe_status launch_shared_expert(const moe_shared_expert& sw, const uint16_t* x, int T, void* h_ws, float* y,
+                                hipStream_t s);
 size_t expert_ffn_workspace(moe_act_mode mode, int T, int k, int H, int I);
 // The fused decode layer (T <= 8): routing in one launch, experts + combine in
 // another; its counter block must start at zero and is left at zero.
@@ -71,6 +77,6 @@ moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, in
                                int T, int k, const uint16_t* residual, uint16_t* out,
                                int32_t* ids, float* tw, int32_t* offsets, int32_t* sorted,
                                int32_t* prow, float* y, float* logits, void* ffn_ws, void* state,
-                               hipStream_t s);
+                               const float* shared_y, hipStream_t s);
 
 }  // namespace moe

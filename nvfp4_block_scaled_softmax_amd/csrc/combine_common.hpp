@@ -48,17 +48,31 @@ __device__ __forceinline__ uint2 combine_round4(float4 acc, bool has_residual, u
   return make_uint2(o0 | (o1 << 16), o2 | (o3 << 16));
 }
 
+// The shared expert's gated output (fp32 [T][H], nullable) joins the routed
+// sum after its last term, before the rounding.
+__device__ __forceinline__ void add_shared4(float4& acc, const float* __restrict__ shared_y, int t, int H, int c) {
+  if (shared_y) {
+    const float4 sv = *reinterpret_cast<const float4*>(shared_y + (size_t)t * H + (size_t)c * 4);
+    acc.x += sv.x;
+    acc.y += sv.y;
+    acc.z += sv.z;
+    acc.w += sv.w;
+  }
+}
+
 // out values of token t, hidden 4c .. 4c+3, from y_pairs in global memory.
 template <bool COH = false>
 __device__ __forceinline__ uint2 combine4(const float* __restrict__ y,
                                           const int32_t* __restrict__ pair_row,
                                           const float* __restrict__ w, int t, int k, int H, int c,
-                                          const uint16_t* __restrict__ residual) {
-  const float4 acc = combine_acc4<COH>(
+                                          const uint16_t* __restrict__ residual,
+                                          const float* __restrict__ shared_y = nullptr) {
+  float4 acc = combine_acc4<COH>(
       [&](int r) {
         return __builtin_bit_cast(float4, hld128<COH>(y, 4 * ((size_t)r * H) + 16 * (size_t)c));
       },
       pair_row, w, t, k);
+  add_shared4(acc, shared_y, t, H, c);
   const uint2 rr = residual ? *reinterpret_cast<const uint2*>(residual + (size_t)t * H + (size_t)c * 4)
                             : make_uint2(0u, 0u);
   return combine_round4(acc, residual != nullptr, rr);

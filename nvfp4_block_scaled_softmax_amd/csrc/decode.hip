@@ -281,7 +281,7 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
                                              const float* __restrict__ tw,
                                              const uint16_t* __restrict__ residual,
                                              uint16_t* __restrict__ out, uint8_t* lds,
-                                             PlanOf&& plan_of) {
+                                             const float* __restrict__ shared_y, PlanOf&& plan_of) {
   __shared__ int s_flag;
   __shared__ int s_prow[kDecMaxSlots];            // the combine's pair rows, weights and residual,
   __shared__ float s_tw[kDecMaxSlots];            // loaded while the tile waits for gate/up
@@ -375,6 +375,7 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
             if (j0 + u < a.k)
               acc = __builtin_fmaf(s_tw[t * a.k + j0 + u], __builtin_bit_cast(float, (uint32_t)(v[u] >> 32)), acc);
         }
+        if (shared_y) acc += shared_y[(size_t)t * a.H + o];   // as add_shared4, one element
         uint32_t ob = f32_to_bf16(acc);   // as combine_round4, one element
         if (residual) ob = f32_to_bf16(bf16_to_f32(s_res[t][ol]) + bf16_to_f32(ob));
         out[(size_t)t * a.H + o] = aborted != 0u ? kBf16NaN : (uint16_t)ob;
@@ -401,11 +402,12 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
       for (int i = tid; i < a.T * n4; i += kTileThreads) {
         const int t = i / n4, c = c0 + i % n4;
         if (4 * c < a.H) {
-          const float4 acc = combine_acc4(
+          float4 acc = combine_acc4(
               [&](int r) {
                 return __builtin_bit_cast(float4, hld128<true>(a.y, 4 * ((size_t)r * a.H) + 16 * (size_t)c));
               },
               s_prow, s_tw, t, a.k);
+          add_shared4(acc, shared_y, t, a.H, c);
           const uint2 rr = *reinterpret_cast<const uint2*>(&s_res[t][4 * (c - c0)]);
           *reinterpret_cast<uint2*>(out + (size_t)t * a.H + (size_t)c * 4) =
               combine_round4(acc, residual != nullptr, rr);
@@ -422,11 +424,11 @@ __global__ void __launch_bounds__(kTileThreads)
     k_experts_decode(FfnArgs a, DecodeState* __restrict__ st, int max_slots, int cols_gu,
                      int cols_dn, const int32_t* __restrict__ pair_row,
                      const float* __restrict__ tw, const uint16_t* __restrict__ residual,
-                     uint16_t* __restrict__ out) {
+                     uint16_t* __restrict__ out, const float* __restrict__ shared_y) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int n_active = st->n_active;
   expert_tiles<MODE, GL, GC, DL, DC>(
-      a, st, blockIdx.x, 0u, max_slots, cols_gu, cols_dn, pair_row, tw, residual, out, lds,
+      a, st, blockIdx.x, 0u, max_slots, cols_gu, cols_dn, pair_row, tw, residual, out, lds, shared_y,
       [&](int slot, int) {
         if (slot >= n_active) return SlotPlan{-1, 0, 0, 0, -1, 0u};
         const int4 pl = st->plan[slot];
@@ -464,7 +466,8 @@ __global__ void __launch_bounds__(kTileThreads)
                    int32_t* __restrict__ ids, float* __restrict__ tw, FfnArgs a,
                    DecodeState* __restrict__ st, int max_slots, int cols_gu, int cols_dn,
                    int32_t* __restrict__ pair_row, const uint16_t* __restrict__ residual,
-                   uint16_t* __restrict__ out, uint32_t epoch_arg, uint32_t dn_hold) {
+                   uint16_t* __restrict__ out, uint32_t epoch_arg, uint32_t dn_hold,
+                   const float* __restrict__ shared_y) {
   extern __shared__ __align__(16) uint8_t lds[];
   // epoch_arg 0: the epoch is in the workspace, advanced by k_epoch_bump just
   // before this kernel (complete at the kernel boundary, the same for every
@@ -548,7 +551,7 @@ __global__ void __launch_bounds__(kTileThreads)
     return;
   }
   expert_tiles<MODE, GL, GC, DL, DC>(
-      a, st, wg - R, dn_hold, max_slots, cols_gu, cols_dn, pair_row, tw, residual, out, lds,
+      a, st, wg - R, dn_hold, max_slots, cols_gu, cols_dn, pair_row, tw, residual, out, lds, shared_y,
       [&](int slot, int role) {
         if (tid == 0) {
           const uint64_t* e = &st->pub[role][slot];
@@ -647,43 +650,44 @@ int decode_launches(moe_act_mode mode, int T, int k, int H, int I) {
 template <int MODE, int GC, int DL>
 static void launch_b3(const FfnArgs& a, DecodeState* st, int max_slots, int cols_gu, int cols_dn,
                       const int32_t* prow, const float* tw, const uint16_t* residual,
-                      uint16_t* out, hipStream_t s) {
+                      uint16_t* out, const float* shared_y, hipStream_t s) {
   const int grid = max_slots * (a.I / kGuRows + (a.H + kDnRows - 1) / kDnRows);
   const size_t lds_gu = (size_t)cols_gu * (a.H / 32) * ChunkLds<MODE>::kStride;
   const size_t lds_dn = (size_t)cols_dn * (a.I / 32) * ChunkLds<MODE>::kStride;
   hipLaunchKernelGGL((k_experts_decode<MODE, 32, GC, DL, 1>), dim3(grid), dim3(kTileThreads),
                      lds_gu > lds_dn ? lds_gu : lds_dn, s, a, st, max_slots, cols_gu, cols_dn, prow,
-                     tw, residual, out);
+                     tw, residual, out, shared_y);
 }
 
 template <int MODE, int GC>
 static void launch_b2(const FfnArgs& a, int dl, DecodeState* st, int max_slots, int cols_gu,
                       int cols_dn, const int32_t* prow, const float* tw, const uint16_t* residual,
-                      uint16_t* out, hipStream_t s) {
-  if (dl == 8) launch_b3<MODE, GC, 8>(a, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, s);
-  else if (dl == 16) launch_b3<MODE, GC, 16>(a, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, s);
-  else launch_b3<MODE, GC, 32>(a, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, s);
+                      uint16_t* out, const float* shy, hipStream_t s) {
+  if (dl == 8) launch_b3<MODE, GC, 8>(a, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, shy, s);
+  else if (dl == 16) launch_b3<MODE, GC, 16>(a, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, shy, s);
+  else launch_b3<MODE, GC, 32>(a, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, shy, s);
 }
 
 template <int MODE>
 static void launch_b(const FfnArgs& a, DecodeState* st, int max_slots, const int32_t* prow,
-                     const float* tw, const uint16_t* residual, uint16_t* out, hipStream_t s) {
+                     const float* tw, const uint16_t* residual, uint16_t* out, const float* shy,
+                     hipStream_t s) {
   // column groups as the per-stage kernels size them
   const int per_col_gu = (a.H / 32) * ChunkLds<MODE>::kStride;
   const int per_col_dn = (a.I / 32) * ChunkLds<MODE>::kStride;
   const int cols_gu = max(1, min(min(8, a.T), kLdsBudget / per_col_gu));
   const int cols_dn = max(1, min(min(8, a.T), kLdsBudget / per_col_dn));
   const int gc = gu_config(a.H / 32), dl = dn_config(a.I / 32);
-  if (gc == 2) launch_b2<MODE, 2>(a, dl, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, s);
-  else if (gc == 3) launch_b2<MODE, 3>(a, dl, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, s);
-  else launch_b2<MODE, 4>(a, dl, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, s);
+  if (gc == 2) launch_b2<MODE, 2>(a, dl, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, shy, s);
+  else if (gc == 3) launch_b2<MODE, 3>(a, dl, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, shy, s);
+  else launch_b2<MODE, 4>(a, dl, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, shy, s);
 }
 
 // ---- the single-launch layer (16-bit activations, up to kSmallP pairs)
 template <int S, int GC, int DL>
 static void launch_one3(const FfnArgs& a, const uint16_t* x, const uint16_t* wr, const float* bias,
                         float* logits, int32_t* ids, float* tw, int32_t* prow, DecodeState* st,
-                        const uint16_t* residual, uint16_t* out, uint64_t epoch, hipStream_t s) {
+                        const uint16_t* residual, uint16_t* out, uint64_t epoch, const float* shy, hipStream_t s) {
   const int P = a.T * a.k, max_slots = P < a.E ? P : a.E;
   const int cols = max(1, min(min(8, a.T), kLdsBudget / ((a.H / 32) * ChunkLds<MOE_A16>::kStride)));
   const int cols_dn = max(1, min(min(8, a.T), kLdsBudget / ((a.I / 32) * ChunkLds<MOE_A16>::kStride)));
@@ -696,27 +700,27 @@ static void launch_one3(const FfnArgs& a, const uint16_t* x, const uint16_t* wr,
   const uint32_t dn_hold = cap > 0 && grid <= cap ? kDnHoldTicksPerExpert : 0u;
   hipLaunchKernelGGL((k_layer_decode<S, MOE_A16, 32, GC, DL, 1>), dim3(grid), dim3(kTileThreads), lds, s,
                      x, wr, bias, logits, ids, tw, a, st, max_slots, cols, cols_dn, prow, residual, out,
-                     (uint32_t)epoch, dn_hold);
+                     (uint32_t)epoch, dn_hold, shy);
 }
 
 template <int S, int GC>
 static void launch_one2(int dl, const FfnArgs& a, const uint16_t* x, const uint16_t* wr,
                         const float* bias, float* logits, int32_t* ids, float* tw, int32_t* prow,
                         DecodeState* st, const uint16_t* residual, uint16_t* out, uint64_t epoch,
-                        hipStream_t s) {
-  if (dl == 8) launch_one3<S, GC, 8>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
-  else if (dl == 16) launch_one3<S, GC, 16>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
-  else launch_one3<S, GC, 32>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
+                        const float* shy, hipStream_t s) {
+  if (dl == 8) launch_one3<S, GC, 8>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, s);
+  else if (dl == 16) launch_one3<S, GC, 16>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, s);
+  else launch_one3<S, GC, 32>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, s);
 }
 
 template <int S>
 static void launch_one(const FfnArgs& a, const uint16_t* x, const uint16_t* wr, const float* bias,
                        float* logits, int32_t* ids, float* tw, int32_t* prow, DecodeState* st,
-                       const uint16_t* residual, uint16_t* out, uint64_t epoch, hipStream_t s) {
+                       const uint16_t* residual, uint16_t* out, uint64_t epoch, const float* shy, hipStream_t s) {
   const int gc = gu_config(a.H / 32), dl = dn_config(a.I / 32);
-  if (gc == 2) launch_one2<S, 2>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
-  else if (gc == 3) launch_one2<S, 3>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
-  else launch_one2<S, 4>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
+  if (gc == 2) launch_one2<S, 2>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, s);
+  else if (gc == 3) launch_one2<S, 3>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, s);
+  else launch_one2<S, 4>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, s);
 }
 
 // Epochs of eager single-launch calls: 31 bits, not reused within 2^31 calls
@@ -729,7 +733,7 @@ moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, in
                                int T, int k, const uint16_t* residual, uint16_t* out,
                                int32_t* ids, float* tw, int32_t* offsets, int32_t* sorted,
                                int32_t* prow, float* y, float* logits, void* ffn_ws, void* state,
-                               hipStream_t s) {
+                               const float* shared_y, hipStream_t s) {
   DecodeState* st = static_cast<DecodeState*>(state);
   const int E = w.E, H = w.H;
   moe_status r;
@@ -748,11 +752,11 @@ moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, in
         moe_status rb = check_launch("moe_layer_forward (epoch)");
         if (rb != MOE_OK) return rb;
       }
-      if (E <= 64) launch_one<1>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
-      else if (E <= 128) launch_one<2>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
-      else if (E <= 256) launch_one<4>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
-      else if (E <= 512) launch_one<8>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
-      else launch_one<16>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, s);
+      if (E <= 64) launch_one<1>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shared_y, s);
+      else if (E <= 128) launch_one<2>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shared_y, s);
+      else if (E <= 256) launch_one<4>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shared_y, s);
+      else if (E <= 512) launch_one<8>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shared_y, s);
+      else launch_one<16>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shared_y, s);
       return check_launch("moe_layer_forward (decode layer)");
     }
   }
@@ -773,9 +777,9 @@ moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, in
     const FfnArgs a = make_ffn_args(w, mode, x, T, k, offsets, sorted, y, ffn_ws);
     const int P = T * k, max_slots = P < E ? P : E;
     switch (mode) {
-      case MOE_A16: launch_b<MOE_A16>(a, st, max_slots, prow, tw, residual, out, s); break;
-      case MOE_A8: launch_b<MOE_A8>(a, st, max_slots, prow, tw, residual, out, s); break;
-      default: launch_b<MOE_A4>(a, st, max_slots, prow, tw, residual, out, s); break;
+      case MOE_A16: launch_b<MOE_A16>(a, st, max_slots, prow, tw, residual, out, shared_y, s); break;
+      case MOE_A8: launch_b<MOE_A8>(a, st, max_slots, prow, tw, residual, out, shared_y, s); break;
+      default: launch_b<MOE_A4>(a, st, max_slots, prow, tw, residual, out, shared_y, s); break;
     }
     return check_launch("moe_layer_forward (decode experts)");
   }

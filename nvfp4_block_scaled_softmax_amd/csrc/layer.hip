@@ -23,10 +23,13 @@ void clear_error() { g_error.clear(); }
 moe_status check_experts(const char* name, const moe_nvfp4_experts* w, moe_act_mode mode);
 
 struct LayerLayout {
-  size_t ids, w, offsets, sorted, pair_row, y, ffn, route, state, total;
+  size_t ids, w, offsets, sorted, pair_row, y, ffn, route, state, sh_h, sh_y, total;
 };
 
-static bool layer_layout(moe_act_mode mode, int T, int k, int E, int H, int I, LayerLayout& L) {
+// Is > 0: a shared expert of that intermediate size; its segments (bf16 h
+// [T][Is], gated fp32 y [T][H]) come last, so every other offset is the same
+// with or without it.
+static bool layer_layout(moe_act_mode mode, int T, int k, int E, int H, int I, LayerLayout& L, int Is = 0) {
   if (T < 1 || k < 1 || k > kMaxTopK || E < 1 || E > kMaxExperts || k > E || !dim_ok(H) || !dim_ok(I) ||
       (int64_t)T * k > (1 << 24))
     return false;
@@ -47,6 +50,11 @@ static bool layer_layout(moe_act_mode mode, int T, int k, int E, int H, int I, L
   // router logits, dead after top-k; then the permutation's block counts
   const size_t route = (size_t)T * E * 4, perm = permute_workspace((int)P, E);
   L.route = seg(route > perm ? route : perm);
+  L.sh_h = L.sh_y = 0;
+  if (Is > 0) {
+    L.sh_h = seg(shared_workspace(T, Is));
+    L.sh_y = seg((size_t)T * H * 4);
+  }
   L.total = o;
   return true;
 }
@@ -90,13 +98,15 @@ extern "C" moe_status moe_layer_workspace_layout(moe_act_mode mode, int T, int k
 static moe_status layer_call(const char* name, const moe_nvfp4_experts* w, moe_act_mode mode,
                              int stage_mask, const uint16_t* x, const uint16_t* w_router,
                              const float* router_bias, int T, int k, const uint16_t* residual,
-                             uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s) {
+                             uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s,
+                             const moe_shared_expert* sw = nullptr) {
   moe::clear_error();
   moe_status st = moe::check_experts(name, w, mode);
   if (st != MOE_OK) return st;
   MOE_REQUIRE(x && w_router && out && ws, MOE_E_ARG, "%s: null pointer argument", name);
+  if (sw && (st = moe::check_shared(name, sw, w->H)) != MOE_OK) return st;
   moe::LayerLayout L;
-  MOE_REQUIRE(moe::layer_layout(mode, T, k, w->E, w->H, w->I, L), MOE_E_SHAPE,
+  MOE_REQUIRE(moe::layer_layout(mode, T, k, w->E, w->H, w->I, L, sw ? sw->Is : 0), MOE_E_SHAPE,
               "%s: bad shape T=%d k=%d", name, T, k);
   MOE_REQUIRE(out != x, MOE_E_ARG, "%s: out must not alias x", name);
   MOE_REQUIRE(moe::aligned(x, 16) && moe::aligned(w_router, 16) && moe::aligned(out, 16) &&
@@ -112,10 +122,15 @@ static moe_status layer_call(const char* name, const moe_nvfp4_experts* w, moe_a
   int32_t* sorted = reinterpret_cast<int32_t*>(b + L.sorted);
   int32_t* prow = reinterpret_cast<int32_t*>(b + L.pair_row);
   float* y = reinterpret_cast<float*>(b + L.y);
+  // the shared expert needs no routing: its kernels go first, with the routing half
+  float* shy = sw ? reinterpret_cast<float*>(b + L.sh_y) : nullptr;
+  if (sw && (stage_mask & 1) &&
+      (st = moe::launch_shared_expert(*sw, x, T, b + L.sh_h, shy, s)) != MOE_OK)
+    return st;
   if (moe::decode_fusable(T, w->H, w->I))
     return moe::launch_layer_decode(*w, mode, stage_mask, x, w_router, router_bias, T, k,
                                     residual, out, ids, tw, offs, sorted, prow, y,
-                                    reinterpret_cast<float*>(b + L.route), b + L.ffn, b + L.state, s);
+                                    reinterpret_cast<float*>(b + L.route), b + L.ffn, b + L.state, shy, s);
   if (stage_mask & 1) {
     if ((st = moe::launch_route(x, w_router, router_bias, T, w->H, w->E, k, ids, tw,
                                 reinterpret_cast<float*>(b + L.route), s)) != MOE_OK)
@@ -128,7 +143,7 @@ static moe_status layer_call(const char* name, const moe_nvfp4_experts* w, moe_a
   if (stage_mask & 2) {
     if ((st = moe::launch_expert_ffn(*w, mode, x, T, k, offs, sorted, y, b + L.ffn, 6, s)) != MOE_OK)
       return st;
-    return moe::launch_combine(y, prow, tw, T, k, w->H, residual, out, s);
+    return moe::launch_combine(y, prow, tw, T, k, w->H, shy, residual, out, s);
   }
   return MOE_OK;
 }
@@ -170,6 +185,38 @@ extern "C" moe_status moe_layer_status(const void* ws, hipStream_t s) {
               "the outputs of the calls since it was zero-filled are unreliable (NaN where seen)",
               v);
   return MOE_OK;
+}
+
+// ------------------------------------------------------------------ with the shared expert
+extern "C" size_t moe_block_workspace_bytes(moe_act_mode mode, int T, int k, int E, int H, int I, int Is) {
+  moe::LayerLayout L;
+  if (Is < 32 || Is > 1024 || Is % 32 != 0) return 0;
+  return moe::layer_layout(mode, T, k, E, H, I, L, Is) ? L.total : 0;
+}
+
+extern "C" moe_status moe_block_workspace_layout(moe_act_mode mode, int T, int k, int E, int H, int I, int Is,
+                                                 size_t offsets[9]) {
+  moe::clear_error();
+  MOE_REQUIRE(offsets, MOE_E_ARG, "moe_block_workspace_layout: null offsets");
+  moe::LayerLayout L;
+  MOE_REQUIRE(Is >= 32 && Is <= 1024 && Is % 32 == 0 && moe::layer_layout(mode, T, k, E, H, I, L, Is), MOE_E_SHAPE,
+              "moe_block_workspace_layout: bad shape or mode");
+  const size_t v[9] = {L.ids, L.w, L.offsets, L.sorted, L.pair_row, L.y, L.ffn, L.sh_h, L.sh_y};
+  for (int i = 0; i < 9; ++i) offsets[i] = v[i];
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_block_forward(const moe_nvfp4_experts* w, const moe_shared_expert* sw,
+                                        moe_act_mode mode, const uint16_t* x, const uint16_t* w_router,
+                                        const float* router_bias, int T, int k, const uint16_t* residual,
+                                        uint16_t* out, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!sw) {
+    moe::clear_error();
+    moe::set_error("moe_block_forward: null shared expert (use moe_layer_forward)");
+    return MOE_E_ARG;
+  }
+  return layer_call("moe_block_forward", w, mode, 3, x, w_router, router_bias, T, k, residual, out, ws, ws_bytes,
+                    s, sw);
 }
 
 // ------------------------------------------------------------------ no allocation

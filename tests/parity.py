@@ -155,17 +155,37 @@ def _rel_l2(got, acc):
     return np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
 
 
+def check_shared(sh, x_u16, h_gpu, y_gpu, report=None):
+    """The shared expert's stored bf16 intermediate (tests/ties.py rules, as the
+    16-bit mode's) and its gated output y (relative L2 per token <= Y_TOL against
+    the oracle continued from the GPU's validated intermediate).  Returns (that
+    expected gated y [T, H], the oracle's SharedResult, info)."""
+    rep = report if report is not None else ties.TieReport()
+    res = OL.shared_expert(sh, x_u16)
+    hdq = ties.expected_intermediate(res, "A16", h_gpu, None, rep)
+    rep.check()
+    y = res.sig[:, None] * (hdq @ F.bf16_to_f64(sh.dn).T)
+    err = np.linalg.norm(y_gpu - y, axis=1) / np.maximum(np.linalg.norm(y, axis=1), 1e-30)
+    assert err.max() <= Y_TOL, f"shared expert y rel err {err.max():.3g}"
+    return y, res, {"shared_y_worst_rel": float(err.max()), "shared_ties": repr(rep),
+                    "shared_flipped_rows": rep.row_flips}
+
+
 def check_output(out_gpu_u16, y_exp, pair_row, route_oracle, ids_gpu, k, tokens=None, mode=None, y_nom=None,
-                 row_flipped=None, oracle_ids=None):
+                 row_flipped=None, oracle_ids=None, shared_exp=None, shared_nom=None):
     """Per token rel-L2 of the bf16 output against bf16(oracle double result): the
     oracle continued from the GPU's validated intermediate (y_exp), and, where the
     GPU made no other valid choice (same routing; in the 4-bit mode also no flipped
-    intermediate code), the oracle's own nominal result (y_nom)."""
+    intermediate code), the oracle's own nominal result (y_nom).  With a shared
+    expert, its gated output (shared_exp: continued from the GPU's intermediate;
+    shared_nom: the oracle's own) joins the sum before the rounding."""
     T = out_gpu_u16.shape[0]
     toks = range(T) if tokens is None else tokens
     worst, inf_worst, within_ulp, nom_worst, nom_n = 0.0, 0.0, [], 0.0, 0
     for t in toks:
         acc = _weighted(y_exp, route_oracle, ids_gpu, pair_row, t, k)
+        if shared_exp is not None:
+            acc = acc + shared_exp[t]
         got = F.bf16_to_f64(out_gpu_u16[t])
         rel = _rel_l2(got, acc)
         worst = max(worst, rel)
@@ -178,7 +198,10 @@ def check_output(out_gpu_u16, y_exp, pair_row, route_oracle, ids_gpu, k, tokens=
         same_route = oracle_ids is None or np.array_equal(ids_gpu[t], oracle_ids[t])
         rows = pair_row[t * k:(t + 1) * k]
         if same_route and (mode != "A4" or not np.any(row_flipped[rows])):
-            rel_n = _rel_l2(got, _weighted(y_nom, route_oracle, ids_gpu, pair_row, t, k))
+            acc_n = _weighted(y_nom, route_oracle, ids_gpu, pair_row, t, k)
+            if shared_nom is not None:
+                acc_n = acc_n + shared_nom[t]
+            rel_n = _rel_l2(got, acc_n)
             nom_worst = max(nom_worst, rel_n)
             nom_n += 1
             assert rel_n <= OUT_TOL, f"token {t}: rel L2 {rel_n:.3g} against the oracle's nominal result"

@@ -74,10 +74,11 @@ def check_packed_bytes(ex_gpu, cache, experts):
         assert host(ex_gpu.dn_wscale[e]).view(np.uint32) == np.float32(o.dn_wscale).view(np.uint32), e
 
 
-def check_call(w, mode, layer, x, out, ws, sample=None, ex=None, cache=None):
+def check_call(w, mode, layer, x, out, ws, sample=None, ex=None, cache=None, shared=None):
     """Full parity of one GPU layer call on tokens x (bf16 bits) against the oracle.
     ex: the GPU experts (default: the cached layer); cache: an oracle ExpertCache
-    to reuse (default: a new one)."""
+    to reuse (default: a new one); shared: the oracle's SharedExpert of a block call
+    (its intermediate and output are read from the block workspace)."""
     T = x.shape[0]
     wr = synth.router_weight(w, layer)
     bias_np = synth.zipf_bias(w)
@@ -99,8 +100,21 @@ def check_call(w, mode, layer, x, out, ws, sample=None, ex=None, cache=None):
     y_exp, info = parity.check_experts(w, mode, x, cache, w.k, v["expert_offsets"], v["sorted_pairs"],
                                        v["y_pairs"], fv, tokens=None if sample is None else toks, report=rep)
     y_nom, rflip = info.pop("y_nominal"), info.pop("row_flipped")
+    sh_exp = sh_nom = None
+    if shared is not None:
+        bv = moe.block_workspace_views(ws, mode, T, w.k, w.E, w.H, w.I, shared.Is)
+        sh_exp, sres, sinfo = parity.check_shared(shared, x, host(bv["shared_h"]), host(bv["shared_y"]))
+        sh_nom = sres.gated
+        # a token whose shared intermediate took another valid bf16 code has no
+        # unique nominal result at the 4-bit mode's output (16/8-bit: ~1e-4 effect)
+        rflip = rflip.copy()
+        flipped_tokens = np.nonzero(sinfo.pop("shared_flipped_rows"))[0]
+        for t in flipped_tokens:
+            rflip[v["pair_row"][t * w.k:(t + 1) * w.k]] = True
+        info.update(sinfo)
     info.update(parity.check_output(host(out), y_exp, v["pair_row"], r, v["topk_ids"], w.k, tokens=toks,
-                                    mode=mode, y_nom=y_nom, row_flipped=rflip, oracle_ids=r.ids))
+                                    mode=mode, y_nom=y_nom, row_flipped=rflip, oracle_ids=r.ids,
+                                    shared_exp=sh_exp, shared_nom=sh_nom))
     info["router_flips"] = len(flipped)
     info["experts_touched"] = int(len(np.unique(v["topk_ids"])))
     say("ok", info)
