@@ -6,6 +6,11 @@
   (bias 7), 3 mantissa bits; exponent field 0 is subnormal (m/8 * 2^-6); the
   all-ones pattern S.1111.111 is NaN; there is no infinity; largest finite 448.
 * bf16: the upper 16 bits of an IEEE fp32.
+* fp16: IEEE binary16 (the scales and the 16-bit activations of the
+  q4_g64_fp16 encoding); rounding to it is IEEE round-to-nearest-even with
+  overflow to infinity (numpy's float16 conversion, pinned in the tests).
+* int4: a 4-bit two's complement integer in a nibble (codes 0..7 are 0..7,
+  codes 8..15 are -8..-1).
 
 Rounding to these formats is round-to-nearest with ties to the even code (the
 code whose lowest bit is 0, i.e. the even mantissa) and saturation at the
@@ -115,6 +120,23 @@ def e4m3_quantize(v):
     idx = _nearest_index(np.where(nan, 0.0, np.abs(v)), E4M3_FINITE)
     code = idx | (np.signbit(v).astype(np.int64) << 7)
     return np.where(nan, 0, code).astype(np.uint8)
+
+
+def f64_to_f16(x):
+    """fp16 bit patterns (uint16) of values, rounded to nearest even (from double)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, np.float64).astype(np.float16).view(np.uint16)
+
+
+def f16_to_f64(bits):
+    """Value of fp16 bit patterns (uint16) as double (exact)."""
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def int4_decode(codes):
+    """Value of 4-bit two's complement codes (0..15) as integers -8..7."""
+    c = np.asarray(codes).astype(np.int64) & 15
+    return np.where(c >= 8, c - 16, c)
 
 
 def pack_nibbles(codes):

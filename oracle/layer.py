@@ -44,11 +44,11 @@ import dataclasses
 
 import numpy as np
 
-from .formats import bf16_to_f64, f32, f64_to_bf16
+from .formats import bf16_to_f64, f16_to_f64, f32, f64_to_bf16, f64_to_f16
 from .quant import (fp8_block_dequantize, fp8_block_quantize, nvfp4_dequantize,
-                    nvfp4_global_scale, nvfp4_quantize)
+                    nvfp4_global_scale, nvfp4_quantize, q4g64_dequantize, q4g64_quantize)
 
-MODES = ("A16", "A8", "A4")
+MODES = ("A16", "A8", "A4", "F16")
 
 
 # ----------------------------------------------------------------------------- experts
@@ -88,6 +88,47 @@ class Expert:
 
     def down(self):
         return nvfp4_dequantize(self.dn_codes, self.dn_scales, self.dn_wscale)
+
+
+@dataclasses.dataclass
+class Q4Expert:
+    """One expert in the q4_g64_fp16 encoding (page "Qwen3.8-Flash-Next NVIDIA
+    NVFP4 for Infernix (bit-exact)", section "Drafting only": the drafter's routed
+    experts): the canonical layout of Expert with int4 codes and fp16 scales, one
+    per 64 values along K: gu_scales [2I, H/64], dn_scales [H, I/64] (fp16 bits);
+    no per-matrix multiplier.  It runs in the "F16" mode (16-bit float
+    activations: the encoding's fp16 domain)."""
+    gu_codes: np.ndarray
+    gu_scales: np.ndarray
+    dn_codes: np.ndarray
+    dn_scales: np.ndarray
+    gu_inscale = None
+    dn_inscale = None
+
+    @property
+    def I(self):
+        return self.gu_codes.shape[0] // 2
+
+    @property
+    def H(self):
+        return self.dn_codes.shape[0]
+
+    def gate(self):
+        return q4g64_dequantize(self.gu_codes[:self.I], self.gu_scales[:self.I])
+
+    def up(self):
+        return q4g64_dequantize(self.gu_codes[self.I:], self.gu_scales[self.I:])
+
+    def down(self):
+        return q4g64_dequantize(self.dn_codes, self.dn_scales)
+
+
+def pack_expert_q4(w_gate, w_up, w_down):
+    """q4_g64_fp16-pack one expert's fp32 gate [I, H], up [I, H], down [H, I]."""
+    cg, sg = q4g64_quantize(w_gate)
+    cu, su = q4g64_quantize(w_up)
+    cd, sd = q4g64_quantize(w_down)
+    return Q4Expert(np.concatenate([cg, cu]), np.concatenate([sg, su]), cd, sd)
 
 
 def pack_matrix(w):
@@ -174,10 +215,14 @@ class FfnResult:
 
 
 def quantize_activation(x32, mode, inscale=None):
-    """Activation as an expert matrix sees it, per mode; returns (stored form, double value)."""
+    """Activation as an expert matrix sees it, per mode; returns (stored form, double value).
+    "F16" (the q4_g64_fp16 experts): IEEE fp16, rounded to nearest even."""
     if mode == "A16":
         b = f64_to_bf16(x32)
         return (b,), bf16_to_f64(b)
+    if mode == "F16":
+        b = f64_to_f16(np.asarray(x32, np.float32).astype(np.float64))
+        return (b,), f16_to_f64(b)
     if mode == "A8":
         c, s = fp8_block_quantize(x32)
         return (c, s), fp8_block_dequantize(c, s)
@@ -192,6 +237,8 @@ def expert_ffn(ex: Expert, x_bf16, mode):
     x32 = bf16_to_f64(x_bf16).astype(np.float32)
     if mode == "A16":
         a_gate = a_up = x32.astype(np.float64)
+    elif mode == "F16":
+        a_gate = a_up = quantize_activation(x32, "F16")[1]
     elif mode == "A8":
         a_gate = a_up = quantize_activation(x32, "A8")[1]
     elif mode == "A4":

@@ -33,7 +33,8 @@ from __future__ import annotations
 import numpy as np
 
 from .formats import (E2M1_MAX, E4M3_MAX, e2m1_decode, e2m1_quantize, e4m3_decode,
-                      e4m3_quantize, f32, pack_nibbles, unpack_nibbles)
+                      e4m3_quantize, f16_to_f64, f32, f64_to_f16, int4_decode, pack_nibbles,
+                      unpack_nibbles)
 
 BLOCK = 16
 NVFP4_AMAX_DIVISOR = E2M1_MAX * E4M3_MAX  # 2688
@@ -104,3 +105,62 @@ def fp8_block_dequantize(codes, scales):
     R, K = c.shape
     v = e4m3_decode(c).reshape(R, K // BLOCK, BLOCK) * np.asarray(scales, np.float64)[..., None]
     return v.reshape(R, K)
+
+
+# ----------------------------------------------------------------------------- q4_g64_fp16
+Q4_GROUP = 64
+# Candidate divisors of the group amax: 7, 7.125, ..., 8 (the codes reach -8 .. 7).
+Q4_DIVISORS = 7.0 + np.arange(9) / 8.0
+
+
+def q4g64_quantize(w):
+    """q4_g64_fp16 packing of fp32 rows w [R, K] (K % 64 == 0).
+
+    Page "Qwen3.8-Flash-Next NVIDIA NVFP4 for Infernix (bit-exact)", section
+    "Drafting only": the drafter's routed experts are 4-bit with one FP16 scale
+    per 64 weights, the scales chosen by mean squared error from the exact
+    weights.  The pages give no candidate set; the reading taken: per group of 64
+    consecutive values along K, with amax = max |v|,
+
+        d_j = fp16( f32(amax / m_j) ),  m_j = 7 + j/8, j = 0..8
+        q_i = clamp( RNE( f32(v_i / d_j) ), -8, 7 )
+        err_j = sum_i (v_i - d_j q_i)^2   in double, i ascending, each op rounded once
+
+    the first j with the smallest err_j (candidates whose d_j is 0 or infinite
+    are skipped; an all-zero group, or one with no candidate, stores d = +0 and
+    q = 0).  Returns (codes [R, K/2] uint8, two's complement nibbles, element 2i
+    in the low nibble; scales [R, K/64] fp16 bit patterns).
+    """
+    v = np.asarray(w, np.float32)
+    R, K = v.shape
+    assert K % Q4_GROUP == 0, K
+    g = v.reshape(R, K // Q4_GROUP, Q4_GROUP).astype(np.float64)
+    amax = np.abs(g).max(axis=2)
+    best_err = np.full(amax.shape, np.inf)
+    best_d = np.zeros(amax.shape, np.uint16)
+    best_q = np.zeros(g.shape, np.int64)
+    for m in Q4_DIVISORS:
+        dbits = f64_to_f16(f32(amax / m).astype(np.float64))
+        d = f16_to_f64(dbits)
+        ok = (d > 0) & np.isfinite(d)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            r = f32(g / np.where(ok, d, 1.0)[..., None]).astype(np.float64)
+        q = np.clip(np.rint(r), -8, 7).astype(np.int64)
+        err = np.zeros(amax.shape)
+        for i in range(Q4_GROUP):                      # index order, one rounding per op
+            e = g[..., i] - d * q[..., i]
+            err = err + e * e
+        better = ok & (err < best_err)
+        best_err = np.where(better, err, best_err)
+        best_d = np.where(better, dbits, best_d)
+        best_q = np.where(better[..., None], q, best_q)
+    codes = (best_q & 15).astype(np.uint8).reshape(R, K)
+    return pack_nibbles(codes), best_d.astype(np.uint16)
+
+
+def q4g64_dequantize(codes, scales):
+    """Exact double value of q4_g64_fp16 rows: int4(code) * fp16 scale of its group of 64."""
+    q = int4_decode(unpack_nibbles(codes)).astype(np.float64)
+    R, K = q.shape
+    d = f16_to_f64(scales)
+    return (q.reshape(R, K // Q4_GROUP, Q4_GROUP) * d[..., None]).reshape(R, K)
