@@ -48,11 +48,12 @@ METRIC = "NVFP4 MoE layer: weight GB/s (% HBM peak), tokens/s at T=1/8/1024"
 
 
 # --------------------------------------------------------------------------- GPU workload
-def build_layer(w, layer, device, mode="A16", gen_buffers=None):
+def build_layer(w, layer, device, mode="A16", gen_buffers=None, fmt="nvfp4"):
     """One seeded layer on the GPU: (Experts, router bf16 [E, H], bias fp32 [E] or None).
 
     Expert weights are drawn on the GPU by the seeded generator (bit-identical
-    to its host build) as fp32 and NVFP4-packed by the library.
+    to its host build) as fp32 and packed by the library: NVFP4, or with
+    fmt="q4" q4_g64_fp16.
     """
     import torch
     import nvfp4_block_scaled_softmax_amd as moe
@@ -73,7 +74,10 @@ def build_layer(w, layer, device, mode="A16", gen_buffers=None):
         g, d = synth.load_input_scales(w)
         gu_in = torch.from_numpy(g).to(device)
         dn_in = torch.from_numpy(d).to(device)
-    ex = moe.pack_experts(gu.view(E, 2 * I, H), dn.view(E, H, I), gu_in, dn_in)
+    if fmt == "q4":
+        ex = moe.pack_experts_q4(gu.view(E, 2 * I, H), dn.view(E, H, I))
+    else:
+        ex = moe.pack_experts(gu.view(E, 2 * I, H), dn.view(E, H, I), gu_in, dn_in)
     router = torch.empty(E, H, dtype=torch.bfloat16, device=device)
     synth.gpu_normal_(router, w.seed, synth.TAG_ROUTER, layer=layer, sigma=synth.SIGMA_W)
     bias = synth.zipf_bias(w)

@@ -59,17 +59,33 @@ typedef enum {
 
 typedef enum { MOE_DT_BF16 = 0, MOE_DT_F32 = 1 } moe_dtype;
 
+/* Encoding of the expert weights. */
+typedef enum {
+  /* NVFP4 (the routed experts of page "Qwen3.8-Flash-Next NVIDIA NVFP4 for
+   * Infernix (bit-exact)", section "What is bit-exact and what is quantized") */
+  MOE_FMT_NVFP4 = 0,
+  /* q4_g64_fp16 (same page, section "Drafting only": the drafter's routed
+   * experts): 4-bit two's complement codes (element 2i in the low nibble of byte
+   * i), one fp16 scale per 64 consecutive values along the reduction dimension,
+   * no per-matrix multiplier.  These experts compute in fp16: they take the
+   * 16-bit mode (MOE_A16) only, with x rounded to fp16 (nearest even) at the
+   * expert input and the intermediate held as fp16. */
+  MOE_FMT_Q4G64 = 2
+} moe_weight_format;
+
 /* One layer's experts, stacked over E, canonical layout.  The struct itself
  * lives in host memory; its pointers are device pointers.  16-byte alignment
  * is required for the code and scale arrays, 4-byte for the fp32 arrays.
  *   gu_codes   [E][2I][H/2]  gate rows 0..I-1, then up rows I..2I-1
- *   gu_scales  [E][2I][H/16] E4M3 block scales
+ *   gu_scales  [E][2I][H/16] E4M3 block scales   (MOE_FMT_Q4G64: fp16 [E][2I][H/64])
  *   dn_codes   [E][H][I/2]
- *   dn_scales  [E][H][I/16]
- *   gu_wscale  [E][2]        fp32 multiplier of the gate and the up matrix
- *   dn_wscale  [E]           fp32 multiplier of the down matrix
+ *   dn_scales  [E][H][I/16]                      (MOE_FMT_Q4G64: fp16 [E][H][I/64])
+ *   gu_wscale  [E][2]        fp32 multiplier of the gate and the up matrix (NVFP4 only)
+ *   dn_wscale  [E]           fp32 multiplier of the down matrix (NVFP4 only)
  *   gu_inscale [E][2]        fp32 activation input scales (MOE_A4 only, else may be NULL)
  *   dn_inscale [E]           fp32 activation input scale of down (MOE_A4 only)
+ *   fmt                      the encoding (a zero-filled struct is NVFP4); MOE_FMT_Q4G64
+ *                            needs H and I multiples of 64
  */
 typedef struct {
   const uint8_t* gu_codes;
@@ -81,6 +97,7 @@ typedef struct {
   const float* gu_inscale;
   const float* dn_inscale;
   int32_t E, H, I;
+  int32_t fmt; /* moe_weight_format */
 } moe_nvfp4_experts;
 
 /* The shared expert of a layer and its gate, BF16 (page "Qwen3.8-Flash-Next
@@ -157,6 +174,18 @@ moe_status act_quant_nvfp4(const void* x, moe_dtype xdt, int rows, int cols, con
  * all-zero codes.  codes [rows][cols]; scales [rows][cols/16] fp32. */
 moe_status act_quant_fp8(const void* x, moe_dtype xdt, int rows, int cols, uint8_t* codes,
                          float* scales, hipStream_t s);
+
+/* q4g64_quantize: q4_g64_fp16 packing of fp32 rows (page "Qwen3.8-Flash-Next
+ * NVIDIA NVFP4 for Infernix (bit-exact)", section "Drafting only": 4-bit, one
+ * FP16 scale per 64, scales chosen by mean squared error from the exact
+ * values).  Per group of 64 values with amax = max |v|: the candidates
+ * d_j = fp16(f32(amax / m_j)), m_j = 7 + j/8 for j = 0..8; codes
+ * q = clamp(RNE(f32(v / d_j)), -8, 7); the first candidate with the least
+ * sum of (v - d_j q)^2 (double, in index order, each op rounded once) is kept;
+ * candidates whose d is 0 or infinite are skipped; a group with none stores
+ * d = 0 and q = 0.  x [rows][cols] fp32 (cols % 64 == 0); codes [rows][cols/2];
+ * scales [rows][cols/64] fp16 bit patterns. */
+moe_status q4g64_quantize(const float* x, int rows, int cols, uint8_t* codes, uint16_t* scales, hipStream_t s);
 
 /* nvfp4_global_scale: per-matrix fp32 multiplier of NVFP4 packing,
  * global[m] = f32(amax(|x_m|) / 2688) (2688 = 6 * 448) for the n_mat
@@ -339,6 +368,12 @@ moe_status moe_layer_forward_noalloc(const moe_nvfp4_experts* w, moe_act_mode mo
  * in any summation order (page "Infernix releases", release 2026.10.11,
  * "Highlights": FP4 products and their row sums stay exact). */
 size_t moe_debug_nvfp4_matmul_workspace_bytes(int core, int cols);
+/* moe_debug_q4g64_matmul: the same for q4_g64_fp16 weights (codes [N][K/2],
+ * fp16 scales [N][K/64]) on the narrow tile, x bf16 [cols][K] rounded to fp16
+ * as the experts take it: out[c][n] = sum_k dec(W[n][k]) * fp16(x[c][k]).
+ * K % 64 == 0, K <= 4096. */
+moe_status moe_debug_q4g64_matmul(const uint8_t* codes, const uint16_t* scales, int N, int K, const uint16_t* x,
+                                  int cols, float* out, hipStream_t s);
 moe_status moe_debug_nvfp4_matmul(int core, moe_act_mode mode, const uint8_t* codes, const uint8_t* scales,
                                   const float* wscale, int N, int K, const void* x, const void* x_scales,
                                   const float* inscale, int cols, float* out, void* ws, size_t ws_bytes,

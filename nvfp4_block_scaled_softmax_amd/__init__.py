@@ -18,8 +18,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_nvfp4.so")
 
 MOE_A16, MOE_A8, MOE_A4 = 0, 1, 2
-MODES = {"A16": MOE_A16, "A8": MOE_A8, "A4": MOE_A4}
+MODES = {"A16": MOE_A16, "A8": MOE_A8, "A4": MOE_A4,
+         "F16": MOE_A16}   # "F16": the 16-bit activations as q4_g64_fp16 experts take them (fp16)
 DT_BF16, DT_F32 = 0, 1
+FMT_NVFP4, FMT_Q4G64 = 0, 2
 STATUS = {0: "MOE_OK", -1: "MOE_E_ARG", -2: "MOE_E_ALIGN", -3: "MOE_E_SHAPE",
           -4: "MOE_E_UNSUPPORTED", -5: "MOE_E_WORKSPACE", -6: "MOE_E_HIP", -7: "MOE_E_STALLED"}
 
@@ -33,7 +35,8 @@ EXPORTS = ("moe_last_error", "moe_route_workspace_bytes", "moe_route_topk",
            "moe_layer_status", "moe_debug_nvfp4_matmul_workspace_bytes", "moe_debug_nvfp4_matmul",
            "moe_layer_forward_noalloc",
            "moe_shared_expert_workspace_bytes", "moe_shared_expert_forward", "moe_combine_shared",
-           "moe_block_workspace_bytes", "moe_block_workspace_layout", "moe_block_forward")
+           "moe_block_workspace_bytes", "moe_block_workspace_layout", "moe_block_forward",
+           "q4g64_quantize", "moe_debug_q4g64_matmul")
 
 
 class MoeError(RuntimeError):
@@ -47,7 +50,8 @@ class _Experts(ctypes.Structure):
                 ("dn_codes", ctypes.c_void_p), ("dn_scales", ctypes.c_void_p),
                 ("gu_wscale", ctypes.c_void_p), ("dn_wscale", ctypes.c_void_p),
                 ("gu_inscale", ctypes.c_void_p), ("dn_inscale", ctypes.c_void_p),
-                ("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32)]
+                ("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("fmt", ctypes.c_int32)]
 
 
 class _Shared(ctypes.Structure):
@@ -88,6 +92,8 @@ def lib():
             "moe_layer_forward_stage": ([ctypes.POINTER(_Experts), _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _Z, _P], _I),
             "moe_layer_forward": ([ctypes.POINTER(_Experts), _I, _P, _P, _P, _I, _I, _P, _P, _P, _Z, _P], _I),
             "moe_layer_status": ([_P, _P], _I),
+            "q4g64_quantize": ([_P, _I, _I, _P, _P, _P], _I),
+            "moe_debug_q4g64_matmul": ([_P, _P, _I, _I, _P, _I, _P, _P], _I),
             "moe_shared_expert_workspace_bytes": ([_I, _I], _Z),
             "moe_shared_expert_forward": ([ctypes.POINTER(_Shared), _P, _I, _P, _P, _Z, _P], _I),
             "moe_combine_shared": ([_P, _P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
@@ -148,15 +154,18 @@ def _mode(mode):
 # --------------------------------------------------------------------------- experts
 @dataclasses.dataclass
 class Experts:
-    """One layer's NVFP4 experts on the GPU, canonical layout (see the C header)."""
+    """One layer's experts on the GPU, canonical layout (see the C header).
+    NVFP4 (fmt FMT_NVFP4) or q4_g64_fp16 (fmt FMT_Q4G64: scales fp16 bits, one
+    per 64, no multipliers)."""
     gu_codes: torch.Tensor     # uint8 [E, 2I, H/2]
-    gu_scales: torch.Tensor    # uint8 [E, 2I, H/16]
+    gu_scales: torch.Tensor    # uint8 [E, 2I, H/16]  (q4: 16-bit [E, 2I, H/64])
     dn_codes: torch.Tensor     # uint8 [E, H, I/2]
-    dn_scales: torch.Tensor    # uint8 [E, H, I/16]
-    gu_wscale: torch.Tensor    # float32 [E, 2]
-    dn_wscale: torch.Tensor    # float32 [E]
+    dn_scales: torch.Tensor    # uint8 [E, H, I/16]   (q4: 16-bit [E, H, I/64])
+    gu_wscale: torch.Tensor | None = None    # float32 [E, 2] (NVFP4)
+    dn_wscale: torch.Tensor | None = None    # float32 [E] (NVFP4)
     gu_inscale: torch.Tensor | None = None   # float32 [E, 2]
     dn_inscale: torch.Tensor | None = None   # float32 [E]
+    fmt: int = 0
 
     @property
     def E(self):
@@ -177,21 +186,27 @@ class Experts:
             return cached
         E, H, I = self.E, self.H, self.I
         _need(self.gu_codes, "gu_codes", torch.uint8, (E, 2 * I, H // 2))
-        _need(self.gu_scales, "gu_scales", torch.uint8, (E, 2 * I, H // 16))
         _need(self.dn_codes, "dn_codes", torch.uint8, (E, H, I // 2))
-        _need(self.dn_scales, "dn_scales", torch.uint8, (E, H, I // 16))
-        _need(self.gu_wscale, "gu_wscale", torch.float32, (E, 2))
-        _need(self.dn_wscale, "dn_wscale", torch.float32, (E,))
+        if self.fmt == FMT_Q4G64:
+            for n, t, shp in (("gu_scales", self.gu_scales, (E, 2 * I, H // 64)),
+                              ("dn_scales", self.dn_scales, (E, H, I // 64))):
+                _need(t, n, shape=shp)
+                if t.element_size() != 2:
+                    raise TypeError(f"{n}: q4_g64_fp16 scales are 16-bit, got {t.dtype}")
+        else:
+            _need(self.gu_scales, "gu_scales", torch.uint8, (E, 2 * I, H // 16))
+            _need(self.dn_scales, "dn_scales", torch.uint8, (E, H, I // 16))
+            _need(self.gu_wscale, "gu_wscale", torch.float32, (E, 2))
+            _need(self.dn_wscale, "dn_wscale", torch.float32, (E,))
         if self.gu_inscale is not None:
             _need(self.gu_inscale, "gu_inscale", torch.float32, (E, 2))
         if self.dn_inscale is not None:
             _need(self.dn_inscale, "dn_inscale", torch.float32, (E,))
+        opt = lambda t: None if t is None else t.data_ptr()
         st = _Experts(self.gu_codes.data_ptr(), self.gu_scales.data_ptr(),
                       self.dn_codes.data_ptr(), self.dn_scales.data_ptr(),
-                      self.gu_wscale.data_ptr(), self.dn_wscale.data_ptr(),
-                      None if self.gu_inscale is None else self.gu_inscale.data_ptr(),
-                      None if self.dn_inscale is None else self.dn_inscale.data_ptr(),
-                      E, H, I)
+                      opt(self.gu_wscale), opt(self.dn_wscale), opt(self.gu_inscale), opt(self.dn_inscale),
+                      E, H, I, int(self.fmt))
         self.__dict__["_cstruct"] = st
         return st
 
@@ -300,6 +315,46 @@ def act_quant_fp8(x):
     _check("act_quant_fp8", lib().act_quant_fp8(_ptr(x), dt, R, C, _ptr(codes), _ptr(scales),
                                                 _stream()))
     return codes, scales
+
+
+def q4g64_quantize(x):
+    """q4_g64_fp16 packing of fp32 rows x [R, C] (C % 64 == 0).  Returns (codes uint8
+    [R, C/2], scales int16 [R, C/64] holding fp16 bit patterns)."""
+    _need(x, "x", torch.float32)
+    R, C = x.shape
+    codes = torch.empty(R, C // 2, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(R, C // 64, dtype=torch.int16, device=x.device)
+    _check("q4g64_quantize", lib().q4g64_quantize(_ptr(x), R, C, _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales
+
+
+def pack_experts_q4(w_gu, w_dn):
+    """q4_g64_fp16-pack fp32 expert weights on the GPU: w_gu [E, 2I, H] (gate rows then
+    up rows), w_dn [E, H, I]."""
+    _need(w_gu, "w_gu", torch.float32)
+    _need(w_dn, "w_dn", torch.float32)
+    E, I2, H = w_gu.shape
+    I = I2 // 2
+    gc, gs = q4g64_quantize(w_gu.view(E * 2 * I, H))
+    dc, ds = q4g64_quantize(w_dn.view(E * H, I))
+    return Experts(gc.view(E, 2 * I, H // 2), gs.view(E, 2 * I, H // 64), dc.view(E, H, I // 2),
+                   ds.view(E, H, I // 64), fmt=FMT_Q4G64)
+
+
+def debug_q4g64_matmul(codes, scales, x16, out=None):
+    """Test-only: the q4_g64_fp16 narrow core, out [cols, N] fp32 = x16 . dequant(W)^T
+    (x16: fp16 [cols, K], as the experts take it)."""
+    N, K2 = codes.shape
+    K = 2 * K2
+    _need(codes, "codes", torch.uint8, (N, K // 2))
+    _need(scales, "scales", shape=(N, K // 64))
+    _need(x16, "x16", torch.float16)
+    cols = x16.shape[0]
+    if out is None:
+        out = torch.empty(cols, N, dtype=torch.float32, device=codes.device)
+    _check("moe_debug_q4g64_matmul", lib().moe_debug_q4g64_matmul(_ptr(codes), _ptr(scales), N, K, _ptr(x16), cols,
+                                                                  _ptr(out), _stream()))
+    return out
 
 
 def nvfp4_global_scale(x):
@@ -607,7 +662,7 @@ def ffn_workspace_views(ws, mode, T, k, H, I):
         del n
 
     if m == MOE_A16:
-        seg("h", P * I * 2, torch.bfloat16, (P, I))
+        seg("h", P * I * 2, torch.bfloat16, (P, I))   # (q4_g64_fp16 experts: fp16 bits)
     elif m == MOE_A8:
         seg("x_codes", T * H, torch.uint8, (T, H))
         seg("x_scales", T * (H // 16) * 4, torch.float32, (T, H // 16))

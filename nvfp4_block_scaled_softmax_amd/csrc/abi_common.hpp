@@ -36,6 +36,16 @@ inline moe_status check_launch(const char* what) {
     }                                \
   } while (0)
 
+// The kernels' internal mode for q4_g64_fp16 experts (fp16 activations); the
+// public modes are MOE_A16 / MOE_A8 / MOE_A4 = 0 / 1 / 2.
+constexpr int kModeQ4 = 3;
+
+// The mode the kernels run: the public activation mode, or kModeQ4 for
+// q4_g64_fp16 experts (validated to come with MOE_A16).
+inline moe_act_mode kernel_mode(const moe_nvfp4_experts& w, moe_act_mode mode) {
+  return w.fmt == MOE_FMT_Q4G64 ? (moe_act_mode)kModeQ4 : mode;
+}
+
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 64;   // experts per token: one wave lane each in the top-k
 constexpr int kMaxDim = 4096;

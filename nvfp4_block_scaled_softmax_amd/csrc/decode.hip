@@ -779,6 +779,7 @@ moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, in
     switch (mode) {
       case MOE_A16: launch_b<MOE_A16>(a, st, max_slots, prow, tw, residual, out, shared_y, s); break;
       case MOE_A8: launch_b<MOE_A8>(a, st, max_slots, prow, tw, residual, out, shared_y, s); break;
+      case (moe_act_mode)kModeQ4: launch_b<kModeQ4>(a, st, max_slots, prow, tw, residual, out, shared_y, s); break;
       default: launch_b<MOE_A4>(a, st, max_slots, prow, tw, residual, out, shared_y, s); break;
     }
     return check_launch("moe_layer_forward (decode experts)");

@@ -364,6 +364,39 @@ struct Patience {
   }
 };
 
+// ------------------------------------------------------------------ q4_g64_fp16
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);   // v_cvt_f16_f32: nearest even
+}
+
+// Eight 16-bit values in element order (v.x = e0 | e1 << 16, ...) rearranged
+// into the pairs (e0, e4), (e1, e5), (e2, e6), (e3, e7): the order in which
+// q4_expand_pair takes the nibbles of one code dword.
+__device__ __forceinline__ uint4 pair_by_nibble(uint4 v) {
+  return make_uint4((v.x & 0xFFFFu) | (v.z << 16), (v.x >> 16) | (v.z & 0xFFFF0000u),
+                    (v.y & 0xFFFFu) | (v.w << 16), (v.y >> 16) | (v.w & 0xFFFF0000u));
+}
+
+// Eight bf16 values in element order as fp16 (nearest even), paired as above.
+__device__ __forceinline__ uint4 bf16x8_to_f16x8_paired(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = f32_to_f16_bits(bf16_to_f32(w[i] & 0xFFFFu)) | (f32_to_f16_bits(bf16_to_f32(w[i] >> 16)) << 16);
+  return pair_by_nibble(make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// Two int4 codes of a dword (nibbles S and S + 4) as exact fp16 integers: the
+// code xor 8 (offset binary u = q + 8) under the exponent of 1024 is 1024 + u
+// exactly; one packed fp16 add of -1032 leaves q.  `ob` is the dword xor 0x88888888.
+template <int S>
+__device__ __forceinline__ f16x2 q4_expand_pair(uint32_t ob) {
+  const f16x2 v = bitcast<f16x2>(((ob >> (4 * S)) & 0x000F000Fu) | 0x64006400u);
+  const f16x2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  return v + bias;
+}
+
 // bf16 NaN: what a combine writes for an output whose inputs it gave up on.
 constexpr uint16_t kBf16NaN = 0x7FC0;
 

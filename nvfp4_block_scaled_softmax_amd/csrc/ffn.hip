@@ -127,10 +127,11 @@ FfnArgs make_ffn_args(const moe_nvfp4_experts& w, moe_act_mode mode, const uint1
   a.offsets = offsets;
   a.sorted_pairs = sorted_pairs;
   a.x = x;
-  a.xq_codes = mode == MOE_A16 ? nullptr : base + L.xq_codes;
-  a.xq_scales = mode == MOE_A16 ? nullptr : base + L.xq_scales;
+  const bool x16 = mode == MOE_A16 || (int)mode == kModeQ4;   // 16-bit activations, nothing quantized
+  a.xq_codes = x16 ? nullptr : base + L.xq_codes;
+  a.xq_scales = x16 ? nullptr : base + L.xq_scales;
   a.h_codes = base + L.h_codes;
-  a.h_scales = mode == MOE_A16 ? nullptr : base + L.h_scales;
+  a.h_scales = x16 ? nullptr : base + L.h_scales;
   a.y = y_pairs;
   return a;
 }
@@ -179,6 +180,20 @@ moe_status check_experts(const char* name, const moe_nvfp4_experts* w, moe_act_m
   MOE_REQUIRE(w, MOE_E_ARG, "%s: null expert set", name);
   MOE_REQUIRE(mode == MOE_A16 || mode == MOE_A8 || mode == MOE_A4, MOE_E_ARG, "%s: bad mode %d",
               name, (int)mode);
+  MOE_REQUIRE(w->fmt == MOE_FMT_NVFP4 || w->fmt == MOE_FMT_Q4G64, MOE_E_ARG, "%s: bad weight format %d", name,
+              (int)w->fmt);
+  if (w->fmt == MOE_FMT_Q4G64) {
+    MOE_REQUIRE(mode == MOE_A16, MOE_E_UNSUPPORTED, "%s: q4_g64_fp16 experts take 16-bit activations only", name);
+    MOE_REQUIRE(w->gu_codes && w->gu_scales && w->dn_codes && w->dn_scales, MOE_E_ARG, "%s: null expert array",
+                name);
+    MOE_REQUIRE(w->E >= 1 && w->E <= kMaxExperts && dim_ok(w->H) && dim_ok(w->I) && w->H % 64 == 0 &&
+                    w->I % 64 == 0,
+                MOE_E_SHAPE, "%s: bad q4_g64_fp16 expert shape E=%d H=%d I=%d", name, w->E, w->H, w->I);
+    MOE_REQUIRE(aligned(w->gu_codes, 16) && aligned(w->gu_scales, 16) && aligned(w->dn_codes, 16) &&
+                    aligned(w->dn_scales, 16),
+                MOE_E_ALIGN, "%s: misaligned expert array", name);
+    return MOE_OK;
+  }
   MOE_REQUIRE(w->gu_codes && w->gu_scales && w->dn_codes && w->dn_scales && w->gu_wscale &&
                   w->dn_wscale,
               MOE_E_ARG, "%s: null expert array", name);
@@ -209,11 +224,11 @@ static moe_status ffn_entry(const char* name, const moe_nvfp4_experts* w, moe_ac
   MOE_REQUIRE(moe::aligned(x, 16) && moe::aligned(ws, 16) && moe::aligned(y_pairs, 16) &&
                   moe::aligned(expert_offsets, 4) && moe::aligned(sorted_pairs, 4),
               MOE_E_ALIGN, "%s: misaligned pointer", name);
-  const size_t need = moe::expert_ffn_workspace(mode, T, k, w->H, w->I);
+  const size_t need = moe::expert_ffn_workspace(moe::kernel_mode(*w, mode), T, k, w->H, w->I);
   MOE_REQUIRE(ws_bytes >= need, MOE_E_WORKSPACE, "%s: workspace %zu < %zu bytes", name, ws_bytes,
               need);
-  return moe::launch_expert_ffn(*w, mode, x, T, k, expert_offsets, sorted_pairs, y_pairs, ws,
-                                stage_mask, s);
+  return moe::launch_expert_ffn(*w, moe::kernel_mode(*w, mode), x, T, k, expert_offsets, sorted_pairs, y_pairs,
+                                ws, stage_mask, s);
 }
 
 extern "C" moe_status nvfp4_expert_ffn(const moe_nvfp4_experts* w, moe_act_mode mode,
@@ -283,4 +298,26 @@ extern "C" moe_status moe_debug_nvfp4_matmul(int core, moe_act_mode mode, const 
   a.h_scales = const_cast<void*>(x_scales);
   a.y = out;
   return core == 1 ? moe::launch_debug_wide(a, ws, s) : moe::launch_debug_narrow(a, mode, s);
+}
+
+extern "C" moe_status moe_debug_q4g64_matmul(const uint8_t* codes, const uint16_t* scales, int N, int K,
+                                             const uint16_t* x, int cols, float* out, hipStream_t s) {
+  const char* name = "moe_debug_q4g64_matmul";
+  moe::clear_error();
+  MOE_REQUIRE(codes && scales && x && out, MOE_E_ARG, "%s: null pointer argument", name);
+  MOE_REQUIRE(N >= 1 && N <= (1 << 20) && moe::dim_ok(K) && K % 64 == 0 && cols >= 1 && cols <= (1 << 16),
+              MOE_E_SHAPE, "%s: bad shape N=%d K=%d cols=%d", name, N, K, cols);
+  MOE_REQUIRE(moe::aligned(codes, 16) && moe::aligned(scales, 16) && moe::aligned(x, 16) && moe::aligned(out, 16),
+              MOE_E_ALIGN, "%s: misaligned pointer", name);
+  moe::FfnArgs a{};
+  a.dn_codes = codes;
+  a.dn_scales = reinterpret_cast<const uint8_t*>(scales);
+  a.E = 1;
+  a.H = N;
+  a.I = K;
+  a.T = cols;
+  a.k = 1;
+  a.h_codes = const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(x));
+  a.y = out;
+  return moe::launch_debug_narrow(a, (moe_act_mode)moe::kModeQ4, s);
 }

@@ -35,7 +35,7 @@ inline FfnLayout ffn_layout(moe_act_mode mode, int T, int k, int H, int I) {
   FfnLayout L{0, 0, 0, 0, 0, 0};
   size_t o = 0;
   auto seg = [&](size_t bytes) { const size_t at = o; o = round_up(o + bytes, 256); return at; };
-  if (mode == MOE_A16) {
+  if (mode == MOE_A16 || (int)mode == kModeQ4) {
     L.h_codes = seg(P * I * 2);
   } else if (mode == MOE_A8) {
     L.xq_codes = seg((size_t)T * H);
@@ -52,6 +52,7 @@ inline FfnLayout ffn_layout(moe_act_mode mode, int T, int k, int H, int I) {
   L.total = o;
   return L;
 }
+// (kModeQ4 lays out as MOE_A16: the fp16 intermediate [P][I].)
 
 // ---------------------------------------------------------------------------
 // Narrow-path LDS chunk layout: one "chunk" = 32 consecutive K values of one
@@ -69,6 +70,19 @@ template <>
 struct ChunkLds<MOE_A8> { static constexpr int kStride = 48; };
 template <>
 struct ChunkLds<MOE_A4> { static constexpr int kStride = 48; };
+// q4_g64_fp16 experts: [64 B fp16 x, paired by nibble (pair_by_nibble)] stride 80
+template <>
+struct ChunkLds<kModeQ4> { static constexpr int kStride = 80; };
+
+// Bytes of one row's scales per 32-value chunk, and the scale of chunk c within
+// a row's scale bytes: NVFP4 two E4M3 per chunk; q4_g64_fp16 one fp16 per two chunks.
+template <int MODE>
+__device__ __forceinline__ uint32_t chunk_scale(const uint8_t* srow, int c) {
+  if constexpr (MODE == kModeQ4) return *reinterpret_cast<const uint16_t*>(srow + 2 * (c >> 1));
+  else return *reinterpret_cast<const uint16_t*>(srow + 2 * c);
+}
+template <int MODE>
+__host__ __device__ constexpr int scale_row_bytes(int K) { return MODE == kModeQ4 ? K / 32 : K / 16; }
 
 // Dot product of one 16-byte weight chunk (32 E2M1 codes, block scales in the
 // two bytes of wsc) with the activation chunk at `c` (LDS), matrix m (A4).
@@ -140,6 +154,24 @@ __device__ __forceinline__ float chunk_dot<MOE_A4>(const uint4 w, uint32_t wsc, 
   const float s0 = e4m3_to_f32(wsc & 0xFFu) * e4m3_to_f32(xs & 0xFFu);      // exact
   const float s1 = e4m3_to_f32((wsc >> 8) & 0xFFu) * e4m3_to_f32(xs >> 8);  // exact
   return b0 * s0 + b1 * s1;
+}
+
+template <>
+__device__ __forceinline__ float chunk_dot<kModeQ4>(const uint4 w, uint32_t wsc, const uint8_t* c, int) {
+  // q4_g64_fp16: 32 int4 codes (one fp16 scale: a chunk is half a group of 64)
+  // against 32 fp16 x; products of integers -8..7 and fp16 values are exact.
+  const uint4* xc = reinterpret_cast<const uint4*>(c);
+  const uint32_t wd[4] = {w.x ^ 0x88888888u, w.y ^ 0x88888888u, w.z ^ 0x88888888u, w.w ^ 0x88888888u};
+  float acc = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint4 xv = xc[d];
+    acc = __builtin_amdgcn_fdot2(q4_expand_pair<0>(wd[d]), bitcast<f16x2>(xv.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(q4_expand_pair<1>(wd[d]), bitcast<f16x2>(xv.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(q4_expand_pair<2>(wd[d]), bitcast<f16x2>(xv.z), acc, false);
+    acc = __builtin_amdgcn_fdot2(q4_expand_pair<3>(wd[d]), bitcast<f16x2>(xv.w), acc, false);
+  }
+  return acc * (float)bitcast<_Float16>((uint16_t)(wsc & 0xFFFFu));
 }
 
 // Binary search: the expert whose segment [offsets[e], offsets[e+1]) holds row r.

@@ -138,18 +138,20 @@ static moe_status run_debug(const FfnArgs& a, hipStream_t s) {
 }
 
 moe_status launch_debug_narrow(const FfnArgs& a, moe_act_mode mode, hipStream_t s) {
-  switch (mode) {
+  switch ((int)mode) {
     case MOE_A16: return run_debug<MOE_A16>(a, s);
     case MOE_A8: return run_debug<MOE_A8>(a, s);
+    case kModeQ4: return run_debug<kModeQ4>(a, s);
     default: return run_debug<MOE_A4>(a, s);
   }
 }
 
 moe_status launch_ffn_narrow(const FfnArgs& a, moe_act_mode mode, int slots, int stage_mask,
                              hipStream_t s) {
-  switch (mode) {
+  switch ((int)mode) {
     case MOE_A16: return run<MOE_A16>(a, slots, stage_mask, s);
     case MOE_A8: return run<MOE_A8>(a, slots, stage_mask, s);
+    case kModeQ4: return run<kModeQ4>(a, slots, stage_mask, s);
     default: return run<MOE_A4>(a, slots, stage_mask, s);
   }
 }

@@ -23,8 +23,8 @@ __device__ void stage_gateup_cols(const FfnArgs& a, int e, int row0, int c0, int
                                   const int* tok, uint8_t* lds) {
   constexpr int S = ChunkLds<MODE>::kStride;
   const int H = a.H, NC = H / 32;
-  if (MODE == MOE_A16) {
-    // 4 x 16 B per chunk
+  if (MODE == MOE_A16 || MODE == kModeQ4) {
+    // 4 x 16 B per chunk (q4_g64_fp16: as fp16, paired by nibble)
     batched_copy<kTileThreads, kStageBatch>(
         ncol * NC * 4,
         [&](int i) {
@@ -33,6 +33,7 @@ __device__ void stage_gateup_cols(const FfnArgs& a, int e, int row0, int c0, int
         },
         [&](int i, uint4 v) {
           const int col = i / (NC * 4), rem = i % (NC * 4), ch = rem / 4, q = rem % 4;
+          if constexpr (MODE == kModeQ4) v = bf16x8_to_f16x8_paired(v);
           *reinterpret_cast<uint4*>(lds + ((size_t)col * NC + ch) * S + 16 * q) = v;
         });
   } else if (MODE == MOE_A8) {
@@ -90,7 +91,7 @@ template <int MODE, bool COH>
 __device__ void stage_down_cols(const FfnArgs& a, int row0, int c0, int ncol, uint8_t* lds) {
   constexpr int S = ChunkLds<MODE>::kStride;
   const int I = a.I, NC = I / 32;
-  if (MODE == MOE_A16) {
+  if (MODE == MOE_A16 || MODE == kModeQ4) {
     const uint16_t* h = reinterpret_cast<const uint16_t*>(a.h_codes);
     batched_copy<kTileThreads, kStageBatch>(
         ncol * NC * 4,
@@ -100,6 +101,7 @@ __device__ void stage_down_cols(const FfnArgs& a, int row0, int c0, int ncol, ui
         },
         [&](int i, uint4 v) {
           const int col = i / (NC * 4), rem = i % (NC * 4), ch = rem / 4, q = rem % 4;
+          if constexpr (MODE == kModeQ4) v = pair_by_nibble(v);   // fp16 h, paired by nibble
           *reinterpret_cast<uint4*>(lds + ((size_t)col * NC + ch) * S + 16 * q) = v;
         });
   } else if (MODE == MOE_A8) {
@@ -251,12 +253,12 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, i
     const int hl = slot * RP + r;  // h row within the wave's four
     const size_t grow = (size_t)e * 2 * I + (size_t)half * I + i0 + wave * 4 + min(hl, 3);
     const uint8_t* crow = a.gu_codes + grow * (H / 2);
-    const uint8_t* srow = a.gu_scales + grow * (H / 16);
+    const uint8_t* srow = a.gu_scales + grow * scale_row_bytes<MODE>(H);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = min(kl + j * LPR, NC - 1);
       wq[r][j] = *reinterpret_cast<const uint4*>(crow + 16 * c);
-      wsc[r][j] = *reinterpret_cast<const uint16_t*>(srow + 2 * c);
+      wsc[r][j] = chunk_scale<MODE>(srow, c);
     }
   }
   __builtin_amdgcn_sched_barrier(0);   // every load issued before any use of one
@@ -264,7 +266,7 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, i
   // now, with no wait for the pairs' tokens, and columns index it by token.
   const bool by_token = MODE != MOE_A4 && a.T <= max_cols;
   if (by_token) stage_gateup_cols<MODE, true>(a, e, 0, 0, a.T, nullptr, lds);
-  const float wsc_m = a.gu_wscale[2 * e + half];
+  const float wsc_m = MODE == kModeQ4 ? 1.0f : a.gu_wscale[2 * e + half];   // (q4: no multiplier)
   const float in_m = MODE == MOE_A4 ? a.gu_inscale[2 * e + half] : 1.0f;
   const float dn_in = MODE == MOE_A4 ? a.dn_inscale[e] : 0.0f;   // the intermediate's input scale
 
@@ -316,12 +318,14 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, i
         const float h = swiglu(part[col][hr][0], part[col][hr][1]);
         if (MODE == MOE_A16) {
           hst16<COH>(a.h_codes, 2 * ((size_t)(row0 + c0 + col) * I + i0 + hr), (uint16_t)f32_to_bf16(h));
+        } else if (MODE == kModeQ4) {   // the fp16 intermediate
+          hst16<COH>(a.h_codes, 2 * ((size_t)(row0 + c0 + col) * I + i0 + hr), (uint16_t)f32_to_f16_bits(h));
         } else {
           hbuf[col][hr] = h;
         }
       }
     }
-    if (MODE != MOE_A16) {
+    if (MODE == MOE_A8 || MODE == MOE_A4) {
       __syncthreads();
       if (threadIdx.x < ncol) {
         const int col = threadIdx.x;
@@ -376,16 +380,16 @@ __device__ __forceinline__ void down_tile(const FfnArgs& a, int e, int row0, int
     const int orow = o0 + wave * 16 + slot * RP + r;
     const size_t grow = (size_t)e * H + min(orow, H - 1);
     const uint8_t* crow = a.dn_codes + grow * (I / 2);
-    const uint8_t* srow = a.dn_scales + grow * (I / 16);
+    const uint8_t* srow = a.dn_scales + grow * scale_row_bytes<MODE>(I);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = min(kl + j * LPR, NC - 1);
       wq[r][j] = *reinterpret_cast<const uint4*>(crow + 16 * c);
-      wsc[r][j] = *reinterpret_cast<const uint16_t*>(srow + 2 * c);
+      wsc[r][j] = chunk_scale<MODE>(srow, c);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  const float scale = a.dn_wscale[e] * (MODE == MOE_A4 ? a.dn_inscale[e] : 1.0f);
+  const float scale = MODE == kModeQ4 ? 1.0f : a.dn_wscale[e] * (MODE == MOE_A4 ? a.dn_inscale[e] : 1.0f);
   wait();
 
   for (int c0 = 0; c0 < ne; c0 += max_cols) {

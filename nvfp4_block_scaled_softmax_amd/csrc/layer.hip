@@ -108,6 +108,7 @@ static moe_status layer_call(const char* name, const moe_nvfp4_experts* w, moe_a
   moe::LayerLayout L;
   MOE_REQUIRE(moe::layer_layout(mode, T, k, w->E, w->H, w->I, L, sw ? sw->Is : 0), MOE_E_SHAPE,
               "%s: bad shape T=%d k=%d", name, T, k);
+  mode = moe::kernel_mode(*w, mode);   // (q4_g64_fp16 experts: the fp16 kernels; the layout is the same)
   MOE_REQUIRE(out != x, MOE_E_ARG, "%s: out must not alias x", name);
   MOE_REQUIRE(moe::aligned(x, 16) && moe::aligned(w_router, 16) && moe::aligned(out, 16) &&
                   moe::aligned(ws, 256) && (!residual || moe::aligned(residual, 16)) &&

@@ -162,3 +162,82 @@ extern "C" moe_status nvfp4_global_scale(const float* x, int n_mat, int64_t mat_
   hipLaunchKernelGGL(moe::k_global_scale, dim3(n_mat), dim3(1024), 0, s, x, mat_elems, global);
   return moe::check_launch("nvfp4_global_scale");
 }
+
+// ------------------------------------------------------------------ q4_g64_fp16
+// One thread per group of 64 values (page "Qwen3.8-Flash-Next NVIDIA NVFP4 for
+// Infernix (bit-exact)", section "Drafting only": 4-bit codes, one FP16 scale
+// per 64, scales chosen by squared error from the exact values).  The nine
+// candidate scales d = fp16(amax / m), m = 7, 7.125, ..., 8, are each scored
+// by the sum of (v - d q)^2 in double, in index order, every operation rounded
+// once (no contraction), and the first least-error candidate is kept: the
+// choice is a deterministic function of the 64 fp32 values.
+namespace moe {
+
+__global__ void __launch_bounds__(256) k_q4g64_quantize(const float* __restrict__ x, int64_t n_groups,
+                                                        uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+#pragma clang fp contract(off)   // every product and sum below is rounded on its own, as defined
+  const int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gi >= n_groups) return;
+  const uint4* src = reinterpret_cast<const uint4*>(x + gi * 64);
+  float v[64];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const uint4 u = src[q];
+    v[4 * q + 0] = __uint_as_float(u.x);
+    v[4 * q + 1] = __uint_as_float(u.y);
+    v[4 * q + 2] = __uint_as_float(u.z);
+    v[4 * q + 3] = __uint_as_float(u.w);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+  double best = __builtin_inf();
+  uint32_t best_d = 0u;
+  float best_df = 0.0f;
+  for (int j = 0; j <= 8; ++j) {
+    const float m = 7.0f + 0.125f * (float)j;
+    const _Float16 dh = (_Float16)__fdiv_rn(amax, m);   // nearest even
+    const float df = (float)dh;
+    if (!(df > 0.0f) || __builtin_isinf(df)) continue;
+    const double dd = (double)df;
+    double err = 0.0;
+    for (int i = 0; i < 64; ++i) {
+      const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(__fdiv_rn(v[i], df)), -8.0f), 7.0f);
+      const double e = __dsub_rn((double)v[i], __dmul_rn(dd, (double)q));
+      err = __dadd_rn(err, __dmul_rn(e, e));
+    }
+    if (err < best) {
+      best = err;
+      best_d = (uint32_t)__builtin_bit_cast(uint16_t, dh);
+      best_df = df;
+    }
+  }
+  uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  if (best_df > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const float q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(__fdiv_rn(v[i], best_df)), -8.0f), 7.0f);
+      w[i / 8] |= ((uint32_t)(int)q & 15u) << (4 * (i % 8));
+    }
+  }
+  uint4* dst = reinterpret_cast<uint4*>(codes + gi * 32);
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  scales[gi] = (uint16_t)best_d;
+}
+
+}  // namespace moe
+
+extern "C" moe_status q4g64_quantize(const float* x, int rows, int cols, uint8_t* codes, uint16_t* scales,
+                                     hipStream_t s) {
+  moe::clear_error();
+  MOE_REQUIRE(x && codes && scales, MOE_E_ARG, "q4g64_quantize: null pointer argument");
+  MOE_REQUIRE(rows >= 1 && cols >= 64 && cols % 64 == 0, MOE_E_SHAPE, "q4g64_quantize: bad shape %d x %d", rows,
+              cols);
+  MOE_REQUIRE(moe::aligned(x, 16) && moe::aligned(codes, 16) && moe::aligned(scales, 2), MOE_E_ALIGN,
+              "q4g64_quantize: misaligned pointer");
+  const int64_t n = (int64_t)rows * (cols / 64);
+  hipLaunchKernelGGL(moe::k_q4g64_quantize, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, n, codes,
+                     scales);
+  return moe::check_launch("q4g64_quantize");
+}

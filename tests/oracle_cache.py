@@ -32,22 +32,24 @@ def stop_pool():
 
 
 def _pack(args):
-    w, layer, e = args
-    return e, OL.pack_expert(*(synth.expert_matrix(w, layer, e, m) for m in range(3)))
+    w, layer, e, fmt = args
+    pack = OL.pack_expert_q4 if fmt == "q4" else OL.pack_expert
+    return e, pack(*(synth.expert_matrix(w, layer, e, m) for m in range(3)))
 
 
 class ExpertCache:
-    """Lazily packed oracle experts of one (workload, layer)."""
+    """Lazily packed oracle experts of one (workload, layer); fmt "nvfp4" or "q4"
+    (q4_g64_fp16)."""
 
-    def __init__(self, w, layer=0, inscales=None):
-        self.w, self.layer, self.inscales = w, layer, inscales
+    def __init__(self, w, layer=0, inscales=None, fmt="nvfp4"):
+        self.w, self.layer, self.inscales, self.fmt = w, layer, inscales, fmt
         self.cache = {}
 
     def prefetch(self, experts):
         todo = sorted(set(int(e) for e in experts) - set(self.cache))
         if not todo:
             return
-        args = [(self.w, self.layer, e) for e in todo]
+        args = [(self.w, self.layer, e, self.fmt) for e in todo]
         results = _POOL.map(_pack, args) if _POOL is not None and len(todo) > 1 else map(_pack, args)
         for e, ex in results:
             self._store(e, ex)
@@ -61,5 +63,5 @@ class ExpertCache:
     def __call__(self, e):
         e = int(e)
         if e not in self.cache:
-            self._store(*_pack((self.w, self.layer, e)))
+            self._store(*_pack((self.w, self.layer, e, self.fmt)))
         return self.cache[e]

@@ -123,7 +123,7 @@ def check_experts(w, mode, x_u16, get_expert, k, offsets, sorted_pairs, y_gpu, f
                                               ex.gu_inscale[m])[0]
                 assert np.array_equal(ffn_ws["x_codes"][rows, m], c), (e, m)
                 assert np.array_equal(ffn_ws["x_scales"][rows, m], s), (e, m)
-        if mode == "A16":
+        if mode in ("A16", "F16"):
             gpu_h = ffn_ws["h"][rows]
         else:
             gpu_h = (ffn_ws["h_codes"][rows], ffn_ws["h_scales"][rows])

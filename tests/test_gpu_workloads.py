@@ -67,9 +67,11 @@ def check_packed_bytes(ex_gpu, cache, experts):
     for e in experts:
         o = cache(e)
         assert np.array_equal(host(ex_gpu.gu_codes[e]), o.gu_codes), e
-        assert np.array_equal(host(ex_gpu.gu_scales[e]), o.gu_scales), e
+        assert np.array_equal(host(ex_gpu.gu_scales[e]).view(o.gu_scales.dtype), o.gu_scales), e
         assert np.array_equal(host(ex_gpu.dn_codes[e]), o.dn_codes), e
-        assert np.array_equal(host(ex_gpu.dn_scales[e]), o.dn_scales), e
+        assert np.array_equal(host(ex_gpu.dn_scales[e]).view(o.dn_scales.dtype), o.dn_scales), e
+        if cache.fmt == "q4":
+            continue
         assert np.array_equal(host(ex_gpu.gu_wscale[e]).view(np.uint32), o.gu_wscale.view(np.uint32)), e
         assert host(ex_gpu.dn_wscale[e]).view(np.uint32) == np.float32(o.dn_wscale).view(np.uint32), e
 

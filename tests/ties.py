@@ -99,18 +99,19 @@ def expected_intermediate(res, mode, gpu, dn_inscale=None, report=None):
     err = h_error_bound(res)
     n, I = h.shape
     rep.elements += n * I
-    if mode == "A16":
+    if mode in ("A16", "F16"):   # one rounding to bf16 / fp16
+        to16, from16 = (F.f64_to_bf16, F.bf16_to_f64) if mode == "A16" else (F.f64_to_f16, F.f16_to_f64)
         g = np.asarray(gpu, np.uint16)
-        lo = F.f64_to_bf16(F.f32(h - err).astype(np.float64))
-        hi = F.f64_to_bf16(F.f32(h + err).astype(np.float64))
-        gv, lv, hv = F.bf16_to_f64(g), F.bf16_to_f64(lo), F.bf16_to_f64(hi)
+        lo = to16(F.f32(h - err).astype(np.float64))
+        hi = to16(F.f32(h + err).astype(np.float64))
+        gv, lv, hv = from16(g), from16(lo), from16(hi)
         ok = (gv >= lv) & (gv <= hv)
         nom = res.hq[0]
         rep.two_candidate += int(np.sum(lo != hi))
         rep.flipped += int(np.sum(g != nom))
         rep.row_flips = np.any(g != nom, axis=1)
         for r, c in zip(*np.nonzero(~ok)):
-            rep.bad.append((int(r), int(c), f"bf16 {gv[r, c]} outside [{lv[r, c]}, {hv[r, c]}]"))
+            rep.bad.append((int(r), int(c), f"{mode} h {gv[r, c]} outside [{lv[r, c]}, {hv[r, c]}]"))
         return gv
     blocks = h.reshape(n, I // 16, 16)
     eb = err.reshape(n, I // 16, 16)
