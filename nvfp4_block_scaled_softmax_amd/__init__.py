@@ -661,19 +661,23 @@ def ffn_workspace_views(ws, mode, T, k, H, I):
         o = (o + nbytes + 255) // 256 * 256
         del n
 
+    n_plan = min(P, 1024) + P // 32
     if m == MOE_A16:
         seg("h", P * I * 2, torch.bfloat16, (P, I))   # (q4_g64_fp16 experts: fp16 bits)
+        if T > 8:
+            seg("plan", n_plan * 16, torch.int32, (n_plan, 4))
     elif m == MOE_A8:
         seg("x_codes", T * H, torch.uint8, (T, H))
         seg("x_scales", T * (H // 16) * 4, torch.float32, (T, H // 16))
         seg("h_codes", P * I, torch.uint8, (P, I))
         seg("h_scales", P * (I // 16) * 4, torch.float32, (P, I // 16))
+        if T > 8:
+            seg("plan", n_plan * 16, torch.int32, (n_plan, 4))
     else:
         seg("x_codes", P * 2 * (H // 2), torch.uint8, (P, 2, H // 2))
         seg("x_scales", P * 2 * (H // 16), torch.uint8, (P, 2, H // 16))
         seg("h_codes", P * (I // 2), torch.uint8, (P, I // 2))
         seg("h_scales", P * (I // 16), torch.uint8, (P, I // 16))
-        n_plan = min(P, 1024) + P // 32
         seg("plan", n_plan * 16, torch.int32, (n_plan, 4))
     return out
 

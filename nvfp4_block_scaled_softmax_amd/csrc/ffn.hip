@@ -162,8 +162,8 @@ moe_status launch_expert_ffn(const moe_nvfp4_experts& w, moe_act_mode mode, cons
     moe_status st = check_launch("nvfp4_expert_ffn (x quantization)");
     if (st != MOE_OK) return st;
   }
-  if (mode == MOE_A4 && T > kNarrowMaxT && w.H % 128 == 0 && w.I % 128 == 0)
-    return launch_ffn_wide_a4(a, stage_mask, base + L.plan, s);
+  if ((int)mode != kModeQ4 && T > kNarrowMaxT && w.H % 128 == 0 && w.I % 128 == 0)
+    return launch_ffn_wide(a, mode, stage_mask, base + L.plan, s);
   return launch_ffn_narrow(a, mode, slots, stage_mask, s);
 }
 
@@ -278,7 +278,6 @@ extern "C" moe_status moe_debug_nvfp4_matmul(int core, moe_act_mode mode, const 
                   (!x_scales || moe::aligned(x_scales, 16)),
               MOE_E_ALIGN, "%s: misaligned pointer", name);
   if (core == 1) {
-    MOE_REQUIRE(mode == MOE_A4, MOE_E_UNSUPPORTED, "%s: the wide core takes 4-bit x", name);
     MOE_REQUIRE(N % 16 == 0 && K % 128 == 0, MOE_E_SHAPE, "%s: the wide core needs N %% 16 == 0, K %% 128 == 0",
                 name);
     MOE_REQUIRE(ws && moe::aligned(ws, 16) && ws_bytes >= moe::debug_wide_plan_bytes(cols), MOE_E_WORKSPACE,
@@ -297,7 +296,7 @@ extern "C" moe_status moe_debug_nvfp4_matmul(int core, moe_act_mode mode, const 
   a.h_codes = const_cast<uint8_t*>(static_cast<const uint8_t*>(x));
   a.h_scales = const_cast<void*>(x_scales);
   a.y = out;
-  return core == 1 ? moe::launch_debug_wide(a, ws, s) : moe::launch_debug_narrow(a, mode, s);
+  return core == 1 ? moe::launch_debug_wide(a, mode, ws, s) : moe::launch_debug_narrow(a, mode, s);
 }
 
 extern "C" moe_status moe_debug_q4g64_matmul(const uint8_t* codes, const uint16_t* scales, int N, int K,

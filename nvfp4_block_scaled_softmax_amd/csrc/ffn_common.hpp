@@ -37,11 +37,13 @@ inline FfnLayout ffn_layout(moe_act_mode mode, int T, int k, int H, int I) {
   auto seg = [&](size_t bytes) { const size_t at = o; o = round_up(o + bytes, 256); return at; };
   if (mode == MOE_A16 || (int)mode == kModeQ4) {
     L.h_codes = seg(P * I * 2);
+    if (mode == MOE_A16 && T > 8) L.plan = seg(((P < (size_t)kMaxExperts ? P : (size_t)kMaxExperts) + P / 32) * 16);
   } else if (mode == MOE_A8) {
     L.xq_codes = seg((size_t)T * H);
     L.xq_scales = seg((size_t)T * (H / 16) * 4);
     L.h_codes = seg(P * I);
     L.h_scales = seg(P * (I / 16) * 4);
+    if (T > 8) L.plan = seg(((P < (size_t)kMaxExperts ? P : (size_t)kMaxExperts) + P / 32) * 16);
   } else {
     L.xq_codes = seg(P * 2 * (H / 2));
     L.xq_scales = seg(P * 2 * (H / 16));
@@ -190,14 +192,15 @@ moe_status launch_ffn_narrow(const FfnArgs& a, moe_act_mode mode, int slots, int
 FfnArgs make_ffn_args(const moe_nvfp4_experts& w, moe_act_mode mode, const uint16_t* x, int T,
                       int k, const int32_t* offsets, const int32_t* sorted_pairs, float* y_pairs,
                       void* ws);
-moe_status launch_ffn_wide_a4(const FfnArgs& a, int stage_mask, void* plan_ws, hipStream_t s);
+// The wide (MFMA) path of calls above kNarrowMaxT tokens, for each activation mode.
+moe_status launch_ffn_wide(const FfnArgs& a, moe_act_mode mode, int stage_mask, void* plan_ws, hipStream_t s);
 // Entries of the wide path's work plan for P sorted rows of E experts.
 int wide_plan_entries(int P, int E);
 // The product cores alone (moe_debug_nvfp4_matmul), on an argument block whose
 // expert 0 down matrix is the N x K operand (H = N, I = K) and whose
 // intermediate slots (h_codes, h_scales) hold the T columns.
 moe_status launch_debug_narrow(const FfnArgs& a, moe_act_mode mode, hipStream_t s);
-moe_status launch_debug_wide(const FfnArgs& a, void* plan_ws, hipStream_t s);
+moe_status launch_debug_wide(const FfnArgs& a, moe_act_mode mode, void* plan_ws, hipStream_t s);
 size_t debug_wide_plan_bytes(int cols);
 
 // Calls with more than this many tokens take the MFMA path (4-bit mode).

@@ -53,6 +53,18 @@ __device__ __forceinline__ f16x8 expand8(uint32_t codes, f16x2 s2) {
   return f16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
+// The same as a bf16x8 operand (16-bit activations): E2M1 to fp32, times the
+// E4M3 scale in fp32 (exact: at most 6 significant bits), packed to bf16 (exact).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8 expand8_bf16(uint32_t codes, float s) {
+  const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+  const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+  const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+  const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+  return bf16x8{(__bf16)(a.x * s), (__bf16)(a.y * s), (__bf16)(b.x * s), (__bf16)(b.y * s),
+                (__bf16)(c.x * s), (__bf16)(c.y * s), (__bf16)(d.x * s), (__bf16)(d.y * s)};
+}
+
 // Both E4M3 bytes of a 16-bit scale pair as f16 splats: .x = first, .y = second.
 __device__ __forceinline__ void scale_pair(uint32_t sc, f16x2& s0, f16x2& s1) {
   const f16x2 p = e4m3x2_to_f16<false>(sc);   // bytes 0, 1 of sc
@@ -65,12 +77,6 @@ __device__ __forceinline__ uint32_t e2m1_under(float v, float d) {
   return d > 0.0f ? f32_to_e2m1(__fdiv_rn(v, d)) : 0u;
 }
 
-// 32 consecutive K values of one row: 16 bytes of codes, two E4M3 scales.
-struct Frag {
-  uint4 c;
-  uint16_t s;   // widened where used, so no instruction touches it before then
-};
-
 // Buffer resource over [base, base + bytes); 0x00020000 is the raw-buffer
 // format word of the gfx9 family.  Every offset used below stays inside.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int bytes) {
@@ -79,7 +85,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int byt
 
 // Rows of NVFP4 pieces along K: codes [rows][K/2], scales [rows][K/16].  A lane
 // reads piece g (32 values) of step st of its row: code offset row*K/2 + 16g +
-// 64st, scale offset row*K/16 + 2g + 8st; the step part is a scalar.
+// 64st, scale offset row*K/16 + 2g + 8st; the step part is a scalar.  (As an
+// activation source: the rows of the mode's stored activations, see XRows.)
 struct Rows {
   __amdgpu_buffer_rsrc_t codes, scales;
 };
@@ -115,13 +122,32 @@ __device__ __forceinline__ uint32_t window_scales(const uint4& sw, int lane) {
   return (g & 1) ? d >> 16 : d & 0xFFFFu;
 }
 
-__device__ __forceinline__ void expand_frag(const uint4& c, uint32_t sc, f16x8 (&v)[4]) {
-  f16x2 s0, s1;
-  scale_pair(sc, s0, s1);
-  v[0] = expand8(c.x, s0);
-  v[1] = expand8(c.y, s0);
-  v[2] = expand8(c.z, s1);
-  v[3] = expand8(c.w, s1);
+// The MFMA operand type of a mode: bf16 for 16-bit activations, f16 otherwise.
+template <int MODE>
+using WideOp = typename std::conditional<MODE == MOE_A16, bf16x8, f16x8>::type;
+
+template <int MODE>
+__device__ __forceinline__ void expand_frag(const uint4& c, uint32_t sc, WideOp<MODE> (&v)[4]) {
+  if constexpr (MODE == MOE_A16) {
+    const float s0 = e4m3_to_f32(sc & 0xFFu), s1 = e4m3_to_f32((sc >> 8) & 0xFFu);
+    v[0] = expand8_bf16(c.x, s0);
+    v[1] = expand8_bf16(c.y, s0);
+    v[2] = expand8_bf16(c.z, s1);
+    v[3] = expand8_bf16(c.w, s1);
+  } else {
+    f16x2 s0, s1;
+    scale_pair(sc, s0, s1);
+    v[0] = expand8(c.x, s0);
+    v[1] = expand8(c.y, s0);
+    v[2] = expand8(c.z, s1);
+    v[3] = expand8(c.w, s1);
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ f32x4 wide_mfma(const WideOp<MODE>& a, const uint4& b, const f32x4& c) {
+  if constexpr (MODE == MOE_A16) return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bitcast<bf16x8>(b), c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bitcast<f16x8>(b), c, 0, 0, 0);
 }
 
 // ------------------------------------------------------------------ plan
@@ -220,56 +246,135 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 template <int NM>
 struct WideLds {
-  static constexpr int kBuf = NM * kWideTok * kTokStride;   // [NM][token][k] f16
+  static constexpr int kBuf = NM * kWideTok * kTokStride;   // [NM][token][k] 16-bit values
   __align__(16) uint8_t buf[2 * kBuf];
 };
 
-// One thread's share of staging: matrix sm, token sn, 32-wide piece sq of a chunk.
+// LDS planes of a chunk's activations: 4-bit gate/up, one per matrix (each
+// matrix has its own input scale); 16-bit, the bf16 values; 8-bit, each value
+// f32(E4M3 value * its block's fp32 scale) as the sum of two fp16 (hi, lo:
+// 22 significant bits), which the main loop multiplies in two MFMAs.
+template <int MODE, bool GU>
+constexpr int wide_planes() { return MODE == MOE_A16 ? 1 : (MODE == MOE_A8 ? 2 : (GU ? 2 : 1)); }
+
+// One thread's share of staging: plane sm, token sn, 32-wide piece sq of a chunk.
 struct Stager {
   int sm, sn, sq;
-  int vc, vs;       // byte offsets of the thread's token row (codes, scales)
+  int vc, vs;       // byte offsets of the thread's activation row (values or codes, scales)
   int K;
   bool on;          // the token belongs to a computed column tile
 };
 
-__device__ __forceinline__ void load_chunk(Frag& f, const Rows& x, const Stager& sg, int c) {
-  const int kc = min(c * (kChunkK / 2) + 16 * sg.sq, sg.K / 2 - 16);   // clamped into the row
-  const int ks = min(c * (kChunkK / 16) + 2 * sg.sq, sg.K / 16 - 2);
-  f.c = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x.codes, sg.vc + kc, 0, 0));
-  f.s = __builtin_amdgcn_raw_buffer_load_b16(x.scales, sg.vs + ks, 0, 0);
+// The raw activation piece a staging thread loads per chunk.
+template <int MODE>
+struct XFrag;
+template <>
+struct XFrag<MOE_A4> {
+  uint4 c;
+  uint16_t s;   // widened where used, so no instruction touches it before then
+};
+template <>
+struct XFrag<MOE_A16> {
+  uint4 v[4];
+};
+template <>
+struct XFrag<MOE_A8> {
+  uint4 c[2];
+  uint2 s;
+};
+
+// Activation rows as buffers: 4-bit codes [rows][K/2] + E4M3 [rows][K/16]; 16-bit
+// bf16 [rows][K]; 8-bit E4M3 [rows][K] + fp32 [rows][K/16].
+template <int MODE>
+__device__ __forceinline__ Rows make_xrows(const void* vals, const void* scales, int rows, int K) {
+  if constexpr (MODE == MOE_A16) return Rows{rsrc(vals, rows * K * 2), rsrc(vals, rows * K * 2)};
+  else if constexpr (MODE == MOE_A8) return Rows{rsrc(vals, rows * K), rsrc(scales, rows * (K / 16) * 4)};
+  else return Rows{rsrc(vals, rows * (K / 2)), rsrc(scales, rows * (K / 16))};
 }
 
-__device__ __forceinline__ void stage_chunk(uint8_t* buf, const Frag& f, const Stager& sg) {
+template <int MODE>
+__device__ __forceinline__ void load_chunk(XFrag<MODE>& f, const Rows& x, const Stager& sg, int c) {
+  const int ke = min(c * kChunkK + 32 * sg.sq, sg.K - 32);   // first K value, clamped into the row
+  if constexpr (MODE == MOE_A16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      f.v[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x.codes, sg.vc + 2 * ke + 16 * q, 0, 0));
+  } else if constexpr (MODE == MOE_A8) {
+    f.c[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x.codes, sg.vc + ke, 0, 0));
+    f.c[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x.codes, sg.vc + ke + 16, 0, 0));
+    f.s = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(x.scales, sg.vs + 4 * (ke / 16), 0, 0));
+  } else {
+    f.c = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x.codes, sg.vc + ke / 2, 0, 0));
+    f.s = __builtin_amdgcn_raw_buffer_load_b16(x.scales, sg.vs + ke / 16, 0, 0);
+  }
+}
+
+// Four E4M3 codes (one dword) times fp32 scale s times the token's power of two
+// pw, each product one rounding, split into fp16 hi and lo parts.
+__device__ __forceinline__ void fp8x4_hilo(uint32_t w, float s, float pw, uint2& hi, uint2& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const float v = __fmul_rn(__fmul_rn(e4m3_to_f32((w >> (8 * b)) & 0xFFu), s), pw);
+    const _Float16 vh = (_Float16)v;
+    h[b] = __builtin_bit_cast(uint16_t, vh);
+    l[b] = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)vh));   // v - hi is exact in fp32
+  }
+  hi = make_uint2(h[0] | h[1] << 16, h[2] | h[3] << 16);
+  lo = make_uint2(l[0] | l[1] << 16, l[2] | l[3] << 16);
+}
+
+template <int MODE>
+__device__ __forceinline__ void stage_chunk(uint8_t* buf, const XFrag<MODE>& f, const Stager& sg, float pw) {
   if (!sg.on) return;
-  f16x2 s0, s1;
-  scale_pair(f.s, s0, s1);
   uint4* d = reinterpret_cast<uint4*>(buf + (sg.sm * kWideTok + sg.sn) * kTokStride + 64 * sg.sq);
-  d[0] = bitcast<uint4>(expand8(f.c.x, s0));
-  d[1] = bitcast<uint4>(expand8(f.c.y, s0));
-  d[2] = bitcast<uint4>(expand8(f.c.z, s1));
-  d[3] = bitcast<uint4>(expand8(f.c.w, s1));
+  if constexpr (MODE == MOE_A16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d[q] = f.v[q];
+  } else if constexpr (MODE == MOE_A8) {
+    uint4* dl = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(d) + kWideTok * kTokStride);   // plane 1
+    const float s0 = __uint_as_float(f.s.x), s1 = __uint_as_float(f.s.y);
+    const uint32_t w[8] = {f.c[0].x, f.c[0].y, f.c[0].z, f.c[0].w, f.c[1].x, f.c[1].y, f.c[1].z, f.c[1].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint2 h0, l0, h1, l1;
+      fp8x4_hilo(w[2 * q], q < 2 ? s0 : s1, pw, h0, l0);
+      fp8x4_hilo(w[2 * q + 1], q < 2 ? s0 : s1, pw, h1, l1);
+      d[q] = make_uint4(h0.x, h0.y, h1.x, h1.y);
+      dl[q] = make_uint4(l0.x, l0.y, l1.x, l1.y);
+    }
+  } else {
+    f16x2 s0, s1;
+    scale_pair(f.s, s0, s1);
+    d[0] = bitcast<uint4>(expand8(f.c.x, s0));
+    d[1] = bitcast<uint4>(expand8(f.c.y, s0));
+    d[2] = bitcast<uint4>(expand8(f.c.z, s1));
+    d[3] = bitcast<uint4>(expand8(f.c.w, s1));
+  }
 }
 
 // w: the wave's 16 weight rows, lane offsets wc/ws; x: the chunk's activation
-// rows; m: the wave's matrix (which LDS plane its B operands come from).
-template <int NM, int NT>
+// rows; m: the wave's matrix (4-bit gate/up: which LDS plane its B operands come
+// from; the 8-bit mode reads planes 0 and 1 into the same sums).
+template <int MODE, int NM, int NT>
 __device__ __forceinline__ void wide_mainloop(const Rows& w, int wc, int ws_row, const Rows& x,
                                               const Stager& sg, int m, int K, WideLds<NM>& lds,
-                                              f32x4 (&acc)[kWideTiles]) {
+                                              f32x4 (&acc)[kWideTiles], float pw) {
   const int lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
   const int nsteps = K / kKStep, nchunks = (nsteps + 1) / 2;
   const int nwin = (nsteps + kBody - 1) / kBody;
+  constexpr int kB = MODE == MOE_A8 ? 2 : 1;   // LDS planes per MFMA operand
 #pragma unroll
   for (int t = 0; t < kWideTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint4 fw[kWSets];
-  Frag fx[2];
-  load_chunk(fx[0], x, sg, 0);
-  load_chunk(fx[1], x, sg, min(1, nchunks - 1));
+  XFrag<MODE> fx[2];
+  load_chunk<MODE>(fx[0], x, sg, 0);
+  load_chunk<MODE>(fx[1], x, sg, min(1, nchunks - 1));
   uint4 sw = load_wscales(w, ws_row, g, 0), swn;
 #pragma unroll
   for (int d = 0; d < kWSets - 1; ++d) fw[d] = load_wcodes(w, wc, min(d, nsteps - 1));
-  stage_chunk(lds.buf, fx[0], sg);
+  stage_chunk<MODE>(lds.buf, fx[0], sg, pw);
   __syncthreads();
 
   // step s = s0 + u of the body (one scale window): chunk s / 2, LDS buffer and
@@ -279,27 +384,29 @@ __device__ __forceinline__ void wide_mainloop(const Rows& w, int wc, int ws_row,
     constexpr int cb = (u / 2) % 2;
     const int s = s0 + u;
     if constexpr (u == 0) swn = load_wscales(w, ws_row, g, min(s0 / kBody + 1, nwin - 1));
-    if constexpr (u % 2 == 0)   // first step of a chunk: raw codes of the chunk after next
-      load_chunk(fx[cb], x, sg, min(s / 2 + 2, nchunks - 1));
+    if constexpr (u % 2 == 0)   // first step of a chunk: raw activations of the chunk after next
+      load_chunk<MODE>(fx[cb], x, sg, min(s / 2 + 2, nchunks - 1));
     fw[(u + kWSets - 1) % kWSets] = load_wcodes(w, wc, min(s + kWSets - 1, nsteps - 1));
     __builtin_amdgcn_sched_barrier(0);   // the loads go out before the compute below
     if (s < nsteps) {
-      f16x8 av[4];
-      expand_frag(fw[u % kWSets], window_scales<u>(sw, lane), av);
-      const uint8_t* bm = lds.buf + cb * WideLds<NM>::kBuf + m * kWideTok * kTokStride +
+      WideOp<MODE> av[4];
+      expand_frag<MODE>(fw[u % kWSets], window_scales<u>(sw, lane), av);
+      const uint8_t* bm = lds.buf + cb * WideLds<NM>::kBuf + (MODE == MOE_A4 ? m : 0) * kWideTok * kTokStride +
                           (u % 2) * (kKStep * 2) + 64 * g;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f16x8 bv =
-              bitcast<f16x8>(*reinterpret_cast<const uint4*>(bm + (16 * t + r) * kTokStride + 16 * j));
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[j], bv, acc[t], 0, 0, 0);
+#pragma unroll
+          for (int b = 0; b < kB; ++b) {
+            const uint4 bv = *reinterpret_cast<const uint4*>(bm + (b * kWideTok + 16 * t + r) * kTokStride + 16 * j);
+            acc[t] = wide_mfma<MODE>(av[j], bv, acc[t]);
+          }
         }
       }
     }
     if constexpr (u % 2 == 1) {   // last step of a chunk: stage the next chunk, then sync
-      stage_chunk(lds.buf + (cb ^ 1) * WideLds<NM>::kBuf, fx[cb ^ 1], sg);
+      stage_chunk<MODE>(lds.buf + (cb ^ 1) * WideLds<NM>::kBuf, fx[cb ^ 1], sg, pw);
       __syncthreads();
     }
     if constexpr (u == kBody - 1) sw = swn;   // issued 8 steps ago
@@ -318,30 +425,64 @@ __device__ __forceinline__ void by_tiles(int ntt, F&& f) {
     f(std::integral_constant<int, 2>{});
 }
 
-// Staging share of thread tid for a chunk of np tokens (ntt tiles computed) in
-// NM matrices; activation row of (token, matrix) = token * NM + matrix.
-template <int NM>
-__device__ __forceinline__ Stager make_stager(int np, int ntt, int K) {
+// Staging share of thread tid for a chunk of np tokens (ntt tiles computed).
+// 4-bit gate/up: NM planes, activation row (token, matrix) = token * NM + matrix
+// of the chunk's rows; otherwise one row per token (plane 0 threads stage it,
+// the 8-bit mode into both planes), at row_of(token of the chunk) of the source.
+template <int MODE, int NM, typename RowOf>
+__device__ __forceinline__ Stager make_stager(int np, int ntt, int K, RowOf&& row_of) {
   Stager sg;
   sg.sm = threadIdx.x / (kWideTok * 8);
   sg.sn = (threadIdx.x / 8) % kWideTok;
   sg.sq = threadIdx.x % 8;
-  const int row = min(sg.sn, np - 1) * NM + min(sg.sm, NM - 1);
-  sg.vc = row * (K / 2);
-  sg.vs = row * (K / 16);
   sg.K = K;
-  sg.on = sg.sn < 16 * ntt && sg.sm < NM;   // threads past NM planes only wait at the barriers
+  if constexpr (MODE == MOE_A4) {
+    const int row = min(sg.sn, np - 1) * NM + min(sg.sm, NM - 1);
+    sg.vc = row * (K / 2);
+    sg.vs = row * (K / 16);
+    sg.on = sg.sn < 16 * ntt && sg.sm < NM;   // threads past NM planes only wait at the barriers
+  } else {
+    const int row = row_of(min(sg.sn, np - 1));
+    sg.vc = MODE == MOE_A16 ? row * K * 2 : row * K;
+    sg.vs = row * (K / 16) * 4;
+    sg.sm = 0;
+    sg.on = sg.sn < 16 * ntt && threadIdx.x < kWideTok * 8;
+  }
   return sg;
+}
+
+// 8-bit mode: a power of two per token of the chunk that keeps its activations
+// below 2^14 in magnitude (so their fp16 hi parts are finite; 1 for ordinary
+// data), from the row's block scales (fp32 [rows][K/16]; amax <= 448 * scale):
+// the staging multiplies by pw[n], the epilogue by 1 / pw[n] (both exact).
+template <int NWAVES, typename RowOf>
+__device__ __forceinline__ void token_pow2(const float* scales, int K, int np, RowOf&& row_of, float* pw) {
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  for (int n = wave; n < kWideTok; n += NWAVES) {
+    float mx = 0.0f;
+    if (n < np) {
+      const float* rs = scales + (size_t)row_of(n) * (K / 16);
+      for (int b = lane; b < K / 16; b += kWave) mx = __builtin_fmaxf(mx, rs[b]);
+    }
+    mx = wave_max(mx) * 448.0f;
+    // 2^(13 - floor(log2 mx)) from the exponent field (mx >= 2^14 is normal and finite here)
+    const int ex = (int)((__float_as_uint(mx) >> 23) & 0xFFu) - 127;
+    if (lane == 0) pw[n] = mx >= 16384.0f ? __uint_as_float((uint32_t)(13 - ex + 127) << 23) : 1.0f;
+  }
 }
 
 // ------------------------------------------------------------------ gate/up + SwiGLU + h
 // Workgroup: one chunk, 64 h rows i0 .. i0+63; wave w < 4: gate rows i0+16w ..
 // +15, wave w >= 4: the same up rows.  Rows past I (a ragged last row block)
-// read clamped rows and store nothing.
-__global__ void __launch_bounds__(512) k_gateup_wide_a4(FfnArgs a, const int4* __restrict__ plan,
-                                                        int slots) {
-  __shared__ WideLds<2> lds;
+// read clamped rows and store nothing.  The intermediate in the mode's
+// precision: bf16 (16-bit), E4M3 with an fp32 scale per 16 (8-bit), NVFP4
+// under the down matrix's input scale (4-bit); 16 rows of a wave are one block.
+template <int MODE>
+__global__ void __launch_bounds__(512) k_gateup_wide(FfnArgs a, const int4* __restrict__ plan, int slots) {
+  constexpr int NM = wide_planes<MODE, true>();
+  __shared__ WideLds<NM> lds;
   __shared__ float gbuf[kWideRows][kWideTok];   // gate * its multipliers, [h row][token]
+  __shared__ float s_pw[kWideTok];
   const Job job = wide_job(plan, (a.I + kWideRows - 1) / kWideRows, slots);
   if (job.e < 0) return;
   const int e = job.e, row0 = job.row0, np = job.ne;
@@ -354,26 +495,42 @@ __global__ void __launch_bounds__(512) k_gateup_wide_a4(FfnArgs a, const int4* _
   const bool on = i0 < I;
   const size_t row16 = (size_t)e * 2 * I + (size_t)m * I + (on ? i0 : I - 16);
   const Rows w = make_rows(a.gu_codes + row16 * (H / 2), a.gu_scales + row16 * (H / 16), 16, H);
-  const size_t xr0 = (size_t)row0 * 2;                      // the chunk's first activation row
-  const Rows x = make_rows(a.xq_codes + xr0 * (H / 2),
-                           static_cast<const uint8_t*>(a.xq_scales) + xr0 * (H / 16), 2 * np, H);
   const int ntt = (np + 15) / 16;
-  const Stager sg = make_stager<2>(np, ntt, H);
+  // activation rows: 4-bit, the chunk's pair rows (gate, up) of the quantized x;
+  // otherwise the tokens' rows of x (bf16 or E4M3 + fp32 scales)
+  auto tok_of = [&](int n) { return a.sorted_pairs[row0 + n] / a.k; };
+  Rows x;
+  if constexpr (MODE == MOE_A4) {
+    const size_t xr0 = (size_t)row0 * 2;
+    x = make_rows(a.xq_codes + xr0 * (H / 2), static_cast<const uint8_t*>(a.xq_scales) + xr0 * (H / 16), 2 * np, H);
+  } else if constexpr (MODE == MOE_A16) {
+    x = make_xrows<MODE>(a.x, nullptr, a.T, H);
+  } else {
+    x = make_xrows<MODE>(a.xq_codes, a.xq_scales, a.T, H);
+  }
+  const Stager sg = make_stager<MODE, NM>(np, ntt, H, tok_of);
+  float pw = 1.0f;
+  if constexpr (MODE == MOE_A8) {
+    token_pow2<8>(static_cast<const float*>(a.xq_scales), H, np, tok_of, s_pw);
+    __syncthreads();
+    pw = s_pw[sg.sn];
+  }
   f32x4 acc[kWideTiles];
   by_tiles(ntt, [&](auto NT) {
-    wide_mainloop<2, decltype(NT)::value>(w, r * (H / 2) + 16 * g, r * (H / 16), x, sg, m,
-                                          H, lds, acc);
+    wide_mainloop<MODE, NM, decltype(NT)::value>(w, r * (H / 2) + 16 * g, r * (H / 16), x, sg, m, H, lds, acc, pw);
   });
-  const float fm = a.gu_wscale[2 * e + m] * a.gu_inscale[2 * e + m];
+  const float fm = a.gu_wscale[2 * e + m] * (MODE == MOE_A4 ? a.gu_inscale[2 * e + m] : 1.0f);
+  float tok_f[kWideTiles];   // 8-bit mode: undo the token's power of two (exact)
+#pragma unroll
+  for (int t = 0; t < kWideTiles; ++t) tok_f[t] = MODE == MOE_A8 ? 1.0f / s_pw[16 * t + r] : 1.0f;
   if (m == 0) {
 #pragma unroll
     for (int t = 0; t < kWideTiles; ++t)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) gbuf[wr + 4 * g + q][16 * t + r] = acc[t][q] * fm;
+      for (int q = 0; q < 4; ++q) gbuf[wr + 4 * g + q][16 * t + r] = acc[t][q] * tok_f[t] * fm;
   }
   __syncthreads();
   if (m == 0 || !on) return;
-  const float gdn = a.dn_inscale[e];
 #pragma unroll
   for (int t = 0; t < kWideTiles; ++t) {
     if (t >= ntt) continue;
@@ -381,21 +538,42 @@ __global__ void __launch_bounds__(512) k_gateup_wide_a4(FfnArgs a, const int4* _
     float am = 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      h[q] = swiglu(gbuf[wr + 4 * g + q][16 * t + r], acc[t][q] * fm);
+      h[q] = swiglu(gbuf[wr + 4 * g + q][16 * t + r], acc[t][q] * tok_f[t] * fm);
       am = __builtin_fmaxf(am, __builtin_fabsf(h[q]));
     }
-    am = __builtin_fmaxf(am, __shfl_xor(am, 16, kWave));
-    am = __builtin_fmaxf(am, __shfl_xor(am, 32, kWave));
-    const uint32_t sc = f32_to_e4m3(__fdiv_rn(__fdiv_rn(am, 6.0f), gdn));
-    const float d = __fmul_rn(e4m3_to_f32(sc), gdn);
-    uint32_t nib = 0u;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) nib |= e2m1_under(h[q], d) << (4 * q);
     const int n = 16 * t + r;
-    if (n < np) {
-      const size_t row = (size_t)(row0 + n);
-      *reinterpret_cast<uint16_t*>(a.h_codes + row * (I / 2) + i0 / 2 + 2 * g) = (uint16_t)nib;
-      if (g == 0) static_cast<uint8_t*>(a.h_scales)[row * (I / 16) + i0 / 16] = (uint8_t)sc;
+    const size_t row = (size_t)(row0 + n);
+    if constexpr (MODE == MOE_A16) {
+      if (n < np) {
+        const uint32_t b0 = f32_to_bf16(h[0]) | f32_to_bf16(h[1]) << 16, b1 = f32_to_bf16(h[2]) | f32_to_bf16(h[3]) << 16;
+        *reinterpret_cast<uint2*>(a.h_codes + (row * I + i0 + 4 * g) * 2) = make_uint2(b0, b1);
+      }
+      continue;
+    }
+    am = __builtin_fmaxf(am, __shfl_xor(am, 16, kWave));   // the 16 rows' amax (one block)
+    am = __builtin_fmaxf(am, __shfl_xor(am, 32, kWave));
+    if constexpr (MODE == MOE_A8) {   // as fp8_quant16: s = bamax / 448, codes E4M3(h / s)
+      const float sc = __fdiv_rn(am, 448.0f);
+      uint32_t cw = 0u;
+      if (sc > 0.0f) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cw |= f32_to_e4m3(__fdiv_rn(h[q], sc)) << (8 * q);
+      }
+      if (n < np) {
+        *reinterpret_cast<uint32_t*>(a.h_codes + row * I + i0 + 4 * g) = cw;
+        if (g == 0) static_cast<float*>(a.h_scales)[row * (I / 16) + i0 / 16] = sc;
+      }
+    } else {
+      const float gdn = a.dn_inscale[e];
+      const uint32_t sc = f32_to_e4m3(__fdiv_rn(__fdiv_rn(am, 6.0f), gdn));
+      const float d = __fmul_rn(e4m3_to_f32(sc), gdn);
+      uint32_t nib = 0u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) nib |= e2m1_under(h[q], d) << (4 * q);
+      if (n < np) {
+        *reinterpret_cast<uint16_t*>(a.h_codes + row * (I / 2) + i0 / 2 + 2 * g) = (uint16_t)nib;
+        if (g == 0) static_cast<uint8_t*>(a.h_scales)[row * (I / 16) + i0 / 16] = (uint8_t)sc;
+      }
     }
   }
 }
@@ -404,11 +582,12 @@ __global__ void __launch_bounds__(512) k_gateup_wide_a4(FfnArgs a, const int4* _
 // Workgroup: one chunk, 16 NW output rows (wave w: rows o0 = 16 NW rb + 16w .. +15).
 // Waves past the first four only wait at the staging barriers (the chunk's
 // activations need 256 staging threads).
-template <int NW>
-__global__ void __launch_bounds__(NW * kWave) k_down_wide_a4(FfnArgs a, const int4* __restrict__ plan,
-                                                            int slots) {
+template <int MODE, int NW>
+__global__ void __launch_bounds__(NW * kWave) k_down_wide(FfnArgs a, const int4* __restrict__ plan, int slots) {
   constexpr int kRows = 16 * NW;   // output rows of the workgroup: 16 per wave
-  __shared__ WideLds<1> lds;
+  constexpr int NM = wide_planes<MODE, false>();
+  __shared__ WideLds<NM> lds;
+  __shared__ float s_pw[kWideTok];
   const Job job = wide_job(plan, (a.H + kRows - 1) / kRows, slots);
   if (job.e < 0) return;
   const int e = job.e, row0 = job.row0, np = job.ne;
@@ -419,22 +598,33 @@ __global__ void __launch_bounds__(NW * kWave) k_down_wide_a4(FfnArgs a, const in
   const bool on = o0 < H;
   const size_t row16 = (size_t)e * H + (on ? o0 : H - 16);
   const Rows w = make_rows(a.dn_codes + row16 * (I / 2), a.dn_scales + row16 * (I / 16), 16, I);
-  const Rows x = make_rows(a.h_codes + (size_t)row0 * (I / 2),
-                           static_cast<const uint8_t*>(a.h_scales) + (size_t)row0 * (I / 16), np, I);
+  auto row_of = [&](int n) { return row0 + n; };
+  Rows x;
+  if constexpr (MODE == MOE_A4)
+    x = make_rows(a.h_codes + (size_t)row0 * (I / 2), static_cast<const uint8_t*>(a.h_scales) + (size_t)row0 * (I / 16),
+                  np, I);
+  else   // the rows of the whole intermediate; the stager offsets select the chunk's
+    x = make_xrows<MODE>(a.h_codes, a.h_scales, row0 + np, I);
   const int ntt = (np + 15) / 16;
-  const Stager sg = make_stager<1>(np, ntt, I);
+  const Stager sg = make_stager<MODE, NM>(np, ntt, I, row_of);
+  float pw = 1.0f;
+  if constexpr (MODE == MOE_A8) {
+    token_pow2<NW>(static_cast<const float*>(a.h_scales), I, np, row_of, s_pw);
+    __syncthreads();
+    pw = s_pw[sg.sn];
+  }
   f32x4 acc[kWideTiles];
   by_tiles(ntt, [&](auto NT) {
-    wide_mainloop<1, decltype(NT)::value>(w, r * (I / 2) + 16 * g, r * (I / 16), x, sg, 0,
-                                          I, lds, acc);
+    wide_mainloop<MODE, NM, decltype(NT)::value>(w, r * (I / 2) + 16 * g, r * (I / 16), x, sg, 0, I, lds, acc, pw);
   });
   if (!on) return;
-  const float f = a.dn_wscale[e] * a.dn_inscale[e];
+  const float f = a.dn_wscale[e] * (MODE == MOE_A4 ? a.dn_inscale[e] : 1.0f);
 #pragma unroll
   for (int t = 0; t < kWideTiles; ++t) {
     const int n = 16 * t + r;
     if (t < ntt && n < np) {
-      const float4 o = make_float4(acc[t][0] * f, acc[t][1] * f, acc[t][2] * f, acc[t][3] * f);
+      const float ft = MODE == MOE_A8 ? f / s_pw[n] : f;
+      const float4 o = make_float4(acc[t][0] * ft, acc[t][1] * ft, acc[t][2] * ft, acc[t][3] * ft);
       *reinterpret_cast<float4*>(a.y + (size_t)(row0 + n) * H + o0 + 4 * g) = o;
     }
   }
@@ -460,19 +650,28 @@ __global__ void __launch_bounds__(256) k_debug_plan(int cols, int n_entries, int
 
 size_t debug_wide_plan_bytes(int cols) { return (size_t)((cols + kWideTok - 1) / kWideTok) * sizeof(int4); }
 
-moe_status launch_debug_wide(const FfnArgs& a, void* plan_ws, hipStream_t s) {
+template <int MODE>
+static moe_status launch_down(const FfnArgs& a, const int4* plan, int n, const char* what, hipStream_t s) {
+  const int nrb = (a.H + kDownRows - 1) / kDownRows;
+  hipLaunchKernelGGL((k_down_wide<MODE, kDownWaves>), dim3(wide_grid(n, nrb)), dim3(kDownWaves * kWave), 0, s, a,
+                     plan, n);
+  return check_launch(what);
+}
+
+moe_status launch_debug_wide(const FfnArgs& a, moe_act_mode mode, void* plan_ws, hipStream_t s) {
   int4* plan = static_cast<int4*>(plan_ws);
   const int n = (a.T + kWideTok - 1) / kWideTok;
   hipLaunchKernelGGL(k_debug_plan, dim3((n + 255) / 256), dim3(256), 0, s, a.T, n, plan);
   moe_status st = check_launch("moe_debug_nvfp4_matmul (plan)");
   if (st != MOE_OK) return st;
-  const int nrb = (a.H + kDownRows - 1) / kDownRows;
-  hipLaunchKernelGGL(k_down_wide_a4<kDownWaves>, dim3(wide_grid(n, nrb)), dim3(kDownWaves * kWave), 0, s, a,
-                     plan, n);
-  return check_launch("moe_debug_nvfp4_matmul (wide)");
+  const char* what = "moe_debug_nvfp4_matmul (wide)";
+  if (mode == MOE_A16) return launch_down<MOE_A16>(a, plan, n, what, s);
+  if (mode == MOE_A8) return launch_down<MOE_A8>(a, plan, n, what, s);
+  return launch_down<MOE_A4>(a, plan, n, what, s);
 }
 
-moe_status launch_ffn_wide_a4(const FfnArgs& a, int stage_mask, void* plan_ws, hipStream_t s) {
+template <int MODE>
+static moe_status launch_wide(const FfnArgs& a, int stage_mask, void* plan_ws, hipStream_t s) {
   int4* plan = static_cast<int4*>(plan_ws);
   const int n = wide_plan_entries(a.T * a.k, a.E);
   if (stage_mask & 6) {
@@ -482,17 +681,18 @@ moe_status launch_ffn_wide_a4(const FfnArgs& a, int stage_mask, void* plan_ws, h
   }
   if (stage_mask & 2) {
     const int nrb = (a.I + kWideRows - 1) / kWideRows;
-    hipLaunchKernelGGL(k_gateup_wide_a4, dim3(wide_grid(n, nrb)), dim3(512), 0, s, a, plan, n);
+    hipLaunchKernelGGL(k_gateup_wide<MODE>, dim3(wide_grid(n, nrb)), dim3(512), 0, s, a, plan, n);
     moe_status st = check_launch("nvfp4_expert_ffn (wide gate/up)");
     if (st != MOE_OK) return st;
   }
-  if (stage_mask & 4) {
-    const int nrb = (a.H + kDownRows - 1) / kDownRows;
-    hipLaunchKernelGGL(k_down_wide_a4<kDownWaves>, dim3(wide_grid(n, nrb)), dim3(kDownWaves * kWave), 0, s,
-                       a, plan, n);
-    return check_launch("nvfp4_expert_ffn (wide down)");
-  }
+  if (stage_mask & 4) return launch_down<MODE>(a, plan, n, "nvfp4_expert_ffn (wide down)", s);
   return MOE_OK;
+}
+
+moe_status launch_ffn_wide(const FfnArgs& a, moe_act_mode mode, int stage_mask, void* plan_ws, hipStream_t s) {
+  if (mode == MOE_A16) return launch_wide<MOE_A16>(a, stage_mask, plan_ws, s);
+  if (mode == MOE_A8) return launch_wide<MOE_A8>(a, stage_mask, plan_ws, s);
+  return launch_wide<MOE_A4>(a, stage_mask, plan_ws, s);
 }
 
 }  // namespace moe

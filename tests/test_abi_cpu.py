@@ -155,7 +155,7 @@ def test_debug_matmul_validation():
     assert call(K=3000) == "MOE_E_SHAPE"
     assert call(cols=0) == "MOE_E_SHAPE"
     assert call(x=P4) == "MOE_E_ALIGN"
-    assert call(core=1) == "MOE_E_UNSUPPORTED"                           # wide core: 4-bit x
+    assert call(core=1, N=250) == "MOE_E_SHAPE"                          # wide core: N % 16
     a4 = dict(mode=moe.MOE_A4, x_scales=P16, inscale=P16)
     assert call(core=1, N=250, **a4) == "MOE_E_SHAPE"                    # N % 16
     assert call(core=1, K=3040, **a4) == "MOE_E_SHAPE"                   # K % 128

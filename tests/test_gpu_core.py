@@ -91,7 +91,9 @@ def _run(dev, core, mode, w, x, wscale=1.0, inscale=1.0):
 NARROW = [("A16", 256, 3072, 8), ("A16", 200, 4096, 13), ("A16", 70, 160, 1),
           ("A8", 256, 3072, 8), ("A8", 130, 512, 11),
           ("A4", 256, 3072, 8), ("A4", 200, 4096, 9), ("A4", 64, 96, 3)]
-WIDE = [("A4", 256, 3072, 40), ("A4", 128, 512, 1), ("A4", 3072, 512, 64), ("A4", 48, 4096, 33)]
+WIDE = [("A4", 256, 3072, 40), ("A4", 128, 512, 1), ("A4", 3072, 512, 64), ("A4", 48, 4096, 33),
+        ("A16", 256, 3072, 40), ("A16", 128, 512, 1), ("A16", 48, 4096, 33),
+        ("A8", 256, 3072, 40), ("A8", 128, 512, 1), ("A8", 48, 4096, 33)]
 
 
 @pytest.mark.parametrize("core,case", [(0, c) for c in NARROW] + [(1, c) for c in WIDE],
@@ -115,8 +117,9 @@ def test_core_exact_integer_sums(dev, core, case):
 
 
 @pytest.mark.parametrize("core,case", [(0, ("A16", 192, 3072, 8)), (0, ("A8", 192, 512, 5)),
-                                       (0, ("A4", 192, 3072, 8)), (1, ("A4", 192, 3072, 40))],
-                         ids=["narrow-A16", "narrow-A8", "narrow-A4", "wide-A4"])
+                                       (0, ("A4", 192, 3072, 8)), (1, ("A4", 192, 3072, 40)),
+                                       (1, ("A16", 192, 3072, 40)), (1, ("A8", 192, 512, 40))],
+                         ids=["narrow-A16", "narrow-A8", "narrow-A4", "wide-A4", "wide-A16", "wide-A8"])
 def test_core_scaled_matches_oracle(dev, core, case):
     """Random block scales and multipliers: the fp32 result within the fp32
     accumulation bound of the oracle's dequantized double product."""

@@ -360,12 +360,13 @@ def test_layer_is_deterministic(dev):
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
+@pytest.mark.parametrize("mode", ["A4", "A16", "A8"])
 @pytest.mark.parametrize("H,I", [(256, 128), (384, 256), (640, 384), (96, 160), (3072, 512)])
-def test_expert_ffn_wide_hot_expert(dev, H, I):
-    """4-bit calls wider than 8 tokens take the MFMA path when H and I are
-    multiples of 128 (K loops of 1-5 and 24 steps), the one-column kernels
-    otherwise (96, 160): one expert with more than 128 tokens (several passes),
-    others with a few, one with none."""
+def test_expert_ffn_wide_hot_expert(dev, H, I, mode):
+    """Calls wider than 8 tokens take the MFMA path when H and I are multiples of
+    128 (K loops of 1-5 and 24 steps), the one-column kernels otherwise (96,
+    160): one expert with more than 128 tokens (several passes), others with a
+    few, one with none; in each activation mode."""
     E, k, T = 6, 2, 300
     w = _small_workload(20 + H % 7, E, k, H, I, T)
     ins = _inscales_for(E, 21)
@@ -377,11 +378,12 @@ def test_expert_ffn_wide_hot_expert(dev, H, I):
     ids = np.stack([[0, int(rng.choice([1, 2, 3, 5], p=[0.6, 0.3, 0.05, 0.05]))] for _ in range(T)]).astype(np.int32)
     p = OL.permute(ids, E)
     assert np.diff(p.offsets)[0] == T and np.diff(p.offsets)[4] == 0
-    say("ffn wide", H, I, np.diff(p.offsets))
-    y, wsb = moe.nvfp4_expert_ffn(experts, "A4", bf16_dev(x, dev), k, to_dev(p.offsets, dev),
+    say("ffn wide", mode, H, I, np.diff(p.offsets))
+    y, wsb = moe.nvfp4_expert_ffn(experts, mode, bf16_dev(x, dev), k, to_dev(p.offsets, dev),
                                   to_dev(p.sorted_pairs, dev))
-    views = {n: host(v) for n, v in moe.ffn_workspace_views(wsb, "A4", T, k, H, I).items()}
-    parity.check_experts(w, "A4", x, cache, k, p.offsets, p.sorted_pairs, host(y), views)
+    views = {n: host(v) for n, v in moe.ffn_workspace_views(wsb, mode, T, k, H, I).items()}
+    _, info = parity.check_experts(w, mode, x, cache, k, p.offsets, p.sorted_pairs, host(y), views)
+    say("ok", info["y_worst_rel"], info["ties"])
     if H % 128 == 0 and I % 128 == 0:
         # the work plan: each expert's rows in chunks of at most 32, experts in order
         want = [(e, r0, min(32, p.offsets[e + 1] - r0)) for e in range(E)

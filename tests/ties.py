@@ -145,7 +145,9 @@ def expected_intermediate(res, mode, gpu, dn_inscale=None, report=None):
         fl = (codes_g != nom_g).reshape(n, I)
         rep.flipped += int(np.sum(fl))
         rep.block_scale_flips += int(np.sum(s_g != nom_s.astype(np.float64)))
-        rep.row_flips = np.any(fl, axis=1)
+        # rows whose stored codes differ from the oracle's own (also where only the
+        # fp32 scale's last bit moved a code across a midpoint): no unique result
+        rep.row_flips = np.any(fl | (codes_g.reshape(n, I) != nom_c), axis=1)
     else:
         g_in = np.float64(np.float32(dn_inscale))
         codes_g = F.unpack_nibbles(np.asarray(gpu[0], np.uint8)).reshape(n, I // 16, 16)
