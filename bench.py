@@ -233,7 +233,7 @@ def stack_step(w, mode, layers, x0, ws, steps, warmup, depth=48):
     """One decode step through `depth` stacked layers (the layer copies cycled),
     each layer's output plus its input feeding the next, timed eagerly and as a
     replayed HIP graph of the whole step (the layer calls are single-launch
-    kernels in both; under capture each is preceded by its epoch kernel)."""
+    kernels in both; each is one node of the captured graph)."""
     import torch
     import nvfp4_block_scaled_softmax_amd as moe
     bufs = [torch.empty_like(x0) for _ in range(2)]

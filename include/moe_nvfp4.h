@@ -294,14 +294,14 @@ moe_status moe_layer_status(const void* ws, hipStream_t s);
  * to 8 tokens, H/32 in 33..128, I/32 in 5..32), else 0 (per-stage kernels). */
 int moe_layer_is_fused(int T, int H, int I);
 
-/* Kernel launches of one moe_layer_forward call on a stream that is not being
- * captured into a graph: 1 for the single-launch decode layer (fused sizes,
- * MOE_A16, T*k <= 64), 2 or 3 for the fused two-kernel path (routing, for
- * MOE_A8 the activation quantizer, experts + combine; MOE_A4 quantizes x in
- * the expert kernel's gate/up tiles), 0 when the per-stage
- * kernels run.  Under capture the single-launch case is preceded by a
- * one-thread kernel that advances the call's number in the workspace (a number
- * baked into the launch would repeat on every replay): 2 launches. */
+/* Kernel launches of one moe_layer_forward call: 1 for the single-launch
+ * decode layer (fused sizes, MOE_A16 with NVFP4 experts, T*k <= 64), 2 or 3
+ * for the fused two-kernel path (routing, for MOE_A8 the activation
+ * quantizer, experts + combine; MOE_A4 quantizes x in the expert kernel's
+ * gate/up tiles; q4_g64_fp16 experts take this path), 0 when the per-stage
+ * kernels run.  Under stream capture the single-launch layer is one graph node
+ * too: it then takes its call number from the workspace and advances it itself
+ * (a number baked into the launch would repeat on every replay). */
 int moe_layer_launches(moe_act_mode mode, int T, int k, int H, int I);
 size_t moe_layer_workspace_bytes(moe_act_mode mode, int T, int k, int E, int H, int I);
 moe_status moe_layer_forward(const moe_nvfp4_experts* w, moe_act_mode mode, const uint16_t* x,

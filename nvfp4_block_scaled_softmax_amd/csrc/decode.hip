@@ -61,6 +61,10 @@ namespace moe {
 constexpr int kDecMaxSlots = 512;     // active experts of a call: at most T * k <= 8 * 64
 constexpr int kDecMaxRowBlocks = kMaxDim / kDnRows;
 constexpr int kSmallP = 64;           // up to this many pairs the routing tail ranks them directly
+// Arrival counters of a captured call: one per 128-byte line, workgroup i
+// counting on line i % kArrivalLines, so that ~2000 adds at the start of a
+// launch do not queue on one address.
+constexpr int kArrivalLines = 64;
 
 // Each counter sits on its own 128-byte line: many workgroups poll or bump them
 // at once, and counters sharing a line would queue behind each other.
@@ -72,8 +76,11 @@ struct alignas(128) Counter {
 struct DecodeState {
   Counter route_done;                  // A: workgroups finished
   Counter timeouts;                    // waits that gave up: the abort word (stays 0)
-  Counter dev_epoch;                   // single launch under graph capture: the call's epoch,
-                                       // advanced by k_epoch_bump before each call
+  Counter dev_epoch;                   // single launch under graph capture: the low 31 bits of
+                                       // the call's epoch, advanced by the call itself
+  Counter arrivals[kArrivalLines];     // single launch under graph capture: workgroups of the
+                                       // call that have read dev_epoch, spread over lines by
+                                       // workgroup index (reset by the call)
   Counter outs_epoch;                  // single launch: epoch of the call whose routing outputs
                                        // (ids, weights, sorted pairs, pair rows) are complete
   int32_t n_active;                    // active experts (written by A)
@@ -440,7 +447,7 @@ __global__ void __launch_bounds__(kTileThreads)
 // Up to kSmallP pairs: workgroups [0, R) compute the router logits (one expert
 // per wave), each published as a word stamped with this call's epoch (a number
 // not reused, never 0: from the host, or under graph capture from the device,
-// see k_epoch_bump); the last routing workgroup polls them and runs top-k and
+// see below); the last routing workgroup polls them and runs top-k and
 // the permutation; the expert tiles follow.  It publishes each slot's plan
 // entry stamped with the epoch; expert tiles poll their slot's entry until the
 // stamp matches.  An entry and its stamp are one 64-bit word, written and
@@ -469,11 +476,25 @@ __global__ void __launch_bounds__(kTileThreads)
                    uint16_t* __restrict__ out, uint32_t epoch_arg, uint32_t dn_hold,
                    const float* __restrict__ shared_y) {
   extern __shared__ __align__(16) uint8_t lds[];
-  // epoch_arg 0: the epoch is in the workspace, advanced by k_epoch_bump just
-  // before this kernel (complete at the kernel boundary, the same for every
-  // workgroup)
-  const uint32_t epoch = epoch_arg != 0u ? epoch_arg
-                                         : __hip_atomic_load(&st->dev_epoch.v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // epoch_arg 0 (a call recorded into a graph, where an epoch baked into the
+  // launch would repeat on every replay): the epoch is 2^31 | dev_epoch (never 0
+  // and never a host epoch, whose top bit is clear).  Every workgroup reads it
+  // first and then counts itself in `arrivals` (an add whose result nobody waits
+  // for); once all have arrived, the routing tail advances dev_epoch for the
+  // next call and resets the count.  No workgroup reads dev_epoch after its
+  // start, so every workgroup of the call holds the same epoch, and the next call
+  // (a later kernel on the stream) sees the advanced one: the captured layer is
+  // one graph node.
+  uint32_t epoch = epoch_arg;
+  if (epoch_arg == 0u) {
+    const uint32_t v = __hip_atomic_load(&st->dev_epoch.v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+      wait_vmem();   // the read has returned before the arrival is counted
+      __hip_atomic_fetch_add(&st->arrivals[blockIdx.x % kArrivalLines].v, 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+    epoch = 0x80000000u | (v & 0x7FFFFFFFu);
+  }
   __shared__ int pid[kSmallP];
   __shared__ int s_n;
   __shared__ int4 splan[kSmallP];
@@ -548,6 +569,20 @@ __global__ void __launch_bounds__(kTileThreads)
     wait_vmem();
     __syncthreads();
     if (tid == 0) __hip_atomic_store(&st->outs_epoch.v, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (epoch_arg == 0u && wave == 0) {   // the next captured call's epoch, once every workgroup holds this one
+      const int lane = lane_id();
+      Patience pat;
+      while (true) {
+        const uint32_t n = lane < kArrivalLines ? ld_relaxed(&st->arrivals[lane].v) : 0u;
+        const uint32_t total = (uint32_t)wave_sum((float)n);   // exact: counts below 2^24
+        if (total >= gridDim.x || pat.expired(&st->timeouts.v)) break;
+        __builtin_amdgcn_s_sleep(8);
+      }
+      if (lane < kArrivalLines)
+        __hip_atomic_store(&st->arrivals[lane].v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0)
+        __hip_atomic_store(&st->dev_epoch.v, (epoch + 1u) & 0x7FFFFFFFu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     return;
   }
   expert_tiles<MODE, GL, GC, DL, DC>(
@@ -575,19 +610,6 @@ __global__ void __launch_bounds__(kTileThreads)
         __syncthreads();
         return s_pl;
       });
-}
-
-// The epoch of a single-launch call made under graph capture, where a number
-// baked into the launch would repeat on every replay: one thread advances the
-// workspace's device epoch (top bit set, so it never equals a host epoch, which
-// keeps the top bit clear; never 0), and the layer kernel that follows reads it.
-__global__ void __launch_bounds__(kWave) k_epoch_bump(DecodeState* __restrict__ st) {
-  if (threadIdx.x == 0) {
-    const uint32_t v = __hip_atomic_load(&st->dev_epoch.v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t c = (v & 0x7FFFFFFFu) + 1u;
-    __hip_atomic_store(&st->dev_epoch.v, 0x80000000u | (c > 0x7FFFFFFFu ? 1u : c), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  }
 }
 
 // ------------------------------------------------------------------ launch
@@ -739,7 +761,7 @@ moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, in
   moe_status r;
   if (stage_mask == 3 && single_launch(mode, T, k)) {
     // one launch; under graph capture, where a replay would repeat an epoch baked
-    // into the launch, a one-thread kernel first advances a device-side epoch
+    // into the launch, epoch 0 makes the kernel use and advance the workspace's
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cs) != hipSuccess) return check_launch("moe_layer_forward (capture query)");
     {
@@ -747,10 +769,6 @@ moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, in
       uint64_t epoch = 0;   // 0: read the device epoch
       if (cs == hipStreamCaptureStatusNone) {
         do epoch = ++g_epoch & 0x7FFFFFFFu; while (epoch == 0u);   // 0: a never-written entry
-      } else {
-        hipLaunchKernelGGL(k_epoch_bump, dim3(1), dim3(kWave), 0, s, st);
-        moe_status rb = check_launch("moe_layer_forward (epoch)");
-        if (rb != MOE_OK) return rb;
       }
       if (E <= 64) launch_one<1>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shared_y, s);
       else if (E <= 128) launch_one<2>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shared_y, s);

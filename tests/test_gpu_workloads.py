@@ -336,11 +336,12 @@ def test_decode_tied_logits(dev, w, group):
 
 
 def test_decode_graph_replay(dev):
-    """Under stream capture the single-launch layer is recorded behind a
-    one-thread kernel that advances the call's epoch in the workspace (an epoch
-    baked into the launch would repeat on replay).  Three replays, each with
-    eager single-launch calls and a synchronisation before it, all equal the
-    eager result bit for bit."""
+    """Under stream capture the single-launch layer is recorded as one node that
+    takes its epoch from the workspace and advances it itself (an epoch baked
+    into the launch would repeat on replay).  Three replays, each with eager
+    single-launch calls and a synchronisation before it, all equal the eager
+    result bit for bit and pass the full oracle check; the graph holds one
+    kernel node per layer call."""
     w = synth.CONFIGS[1]
     ex, router, bias = gpu_layer(w, 0, "A16", dev)
     nws = moe.layer_workspace_bytes("A16", w.T, w.k, w.E, w.H, w.I)
@@ -353,6 +354,7 @@ def test_decode_graph_replay(dev):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         moe.moe_layer_forward(ex, "A16", x_g, router, w.k, ws=ws_g, out=out_g)
+    assert moe.layer_launches("A16", w.T, w.k, w.H, w.I) == 1
     for rep, batch in enumerate((1, 2, 3)):
         say("graph replay", rep, "batch", batch)
         x_new = bench.token_batch(w, batch, dev)
@@ -368,9 +370,9 @@ def test_decode_graph_replay(dev):
 
 def test_decode_graph_chain(dev):
     """Six chained single-launch layers (each output plus its input feeds the
-    next; two seeded layer copies alternate) captured as one graph on one
-    workspace, the epoch kernel ahead of each: three replays on fresh inputs,
-    each equal bit for bit to the same chain run eagerly on another workspace."""
+    next; two seeded layer copies alternate) captured as one graph of six nodes
+    on one workspace: three replays on fresh inputs, each equal bit for bit to
+    the same chain run eagerly on another workspace."""
     w = synth.CONFIGS[3]
     mode = "A16"
     layers = [gpu_layer_pair(w, l, mode, dev) for l in range(2)]
