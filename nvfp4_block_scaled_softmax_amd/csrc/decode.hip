@@ -223,6 +223,7 @@ __global__ void __launch_bounds__(kPermThreads)
   __shared__ int s_n;
   __shared__ int4 splan[kSmallP];
   __shared__ int s_last;
+  __shared__ TopkScratch s_topk[kPermWaves];
   const int tid = threadIdx.x, wave = tid / kWave;
   router_logits_wave<kPermThreads, true>(x, wr, bias, T, H, E, blockIdx.x * kPermWaves + wave,
                            reinterpret_cast<uint4*>(smem), logits);
@@ -238,7 +239,7 @@ __global__ void __launch_bounds__(kPermThreads)
   // ---- the last workgroup: every expert's logits are visible
   const int P = T * k;
   for (int t = wave; t < T; t += kPermWaves)
-    topk_wave<S, true>(logits, t, E, k, ids, tw, P <= kSmallP ? pid : nullptr);
+    topk_wave<S, true>(logits, t, E, k, ids, tw, P <= kSmallP ? pid : nullptr, &s_topk[wave]);
   __syncthreads();   // ids are written (same workgroup)
   if (P <= kSmallP) {
     const int n_act = rank_small<false>(pid, splan, &s_n, P, k, sorted_pairs, pair_row);
@@ -466,8 +467,12 @@ __global__ void __launch_bounds__(kTileThreads)
 // wave before it polls the logits, and it waits for those stores there (while
 // the other workgroups' logits are on their way), so they are complete before
 // any entry goes out.
+// Four workgroups per CU must fit for the whole grid of a one-token call to be
+// resident at once: at most 128 VGPRs (four waves per SIMD), which the shapes
+// up to H = 3072 and E = 512 meet without spilling; wider ones are left to the
+// compiler's choice.
 template <int S, int MODE, int GL, int GC, int DL, int DC>
-__global__ void __launch_bounds__(kTileThreads)
+__global__ void __launch_bounds__(kTileThreads, (GC <= 3 && S <= 8) ? 4 : 1)
     k_layer_decode(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                    const float* __restrict__ bias, float* __restrict__ logits,
                    int32_t* __restrict__ ids, float* __restrict__ tw, FfnArgs a,
@@ -501,6 +506,7 @@ __global__ void __launch_bounds__(kTileThreads)
   __shared__ SlotPlan s_pl;
   __shared__ float s_tw[kSmallP];
   __shared__ int s_sorted[kSmallP], s_prow[kSmallP];
+  __shared__ TopkScratch s_topk[kTileWaves];
   const int tid = threadIdx.x, wave = tid / kWave;
   const int T = a.T, H = a.H, E = a.E, k = a.k, P = T * k;
   const int R = (E + kTileWaves - 1) / kTileWaves;
@@ -545,7 +551,7 @@ __global__ void __launch_bounds__(kTileThreads)
 #pragma unroll
       for (int i = 0; i < S; ++i)
         key[i] = lane * S + i < E ? order_key(__builtin_bit_cast(float, (uint32_t)(v[i] >> 32))) : kNoKey;
-      topk_keys<S, true>(key, t, k, nullptr, nullptr, pid, s_tw);
+      topk_keys<S, true>(key, t, k, nullptr, nullptr, pid, s_tw, &s_topk[wave]);
     }
     __syncthreads();
     const int n_act = rank_small<true>(pid, splan, &s_n, P, k, nullptr, nullptr, s_sorted, s_prow);

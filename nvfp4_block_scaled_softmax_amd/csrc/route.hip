@@ -111,8 +111,9 @@ template <int S>
 __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits, int T, int E,
                                               int k, int32_t* __restrict__ ids,
                                               float* __restrict__ w) {
+  __shared__ TopkScratch sc[4];
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (t < T) topk_wave<S>(logits, t, E, k, ids, w);
+  if (t < T) topk_wave<S>(logits, t, E, k, ids, w, nullptr, &sc[threadIdx.x / kWave]);
 }
 
 static void launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,

@@ -113,11 +113,138 @@ __device__ __forceinline__ int wave_max_key(int v) {
 // [t][k] layout), for a caller that works on them within the workgroup; with
 // ids and w null they go to LDS only.
 constexpr int kNoKey = (int)0x80000000;   // below every key of a finite value
+
+// Candidate selection before the rounds.  Let L be the k-th largest of the 64
+// lanes' maxima: at least k keys are >= L, so every one of the k largest keys
+// is >= L (the candidates), and any key larger than a candidate is itself a
+// candidate: a candidate's rank among the candidates (by key descending, then
+// index ascending) is its rank among all keys.  Each candidate's rank is
+// counted against every other candidate from LDS in parallel (typically a few
+// dozen candidates, no serial rounds), and the k smallest ranks are the
+// selection in order.  More than kTopkCand candidates (many equal keys) take
+// the rounds below instead; both give the same selection.
+constexpr int kTopkCand = 128;
+struct TopkScratch {
+  int lmax[kWave];                         // the lanes' maxima
+  unsigned long long cand[kTopkCand];      // the candidates, then the selection in rank order
+};
+
+// Keys as one ordered 64-bit word: larger key first, then lower index.
+__device__ __forceinline__ unsigned long long topk_composite(int key, int index) {
+  return (unsigned long long)((unsigned)key ^ 0x80000000u) << 32 | (0xFFFFFFFFu - (unsigned)index);
+}
+
+// Orders this wave's LDS writes before its later LDS reads by other lanes (LDS
+// requests of one wave are served in issue order; the compiler must not move
+// the accesses across).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+}
+
+// The chosen experts' weights (lane j < k holds the j-th choice): renormalised
+// softmax over the chosen logits, exp(l_j - l_max) / sum, and the stores.
+template <bool COH>
+__device__ __forceinline__ void topk_weights(int t, int k, int sel_k, int sel_i, int first_k,
+                                             int32_t* __restrict__ ids, float* __restrict__ w, int* lds_ids,
+                                             float* lds_w) {
+  const int lane = lane_id();
+  const float ex = lane < k ? expf(key_value(sel_k) - key_value(first_k)) : 0.0f;
+  const float sum = wave_sum(ex);
+  if (lane < k) {
+    const float wt = __fdiv_rn(ex, sum);
+    if (ids) hst32<COH>(ids, 4 * ((size_t)t * k + lane), (uint32_t)sel_i);
+    if (w) hst32<COH>(w, 4 * ((size_t)t * k + lane), __builtin_bit_cast(uint32_t, wt));
+    if (lds_ids) lds_ids[t * k + lane] = sel_i;
+    if (lds_w) lds_w[t * k + lane] = wt;
+  }
+}
+
+// Exclusive prefix over the wave's lanes of c (0 <= c < 2^BITS) and its total,
+// from one ballot per bit of c and lane-mask counts: no memory round trips.
+template <int BITS>
+__device__ __forceinline__ int wave_prefix(int c, int& total) {
+  int pre = 0;
+  total = 0;
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) {
+    const unsigned long long m = __ballot((c >> b) & 1);
+    pre += (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u)) << b;
+    total += __popcll(m) << b;
+  }
+  return pre;
+}
+
+// Returns false (nothing written) when there are more than kTopkCand candidates.
+template <int S>
+__device__ __forceinline__ bool topk_by_rank(const int* key, int k, TopkScratch* sc, int& sel_k, int& sel_i,
+                                             int& first_k) {
+  static_assert(S <= 31, "a lane's candidate count must fit five bits");
+  const int lane = lane_id();
+  int m = key[0];
+#pragma unroll
+  for (int i = 1; i < S; ++i) m = max(m, key[i]);
+  sc->lmax[lane] = m;
+  wave_lds_sync();
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int q = 0; q < kWave; q += 4) {   // 16 reads in flight together
+    const int4 v = *reinterpret_cast<const int4*>(&sc->lmax[q]);
+    gt += (v.x > m) + (v.y > m) + (v.z > m) + (v.w > m);
+    eq += (v.x == m) + (v.y == m) + (v.z == m) + (v.w == m);
+  }
+  // L: the maxima in descending order, position k - 1 (the lanes whose maximum sits there)
+  const unsigned long long at = __ballot(gt <= k - 1 && k - 1 < gt + eq);
+  const int L = __builtin_amdgcn_readlane(m, __ffsll((long long)at) - 1);
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < S; ++i) c += key[i] >= L;
+  int total;
+  int pos = wave_prefix<S < 16 ? 4 : 5>(c, total);
+  if (total > kTopkCand) return false;
+#pragma unroll
+  for (int i = 0; i < S; ++i)
+    if (key[i] >= L) sc->cand[pos++] = topk_composite(key[i], lane * S + i);
+  const int padded = (total + 15) & ~15;   // zero composites rank below every candidate
+  if (lane < padded - total) sc->cand[total + lane] = 0ull;
+  wave_lds_sync();
+  const int j0 = lane, j1 = lane + kWave;
+  const unsigned long long c0 = j0 < total ? sc->cand[j0] : 0ull;
+  const unsigned long long c1 = j1 < total ? sc->cand[j1] : 0ull;
+  int r0 = 0, r1 = 0;
+  for (int q0 = 0; q0 < padded; q0 += 16) {
+    unsigned long long v[16];
+#pragma unroll
+    for (int q = 0; q < 16; q += 2) {    // 8 reads in flight together
+      const ulonglong2 p = *reinterpret_cast<const ulonglong2*>(&sc->cand[q0 + q]);
+      v[q] = p.x;
+      v[q + 1] = p.y;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      r0 += v[q] > c0;
+      r1 += v[q] > c1;
+    }
+  }
+  wave_lds_sync();   // every lane has read the candidates
+  if (j0 < total && r0 < k) sc->cand[r0] = c0;
+  if (j1 < total && r1 < k) sc->cand[r1] = c1;
+  wave_lds_sync();
+  const unsigned long long sel = sc->cand[lane < k ? lane : 0];
+  sel_k = (int)((unsigned)(sel >> 32) ^ 0x80000000u);
+  sel_i = (int)(0xFFFFFFFFu - (unsigned)sel);
+  first_k = __builtin_amdgcn_readfirstlane(sel_k);
+  wave_lds_sync();   // the next token of this wave writes the scratch again
+  return true;
+}
+
 template <int S, bool COH = false>
 __device__ __forceinline__ void topk_keys(const int* key, int t, int k, int32_t* __restrict__ ids,
                                           float* __restrict__ w, int* lds_ids = nullptr,
-                                          float* lds_w = nullptr) {
+                                          float* lds_w = nullptr, TopkScratch* sc = nullptr) {
   const int lane = lane_id();
+  int sel_k = 0, sel_i = 0, first_k = 0;
+  if (!(sc && topk_by_rank<S>(key, k, sc, sel_k, sel_i, first_k))) {
   long long c[S];
 #pragma unroll
   for (int i = 0; i < S; ++i)
@@ -133,7 +260,6 @@ __device__ __forceinline__ void topk_keys(const int* key, int t, int k, int32_t*
       c[i + 1] = sw ? a : b;
     }
   }
-  int sel_k = 0, sel_i = 0, first_k = 0;
   for (int j = 0; j < k; ++j) {
     const int hk = (int)(c[0] >> 32);
     const int m = wave_max_key(hk);
@@ -149,23 +275,15 @@ __device__ __forceinline__ void topk_keys(const int* key, int t, int k, int32_t*
     sel_k = lane == j ? m : sel_k;
     sel_i = lane == j ? wl * S + slot : sel_i;
   }
-  // renormalised softmax over the chosen logits: exp(l_j - l_max) / sum
-  const float ex = lane < k ? expf(key_value(sel_k) - key_value(first_k)) : 0.0f;
-  const float sum = wave_sum(ex);
-  if (lane < k) {
-    const float wt = __fdiv_rn(ex, sum);
-    if (ids) hst32<COH>(ids, 4 * ((size_t)t * k + lane), (uint32_t)sel_i);
-    if (w) hst32<COH>(w, 4 * ((size_t)t * k + lane), __builtin_bit_cast(uint32_t, wt));
-    if (lds_ids) lds_ids[t * k + lane] = sel_i;
-    if (lds_w) lds_w[t * k + lane] = wt;
   }
+  topk_weights<COH>(t, k, sel_k, sel_i, first_k, ids, w, lds_ids, lds_w);
 }
 
 // topk_keys over token t's row of fp32 logits [T][E] in memory.
 template <int S, bool COH = false>
 __device__ __forceinline__ void topk_wave(const float* __restrict__ logits, int t, int E, int k,
                                           int32_t* __restrict__ ids, float* __restrict__ w,
-                                          int* lds_ids = nullptr) {
+                                          int* lds_ids = nullptr, TopkScratch* sc = nullptr) {
   const int lane = lane_id();
   const float* row = logits + (size_t)t * E;
   int key[S];
@@ -175,7 +293,7 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ logits, int 
     const float x = __builtin_bit_cast(float, hld32<COH>(row, 4 * (size_t)(e < E ? e : E - 1)));   // masked below
     key[i] = e < E ? order_key(x) : kNoKey;
   }
-  topk_keys<S, COH>(key, t, k, ids, w, lds_ids);
+  topk_keys<S, COH>(key, t, k, ids, w, lds_ids, nullptr, sc);
 }
 
 }  // namespace moe
