@@ -156,22 +156,48 @@ __device__ int rank_small(const int* pid, int4* splan, int* s_n, int P, int k,
   if (tid < kWave) {
     const bool mine = lane < P;
     const int e = mine ? pid[lane] : 0x7FFFFFFF;
-    int lt = 0, eq_before = 0, n_eq = 0, tmask = 0;
-    for (int q = 0, tq = 0, jq = 0; q < P; ++q) {   // pair q is token tq's jq-th
-      const int f = __builtin_amdgcn_readlane(e, q);
-      lt += f < e;
-      eq_before += f == e && q < lane;
-      n_eq += f == e;
-      tmask |= (int)(f == e) << tq;
-      if (++jq == k) {
-        jq = 0;
-        ++tq;
+    // every lane reads the pairs' experts four at a time (one broadcast LDS
+    // read; entries past P are masked by the uniform index test)
+    int lt = 0, eq_before = 0, n_eq = 0, tmask = 0, first_lt = 0;
+    if (P == k) {   // one token: its experts are distinct, a pair's row is its expert's rank
+      for (int q0 = 0; q0 < P; q0 += 4) {
+        const int4 f = *reinterpret_cast<const int4*>(pid + q0);
+        lt += (f.x < e) + (q0 + 1 < P && f.y < e) + (q0 + 2 < P && f.z < e) + (q0 + 3 < P && f.w < e);
+      }
+      n_eq = 1;
+      tmask = 1;
+      first_lt = lt;
+    } else {
+      for (int q0 = 0, tq = 0, jq = 0; q0 < P; q0 += 4) {   // pair q is token tq's jq-th
+        const int4 f4 = *reinterpret_cast<const int4*>(pid + q0);
+        const int fv[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int q = q0 + u;
+          if (q < P) {
+            const bool eq = fv[u] == e;
+            lt += fv[u] < e;
+            eq_before += eq && q < lane;
+            n_eq += eq;
+            tmask |= (int)eq << tq;
+            if (++jq == k) {
+              jq = 0;
+              ++tq;
+            }
+          }
+        }
+      }
+      // distinct experts below e: the pairs that are their expert's first
+      const unsigned long long first = __ballot(mine && eq_before == 0);
+      for (int q0 = 0; q0 < P; q0 += 4) {
+        const int4 f4 = *reinterpret_cast<const int4*>(pid + q0);
+        const int fv[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (((first >> (q0 + u)) & 1ull) != 0ull) first_lt += fv[u] < e;
       }
     }
-    const unsigned long long first = __ballot(mine && eq_before == 0);   // each expert's first pair
-    int first_lt = 0;                                                    // distinct experts below e
-    for (int q = 0; q < P; ++q)
-      if ((first >> q) & 1ull) first_lt += __builtin_amdgcn_readlane(e, q) < e;
+    const unsigned long long firsts = __ballot(mine && eq_before == 0);   // (the whole wave takes part)
     if (mine) {
       const int row = lt + eq_before;
       if (sorted_pairs) {
@@ -183,7 +209,7 @@ __device__ int rank_small(const int* pid, int4* splan, int* s_n, int P, int k,
       }
       if (eq_before == 0) splan[first_lt] = make_int4(e, lt, n_eq, tmask);
     }
-    if (lane == 0) *s_n = __popcll(first);
+    if (lane == 0) *s_n = __popcll(firsts);
   }
   __syncthreads();
   return *s_n;
@@ -219,7 +245,7 @@ __global__ void __launch_bounds__(kPermThreads)
   __shared__ int rank[kMaxExperts];
   __shared__ int wcnt[kPermWaves][kMaxExperts];
   __shared__ int wave_tot[kPermWaves];
-  __shared__ int pid[kSmallP];
+  __shared__ __align__(16) int pid[kSmallP];   // 16-byte aligned: rank_small reads it four at a time
   __shared__ int s_n;
   __shared__ int4 splan[kSmallP];
   __shared__ int s_last;
@@ -500,7 +526,7 @@ __global__ void __launch_bounds__(kTileThreads, (GC <= 3 && S <= 8) ? 4 : 1)
     }
     epoch = 0x80000000u | (v & 0x7FFFFFFFu);
   }
-  __shared__ int pid[kSmallP];
+  __shared__ __align__(16) int pid[kSmallP];   // 16-byte aligned: rank_small reads it four at a time
   __shared__ int s_n;
   __shared__ int4 splan[kSmallP];
   __shared__ SlotPlan s_pl;

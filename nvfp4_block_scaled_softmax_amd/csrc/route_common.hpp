@@ -118,21 +118,17 @@ constexpr int kNoKey = (int)0x80000000;   // below every key of a finite value
 // lanes' maxima: at least k keys are >= L, so every one of the k largest keys
 // is >= L (the candidates), and any key larger than a candidate is itself a
 // candidate: a candidate's rank among the candidates (by key descending, then
-// index ascending) is its rank among all keys.  Each candidate's rank is
-// counted against every other candidate from LDS in parallel (typically a few
-// dozen candidates, no serial rounds), and the k smallest ranks are the
-// selection in order.  More than kTopkCand candidates (many equal keys) take
-// the rounds below instead; both give the same selection.
-constexpr int kTopkCand = 128;
+// index ascending) is its rank among all keys.  L comes from a most-significant-
+// bit-first search over ballots (per bit: one vector compare, a scalar count),
+// on the top 16 bits only (any L no larger than that maximum will do);
+// the candidates go to LDS one per lane, each counts the candidates above it,
+// and the k smallest counts are the selection in order.  More than kTopkCand
+// candidates (many equal keys) take the rounds below instead; both give the
+// same selection.
+constexpr int kTopkCand = kWave;
 struct TopkScratch {
-  int lmax[kWave];                         // the lanes' maxima
   unsigned long long cand[kTopkCand];      // the candidates, then the selection in rank order
 };
-
-// Keys as one ordered 64-bit word: larger key first, then lower index.
-__device__ __forceinline__ unsigned long long topk_composite(int key, int index) {
-  return (unsigned long long)((unsigned)key ^ 0x80000000u) << 32 | (0xFFFFFFFFu - (unsigned)index);
-}
 
 // Orders this wave's LDS writes before its later LDS reads by other lanes (LDS
 // requests of one wave are served in issue order; the compiler must not move
@@ -181,54 +177,52 @@ __device__ __forceinline__ bool topk_by_rank(const int* key, int k, TopkScratch*
                                              int& first_k) {
   static_assert(S <= 31, "a lane's candidate count must fit five bits");
   const int lane = lane_id();
-  int m = key[0];
+  unsigned u[S];   // the keys as unsigned order keys
+  unsigned m = 0u;
 #pragma unroll
-  for (int i = 1; i < S; ++i) m = max(m, key[i]);
-  sc->lmax[lane] = m;
-  wave_lds_sync();
-  int gt = 0, eq = 0;
-#pragma unroll
-  for (int q = 0; q < kWave; q += 4) {   // 16 reads in flight together
-    const int4 v = *reinterpret_cast<const int4*>(&sc->lmax[q]);
-    gt += (v.x > m) + (v.y > m) + (v.z > m) + (v.w > m);
-    eq += (v.x == m) + (v.y == m) + (v.z == m) + (v.w == m);
+  for (int i = 0; i < S; ++i) {
+    u[i] = (unsigned)key[i] ^ 0x80000000u;
+    m = max(m, u[i]);
   }
-  // L: the maxima in descending order, position k - 1 (the lanes whose maximum sits there)
-  const unsigned long long at = __ballot(gt <= k - 1 && k - 1 < gt + eq);
-  const int L = __builtin_amdgcn_readlane(m, __ffsll((long long)at) - 1);
+  // L: the largest value, its low 16 bits zero, that at least k of the lanes'
+  // maxima reach (no larger than the k-th largest maximum, which is all the
+  // candidate set needs; the low bits would cost a search step each and admit
+  // only a few candidates fewer)
+  unsigned L = 0u;
+#pragma unroll
+  for (int b = 31; b >= 16; --b) {
+    const unsigned c = L | (1u << b);
+    if (__popcll(__ballot(m >= c)) >= (unsigned)k) L = c;
+  }
   int c = 0;
 #pragma unroll
-  for (int i = 0; i < S; ++i) c += key[i] >= L;
+  for (int i = 0; i < S; ++i) c += u[i] >= L;
   int total;
   int pos = wave_prefix<S < 16 ? 4 : 5>(c, total);
   if (total > kTopkCand) return false;
+  // the candidates as ordered 64-bit words (larger key, then lower index,
+  // first), padded with zeros (below every candidate) to a multiple of 8
 #pragma unroll
   for (int i = 0; i < S; ++i)
-    if (key[i] >= L) sc->cand[pos++] = topk_composite(key[i], lane * S + i);
-  const int padded = (total + 15) & ~15;   // zero composites rank below every candidate
-  if (lane < padded - total) sc->cand[total + lane] = 0ull;
+    if (u[i] >= L) sc->cand[pos++] = (unsigned long long)u[i] << 32 | (0xFFFFFFFFu - (unsigned)(lane * S + i));
+  const int padded = (total + 7) & ~7;
+  if (lane >= total && lane < padded) sc->cand[lane] = 0ull;
   wave_lds_sync();
-  const int j0 = lane, j1 = lane + kWave;
-  const unsigned long long c0 = j0 < total ? sc->cand[j0] : 0ull;
-  const unsigned long long c1 = j1 < total ? sc->cand[j1] : 0ull;
-  int r0 = 0, r1 = 0;
-  for (int q0 = 0; q0 < padded; q0 += 16) {
-    unsigned long long v[16];
+  const unsigned long long mine = lane < total ? sc->cand[lane] : 0ull;
+  int r = 0;
+  for (int q0 = 0; q0 < padded; q0 += 8) {
+    unsigned long long v[8];
 #pragma unroll
-    for (int q = 0; q < 16; q += 2) {    // 8 reads in flight together
+    for (int q = 0; q < 8; q += 2) {   // four reads in flight together
       const ulonglong2 p = *reinterpret_cast<const ulonglong2*>(&sc->cand[q0 + q]);
       v[q] = p.x;
       v[q + 1] = p.y;
     }
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      r0 += v[q] > c0;
-      r1 += v[q] > c1;
-    }
+    for (int q = 0; q < 8; ++q) r += v[q] > mine;
   }
   wave_lds_sync();   // every lane has read the candidates
-  if (j0 < total && r0 < k) sc->cand[r0] = c0;
-  if (j1 < total && r1 < k) sc->cand[r1] = c1;
+  if (lane < total && r < k) sc->cand[r] = mine;
   wave_lds_sync();
   const unsigned long long sel = sc->cand[lane < k ? lane : 0];
   sel_k = (int)((unsigned)(sel >> 32) ^ 0x80000000u);
