@@ -73,7 +73,25 @@ typedef enum {
   MOE_FMT_Q4G64 = 2
 } moe_weight_format;
 
-/* One layer's experts, stacked over E, canonical layout.  The struct itself
+/* Arrangement of the NVFP4 block scales in memory (the codes are the same in
+ * both).  The pages' checkpoint is repacked into the engine's own expert
+ * layout without changing a bit (page "Qwen3.8-Flash-Next NVIDIA NVFP4 for
+ * Infernix (bit-exact)", section "What is bit-exact and what is quantized");
+ * this library's own bit-preserving layout is MOE_LAYOUT_TILED.
+ *   MOE_LAYOUT_CANONICAL: scale row [K/16] in K order: the two E4M3 scales of
+ *     chunk c (values 32c .. 32c+31) at bytes 2c, 2c+1.
+ *   MOE_LAYOUT_TILED: a scale row is cut into windows of 32 chunks (1024
+ *     values, 64 bytes).  In a full window, chunk 4i + g (step i of 128
+ *     values, piece g of 32) has its scale pair at pair position 8g + i of the
+ *     window: piece g of all 8 steps is one contiguous 16-byte word, which one
+ *     lane of the prefill matrix-core path loads for 8 steps at once.  A
+ *     trailing window of fewer than 32 chunks keeps the canonical order.
+ *     NVFP4 only, with H and I multiples of 128.  Produced by moe_nvfp4_repack;
+ *     every entry point that takes moe_nvfp4_experts accepts either layout and
+ *     gives bit-identical results. */
+typedef enum { MOE_LAYOUT_CANONICAL = 0, MOE_LAYOUT_TILED = 1 } moe_layout;
+
+/* One layer's experts, stacked over E.  The struct itself
  * lives in host memory; its pointers are device pointers.  16-byte alignment
  * is required for the code and scale arrays, 4-byte for the fp32 arrays.
  *   gu_codes   [E][2I][H/2]  gate rows 0..I-1, then up rows I..2I-1
@@ -86,6 +104,7 @@ typedef enum {
  *   dn_inscale [E]           fp32 activation input scale of down (MOE_A4 only)
  *   fmt                      the encoding (a zero-filled struct is NVFP4); MOE_FMT_Q4G64
  *                            needs H and I multiples of 64
+ *   layout                   the scale arrangement (moe_layout; zero: canonical)
  */
 typedef struct {
   const uint8_t* gu_codes;
@@ -97,7 +116,8 @@ typedef struct {
   const float* gu_inscale;
   const float* dn_inscale;
   int32_t E, H, I;
-  int32_t fmt; /* moe_weight_format */
+  int32_t fmt;    /* moe_weight_format */
+  int32_t layout; /* moe_layout */
 } moe_nvfp4_experts;
 
 /* The shared expert of a layer and its gate, BF16 (page "Qwen3.8-Flash-Next
@@ -346,6 +366,22 @@ moe_status moe_layer_forward_stage(const moe_nvfp4_experts* w, moe_act_mode mode
 moe_status moe_layer_forward_noalloc(const moe_nvfp4_experts* w, moe_act_mode mode, const uint16_t* x,
                                      const uint16_t* w_router, const float* router_bias, int T, int k,
                                      const uint16_t* residual, uint16_t* out, int reset, hipStream_t s);
+
+/* ------------------------------------------------------------------ repack
+ * moe_nvfp4_repack: the experts of src (canonical) into the tiled layout of dst
+ * (see moe_layout), without changing a bit: every code byte is copied as is
+ * and every scale byte moved to its tiled position (page "Qwen3.8-Flash-Next
+ * NVIDIA NVFP4 for Infernix (bit-exact)", section "What is bit-exact and what
+ * is quantized": the checkpoint is repacked into the engine's layout bit for
+ * bit).  src and dst are host structs of device pointers; dst's code and scale
+ * arrays are caller-allocated, of the same sizes as src's, and written here;
+ * its fp32 arrays are not touched (they may be src's own).  dst's code arrays
+ * may be src's (then they are not copied); its scale arrays must not overlap
+ * src's.  Requirements: src->layout MOE_LAYOUT_CANONICAL, dst->layout
+ * MOE_LAYOUT_TILED, both MOE_FMT_NVFP4 with equal E, H, I; H and I multiples
+ * of 128 (else MOE_E_SHAPE); 16-byte aligned arrays (else MOE_E_ALIGN).
+ * Enqueued on s; nothing is allocated. */
+moe_status moe_nvfp4_repack(const moe_nvfp4_experts* src, const moe_nvfp4_experts* dst, hipStream_t s);
 
 /* ------------------------------------------------------------------ test only
  * moe_debug_nvfp4_matmul: the expert kernels' product core without the

@@ -22,6 +22,7 @@ MODES = {"A16": MOE_A16, "A8": MOE_A8, "A4": MOE_A4,
          "F16": MOE_A16}   # "F16": the 16-bit activations as q4_g64_fp16 experts take them (fp16)
 DT_BF16, DT_F32 = 0, 1
 FMT_NVFP4, FMT_Q4G64 = 0, 2
+LAYOUT_CANONICAL, LAYOUT_TILED = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_E_ARG", -2: "MOE_E_ALIGN", -3: "MOE_E_SHAPE",
           -4: "MOE_E_UNSUPPORTED", -5: "MOE_E_WORKSPACE", -6: "MOE_E_HIP", -7: "MOE_E_STALLED"}
 
@@ -36,7 +37,7 @@ EXPORTS = ("moe_last_error", "moe_route_workspace_bytes", "moe_route_topk",
            "moe_layer_forward_noalloc",
            "moe_shared_expert_workspace_bytes", "moe_shared_expert_forward", "moe_combine_shared",
            "moe_block_workspace_bytes", "moe_block_workspace_layout", "moe_block_forward",
-           "q4g64_quantize", "moe_debug_q4g64_matmul")
+           "q4g64_quantize", "moe_debug_q4g64_matmul", "moe_nvfp4_repack")
 
 
 class MoeError(RuntimeError):
@@ -51,7 +52,7 @@ class _Experts(ctypes.Structure):
                 ("gu_wscale", ctypes.c_void_p), ("dn_wscale", ctypes.c_void_p),
                 ("gu_inscale", ctypes.c_void_p), ("dn_inscale", ctypes.c_void_p),
                 ("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
-                ("fmt", ctypes.c_int32)]
+                ("fmt", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 class _Shared(ctypes.Structure):
@@ -94,6 +95,7 @@ def lib():
             "moe_layer_status": ([_P, _P], _I),
             "q4g64_quantize": ([_P, _I, _I, _P, _P, _P], _I),
             "moe_debug_q4g64_matmul": ([_P, _P, _I, _I, _P, _I, _P, _P], _I),
+            "moe_nvfp4_repack": ([ctypes.POINTER(_Experts), ctypes.POINTER(_Experts), _P], _I),
             "moe_shared_expert_workspace_bytes": ([_I, _I], _Z),
             "moe_shared_expert_forward": ([ctypes.POINTER(_Shared), _P, _I, _P, _P, _Z, _P], _I),
             "moe_combine_shared": ([_P, _P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
@@ -154,9 +156,10 @@ def _mode(mode):
 # --------------------------------------------------------------------------- experts
 @dataclasses.dataclass
 class Experts:
-    """One layer's experts on the GPU, canonical layout (see the C header).
-    NVFP4 (fmt FMT_NVFP4) or q4_g64_fp16 (fmt FMT_Q4G64: scales fp16 bits, one
-    per 64, no multipliers)."""
+    """One layer's experts on the GPU (see the C header).  NVFP4 (fmt FMT_NVFP4)
+    or q4_g64_fp16 (fmt FMT_Q4G64: scales fp16 bits, one per 64, no
+    multipliers); layout LAYOUT_CANONICAL, or LAYOUT_TILED (NVFP4 scales
+    rearranged by moe_nvfp4_repack)."""
     gu_codes: torch.Tensor     # uint8 [E, 2I, H/2]
     gu_scales: torch.Tensor    # uint8 [E, 2I, H/16]  (q4: 16-bit [E, 2I, H/64])
     dn_codes: torch.Tensor     # uint8 [E, H, I/2]
@@ -166,6 +169,7 @@ class Experts:
     gu_inscale: torch.Tensor | None = None   # float32 [E, 2]
     dn_inscale: torch.Tensor | None = None   # float32 [E]
     fmt: int = 0
+    layout: int = 0
 
     @property
     def E(self):
@@ -206,7 +210,7 @@ class Experts:
         st = _Experts(self.gu_codes.data_ptr(), self.gu_scales.data_ptr(),
                       self.dn_codes.data_ptr(), self.dn_scales.data_ptr(),
                       opt(self.gu_wscale), opt(self.dn_wscale), opt(self.gu_inscale), opt(self.dn_inscale),
-                      E, H, I, int(self.fmt))
+                      E, H, I, int(self.fmt), int(self.layout))
         self.__dict__["_cstruct"] = st
         return st
 
@@ -326,6 +330,21 @@ def q4g64_quantize(x):
     scales = torch.empty(R, C // 64, dtype=torch.int16, device=x.device)
     _check("q4g64_quantize", lib().q4g64_quantize(_ptr(x), R, C, _ptr(codes), _ptr(scales), _stream()))
     return codes, scales
+
+
+def moe_nvfp4_repack(experts: Experts, share_codes=True):
+    """The experts in the tiled layout (moe_nvfp4_repack): new scale arrays, the
+    codes shared with `experts` (or copies, share_codes=False), the fp32 arrays
+    shared."""
+    src = experts.struct()
+    tiled = dataclasses.replace(experts, layout=LAYOUT_TILED,
+                                gu_codes=experts.gu_codes if share_codes else torch.empty_like(experts.gu_codes),
+                                dn_codes=experts.dn_codes if share_codes else torch.empty_like(experts.dn_codes),
+                                gu_scales=torch.empty_like(experts.gu_scales),
+                                dn_scales=torch.empty_like(experts.dn_scales))
+    tiled.__dict__.pop("_cstruct", None)
+    _check("moe_nvfp4_repack", lib().moe_nvfp4_repack(ctypes.byref(src), ctypes.byref(tiled.struct()), _stream()))
+    return tiled
 
 
 def pack_experts_q4(w_gu, w_dn):

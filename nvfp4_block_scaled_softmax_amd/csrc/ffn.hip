@@ -133,6 +133,7 @@ FfnArgs make_ffn_args(const moe_nvfp4_experts& w, moe_act_mode mode, const uint1
   a.h_codes = base + L.h_codes;
   a.h_scales = x16 ? nullptr : base + L.h_scales;
   a.y = y_pairs;
+  a.tiled = w.layout == MOE_LAYOUT_TILED ? 1 : 0;
   return a;
 }
 
@@ -182,6 +183,11 @@ moe_status check_experts(const char* name, const moe_nvfp4_experts* w, moe_act_m
               name, (int)mode);
   MOE_REQUIRE(w->fmt == MOE_FMT_NVFP4 || w->fmt == MOE_FMT_Q4G64, MOE_E_ARG, "%s: bad weight format %d", name,
               (int)w->fmt);
+  MOE_REQUIRE(w->layout == MOE_LAYOUT_CANONICAL || w->layout == MOE_LAYOUT_TILED, MOE_E_ARG, "%s: bad layout %d",
+              name, (int)w->layout);
+  MOE_REQUIRE(w->layout == MOE_LAYOUT_CANONICAL || (w->fmt == MOE_FMT_NVFP4 && w->H % 128 == 0 && w->I % 128 == 0),
+              MOE_E_SHAPE, "%s: the tiled layout is for NVFP4 experts with H and I multiples of 128 (H=%d I=%d)",
+              name, w->H, w->I);
   if (w->fmt == MOE_FMT_Q4G64) {
     MOE_REQUIRE(mode == MOE_A16, MOE_E_UNSUPPORTED, "%s: q4_g64_fp16 experts take 16-bit activations only", name);
     MOE_REQUIRE(w->gu_codes && w->gu_scales && w->dn_codes && w->dn_scales, MOE_E_ARG, "%s: null expert array",

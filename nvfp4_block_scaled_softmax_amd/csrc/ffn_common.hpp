@@ -24,6 +24,7 @@ struct FfnArgs {
   uint8_t* h_codes;          // A16: bf16 [P][I]; A8: E4M3 [P][I]; A4: [P][I/2]
   void* h_scales;            // A8: fp32 [P][I/16]; A4: E4M3 [P][I/16]
   float* y;                  // [P][H]
+  int tiled;                 // weight scales in the tiled layout (moe_layout)
 };
 
 struct FfnLayout {
@@ -76,12 +77,22 @@ struct ChunkLds<MOE_A4> { static constexpr int kStride = 48; };
 template <>
 struct ChunkLds<kModeQ4> { static constexpr int kStride = 80; };
 
+// Pair position of chunk c's two E4M3 scales in a tiled scale row of nc
+// chunks: in a full window of 32 chunks, chunk 4i + g (step i, piece g) sits
+// at 8g + i; a trailing partial window keeps the canonical order.
+__host__ __device__ __forceinline__ int tiled_pair(int c, int nc) {
+  const int p = c >> 5, cw = c & 31;
+  return (p + 1) * 32 <= nc ? (p << 5) | ((cw & 3) << 3) | (cw >> 2) : c;
+}
+
 // Bytes of one row's scales per 32-value chunk, and the scale of chunk c within
-// a row's scale bytes: NVFP4 two E4M3 per chunk; q4_g64_fp16 one fp16 per two chunks.
+// a row's scale bytes: NVFP4 two E4M3 per chunk (tiled_nc: the row's chunk
+// count when the scales are in the tiled layout, else 0); q4_g64_fp16 one fp16
+// per two chunks.
 template <int MODE>
-__device__ __forceinline__ uint32_t chunk_scale(const uint8_t* srow, int c) {
+__device__ __forceinline__ uint32_t chunk_scale(const uint8_t* srow, int c, int tiled_nc = 0) {
   if constexpr (MODE == kModeQ4) return *reinterpret_cast<const uint16_t*>(srow + 2 * (c >> 1));
-  else return *reinterpret_cast<const uint16_t*>(srow + 2 * c);
+  else return *reinterpret_cast<const uint16_t*>(srow + 2 * (tiled_nc ? tiled_pair(c, tiled_nc) : c));
 }
 template <int MODE>
 __host__ __device__ constexpr int scale_row_bytes(int K) { return MODE == kModeQ4 ? K / 32 : K / 16; }

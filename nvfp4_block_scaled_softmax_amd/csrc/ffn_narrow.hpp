@@ -258,7 +258,7 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, i
     for (int j = 0; j < CPL; ++j) {
       const int c = min(kl + j * LPR, NC - 1);
       wq[r][j] = *reinterpret_cast<const uint4*>(crow + 16 * c);
-      wsc[r][j] = chunk_scale<MODE>(srow, c);
+      wsc[r][j] = chunk_scale<MODE>(srow, c, a.tiled ? NC : 0);
     }
   }
   __builtin_amdgcn_sched_barrier(0);   // every load issued before any use of one
@@ -385,7 +385,7 @@ __device__ __forceinline__ void down_tile(const FfnArgs& a, int e, int row0, int
     for (int j = 0; j < CPL; ++j) {
       const int c = min(kl + j * LPR, NC - 1);
       wq[r][j] = *reinterpret_cast<const uint4*>(crow + 16 * c);
-      wsc[r][j] = chunk_scale<MODE>(srow, c);
+      wsc[r][j] = chunk_scale<MODE>(srow, c, a.tiled ? NC : 0);
     }
   }
   __builtin_amdgcn_sched_barrier(0);

@@ -102,9 +102,11 @@ __device__ __forceinline__ uint4 load_wcodes(const Rows& t, int vc, int st) {
 }
 
 // Weight scales come in windows of 8 steps: row r has 8 scale bytes per step,
-// 64 per window; lane (r, g) loads bytes 16g .. 16g+15 of its row's window p
-// (steps 8p + 2g and 8p + 2g + 1), one 16-byte load per 8 steps instead of a
-// 2-byte load per step.  Past the end of a row the load reads the next row
+// 64 per window; lane (r, g) loads bytes 16g .. 16g+15 of its row's window p,
+// one 16-byte load per 8 steps instead of a 2-byte load per step.  Canonical
+// layout: those are steps 8p + 2g and 8p + 2g + 1, and each step's pair is
+// fetched from the lane that holds it; tiled layout (a full window): they are
+// piece g of all 8 steps, the lane's own.  Past the end of a row the load reads the next row
 // (unused); past the wave's region the buffer returns zeros.
 __device__ __forceinline__ uint4 load_wscales(const Rows& t, int vs_row, int g, int p) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(t.scales, vs_row + 64 * p + 16 * g, 0, 0));
@@ -120,6 +122,14 @@ __device__ __forceinline__ uint32_t window_scales(const uint4& sw, int lane) {
   const int g = lane >> 4;
   const uint32_t d = g < 2 ? lo : hi;
   return (g & 1) ? d >> 16 : d & 0xFFFFu;
+}
+
+// The same in the tiled layout (a full window): lane (r, g) loaded piece g of
+// all 8 steps, step I in dword I / 2, half I % 2; no exchange between lanes.
+template <int I>
+__device__ __forceinline__ uint32_t window_scales_tiled(const uint4& sw) {
+  const uint32_t d = I / 2 == 0 ? sw.x : I / 2 == 1 ? sw.y : I / 2 == 2 ? sw.z : sw.w;
+  return I % 2 ? d >> 16 : d & 0xFFFFu;
 }
 
 // The MFMA operand type of a mode: bf16 for 16-bit activations, f16 otherwise.
@@ -359,7 +369,7 @@ __device__ __forceinline__ void stage_chunk(uint8_t* buf, const XFrag<MODE>& f, 
 template <int MODE, int NM, int NT>
 __device__ __forceinline__ void wide_mainloop(const Rows& w, int wc, int ws_row, const Rows& x,
                                               const Stager& sg, int m, int K, WideLds<NM>& lds,
-                                              f32x4 (&acc)[kWideTiles], float pw) {
+                                              f32x4 (&acc)[kWideTiles], float pw, int tiled) {
   const int lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
   const int nsteps = K / kKStep, nchunks = (nsteps + 1) / 2;
@@ -390,7 +400,9 @@ __device__ __forceinline__ void wide_mainloop(const Rows& w, int wc, int ws_row,
     __builtin_amdgcn_sched_barrier(0);   // the loads go out before the compute below
     if (s < nsteps) {
       WideOp<MODE> av[4];
-      expand_frag<MODE>(fw[u % kWSets], window_scales<u>(sw, lane), av);
+      // a full window of tiled scales holds this lane's pairs; else fetch them
+      const uint32_t sc = tiled && s0 + kBody <= nsteps ? window_scales_tiled<u>(sw) : window_scales<u>(sw, lane);
+      expand_frag<MODE>(fw[u % kWSets], sc, av);
       const uint8_t* bm = lds.buf + cb * WideLds<NM>::kBuf + (MODE == MOE_A4 ? m : 0) * kWideTok * kTokStride +
                           (u % 2) * (kKStep * 2) + 64 * g;
 #pragma unroll
@@ -517,7 +529,8 @@ __global__ void __launch_bounds__(512) k_gateup_wide(FfnArgs a, const int4* __re
   }
   f32x4 acc[kWideTiles];
   by_tiles(ntt, [&](auto NT) {
-    wide_mainloop<MODE, NM, decltype(NT)::value>(w, r * (H / 2) + 16 * g, r * (H / 16), x, sg, m, H, lds, acc, pw);
+    wide_mainloop<MODE, NM, decltype(NT)::value>(w, r * (H / 2) + 16 * g, r * (H / 16), x, sg, m, H, lds, acc, pw,
+                                                 a.tiled);
   });
   const float fm = a.gu_wscale[2 * e + m] * (MODE == MOE_A4 ? a.gu_inscale[2 * e + m] : 1.0f);
   float tok_f[kWideTiles];   // 8-bit mode: undo the token's power of two (exact)
@@ -615,7 +628,8 @@ __global__ void __launch_bounds__(NW * kWave) k_down_wide(FfnArgs a, const int4*
   }
   f32x4 acc[kWideTiles];
   by_tiles(ntt, [&](auto NT) {
-    wide_mainloop<MODE, NM, decltype(NT)::value>(w, r * (I / 2) + 16 * g, r * (I / 16), x, sg, 0, I, lds, acc, pw);
+    wide_mainloop<MODE, NM, decltype(NT)::value>(w, r * (I / 2) + 16 * g, r * (I / 16), x, sg, 0, I, lds, acc, pw,
+                                                 a.tiled);
   });
   if (!on) return;
   const float f = a.dn_wscale[e] * (MODE == MOE_A4 ? a.dn_inscale[e] : 1.0f);

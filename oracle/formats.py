@@ -152,3 +152,33 @@ def unpack_nibbles(packed):
     out[..., 0::2] = p & 15
     out[..., 1::2] = p >> 4
     return out
+
+
+# ---------------------------------------------------------------- scale layout
+# The engine's own arrangement of the NVFP4 block scales (the pages say the
+# checkpoint is repacked into the engine's expert layout without changing a
+# bit: page "Qwen3.8-Flash-Next NVIDIA NVFP4 for Infernix (bit-exact)",
+# section "What is bit-exact and what is quantized"; the arrangement itself is
+# this library's, stated in its C header under moe_layout).  A scale row holds
+# one pair of E4M3 bytes per chunk of 32 values.  The tiled order cuts the row
+# into windows of 32 chunks; in a full window, chunk 4*i + g moves to position
+# 8*g + i; a trailing partial window stays in place.
+
+def tiled_scale_order(nc):
+    """Tiled pair position of each canonical chunk pair 0 .. nc-1 of a row."""
+    pos = list(range(nc))
+    for w in range(nc // 32):
+        for c in range(32):
+            i, g = divmod(c, 4)
+            pos[32 * w + c] = 32 * w + 8 * g + i
+    return np.array(pos, dtype=np.int64)
+
+
+def tiled_scales(scales):
+    """Canonical scale bytes [..., K/16] (uint8) in the tiled order."""
+    scales = np.asarray(scales, dtype=np.uint8)
+    nc = scales.shape[-1] // 2
+    pairs = scales.reshape(*scales.shape[:-1], nc, 2)
+    out = np.empty_like(pairs)
+    out[..., tiled_scale_order(nc), :] = pairs
+    return out.reshape(scales.shape)

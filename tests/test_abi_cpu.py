@@ -166,3 +166,29 @@ def test_debug_matmul_validation():
 def test_layer_status_validation():
     L = moe.lib()
     assert _err(L.moe_layer_status(None, None))[0] == "MOE_E_ARG"
+
+
+def test_layout_and_repack_validation():
+    L = moe.lib()
+    args = (P16, 1, 10, P16, P16, P16, P16, 1 << 30, None)
+    s = moe._Experts(4096, 4096, 4096, 4096, 4096, 4096, None, None, 512, 3072, 512, 0, 7)
+    assert _err(L.nvfp4_expert_ffn(ctypes.byref(s), moe.MOE_A16, *args))[0] == "MOE_E_ARG"      # bad layout
+    s.layout = moe.LAYOUT_TILED
+    s.I = 480                                                                                  # not % 128
+    assert _err(L.nvfp4_expert_ffn(ctypes.byref(s), moe.MOE_A16, *args))[0] == "MOE_E_SHAPE"
+    s.I, s.fmt = 512, moe.FMT_Q4G64                                                            # tiled is NVFP4 only
+    assert _err(L.nvfp4_expert_ffn(ctypes.byref(s), moe.MOE_A16, *args))[0] == "MOE_E_SHAPE"
+    src = moe._Experts(1 << 20, 2 << 20, 3 << 20, 4 << 20, 4096, 4096, None, None, 4, 1152, 256, 0, 0)
+    dst = moe._Experts(5 << 20, 6 << 20, 7 << 20, 8 << 20, 4096, 4096, None, None, 4, 1152, 256, 0, 1)
+    assert _err(L.moe_nvfp4_repack(None, ctypes.byref(dst), None))[0] == "MOE_E_ARG"
+    dst.layout = 0
+    assert _err(L.moe_nvfp4_repack(ctypes.byref(src), ctypes.byref(dst), None))[0] == "MOE_E_ARG"   # dst not tiled
+    dst.layout, dst.H = 1, 1024
+    assert _err(L.moe_nvfp4_repack(ctypes.byref(src), ctypes.byref(dst), None))[0] == "MOE_E_SHAPE"  # shapes differ
+    dst.H, src.I, dst.I = 1152, 224, 224
+    assert _err(L.moe_nvfp4_repack(ctypes.byref(src), ctypes.byref(dst), None))[0] == "MOE_E_SHAPE"  # I % 128
+    src.I = dst.I = 256
+    dst.gu_scales = src.gu_scales + 64                                                         # overlapping scales
+    assert _err(L.moe_nvfp4_repack(ctypes.byref(src), ctypes.byref(dst), None))[0] == "MOE_E_ARG"
+    dst.gu_scales = (6 << 20) + 8
+    assert _err(L.moe_nvfp4_repack(ctypes.byref(src), ctypes.byref(dst), None))[0] == "MOE_E_ALIGN"

@@ -63,13 +63,16 @@ def gpu_layer(w, layer, mode, dev):
 
 
 def check_packed_bytes(ex_gpu, cache, experts):
-    """GPU-packed weights of these experts == the oracle's packing, byte for byte."""
+    """GPU-packed weights of these experts == the oracle's packing, byte for byte
+    (tiled experts: the oracle's scales in the tiled order)."""
+    tiled = getattr(ex_gpu, "layout", 0) == moe.LAYOUT_TILED
     for e in experts:
         o = cache(e)
+        gs, ds = (F.tiled_scales(o.gu_scales), F.tiled_scales(o.dn_scales)) if tiled else (o.gu_scales, o.dn_scales)
         assert np.array_equal(host(ex_gpu.gu_codes[e]), o.gu_codes), e
-        assert np.array_equal(host(ex_gpu.gu_scales[e]).view(o.gu_scales.dtype), o.gu_scales), e
+        assert np.array_equal(host(ex_gpu.gu_scales[e]).view(gs.dtype), gs), e
         assert np.array_equal(host(ex_gpu.dn_codes[e]), o.dn_codes), e
-        assert np.array_equal(host(ex_gpu.dn_scales[e]).view(o.dn_scales.dtype), o.dn_scales), e
+        assert np.array_equal(host(ex_gpu.dn_scales[e]).view(ds.dtype), ds), e
         if cache.fmt == "q4":
             continue
         assert np.array_equal(host(ex_gpu.gu_wscale[e]).view(np.uint32), o.gu_wscale.view(np.uint32)), e
@@ -455,3 +458,29 @@ def test_decode_graph_layers_oracle(dev):
             assert moe.layer_wait_timeouts(wss[l]) == 0
     _LAYERS.clear()
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("wi,mode,T", [(1, "A16", None), (2, "A4", None), (4, "A4", None), (4, "A16", 96)],
+                         ids=["decode-A16", "verify-A4", "prefill-A4", "wide-A16-T96"])
+def test_tiled_layout(dev, wi, mode, T):
+    """Experts repacked into the tiled scale layout (moe_nvfp4_repack): the
+    repacked bytes are the oracle's in the tiled order, and the layer (the fused
+    decode launch, the two-launch narrow path, the wide matrix-core path) gives
+    the oracle's result and the canonical experts' output bit for bit."""
+    w = synth.CONFIGS[wi]
+    T = w.T if T is None else T
+    ex, router, bias = gpu_layer(w, 0, mode, dev)
+    tiled = moe.moe_nvfp4_repack(ex)
+    torch.cuda.synchronize()
+    assert tiled.layout == moe.LAYOUT_TILED and tiled.gu_codes.data_ptr() == ex.gu_codes.data_ptr()
+    xb = bench.token_batch(w, 3, dev, T)
+    say("tiled", w.index, mode, "T", T)
+    out_c, _ = moe.moe_layer_forward(ex, mode, xb, router, w.k, bias=bias)
+    out_t, ws = moe.moe_layer_forward(tiled, mode, xb, router, w.k, bias=bias)
+    torch.cuda.synchronize()
+    moe.moe_layer_status(ws)
+    assert torch.equal(out_c.view(torch.int16), out_t.view(torch.int16))
+    sample = None if T <= 8 else np.arange(0, T, max(1, T // 48))
+    check_call(w, mode, 0, synth.tokens(w, batch=3, T=T), out_t, ws, sample=sample, ex=tiled)
+    del tiled
