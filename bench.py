@@ -129,7 +129,8 @@ def expert_bytes(w, fmt):
     return n // 2 + (n // 16 if fmt == "nvfp4" else n // 32)
 
 
-def run_gpu(w, mode, steps, warmup, n_layers, n_batches, fmt="nvfp4", shared=False, split=True, stack=False):
+def run_gpu(w, mode, steps, warmup, n_layers, n_batches, fmt="nvfp4", shared=False, split=True, stack=False,
+            layout="canonical"):
     """Timed whole-layer calls of one workload; returns a dict of measurements.
 
     The steps cycle over n_layers seeded layer copies and n_batches token batches;
@@ -142,6 +143,9 @@ def run_gpu(w, mode, steps, warmup, n_layers, n_batches, fmt="nvfp4", shared=Fal
     f32 = dict(dtype=torch.float32, device=dev)
     bufs = (torch.empty(E, 2, I * H, **f32), torch.empty(E, I * H, **f32), torch.empty(E, H * I, **f32))
     layers = [build_layer(w, l, dev, mode, bufs, fmt) for l in range(n_layers)]
+    if layout == "tiled":   # the experts' scales in the tiled layout (moe_nvfp4_repack), codes shared
+        layers = [(moe.moe_nvfp4_repack(ex), router, bias) for ex, router, bias in layers]
+        torch.cuda.synchronize()
     shareds = [shared_on_gpu(w, l, dev) for l in range(n_layers)] if shared else None
     del bufs
     torch.cuda.empty_cache()
@@ -462,6 +466,8 @@ SUBRECORDS = (
     ("prefill_w4a4_T1024", 4, "A4", "nvfp4", False, 20, 2, 4, {}),
     ("prefill_w4a16_T1024", 4, "A16", "nvfp4", False, 20, 2, 4, {}),
     ("prefill_w4a8_T1024", 4, "A8", "nvfp4", False, 20, 2, 4, {}),
+    ("prefill_w4a4_T1024_tiled", 4, "A4", "nvfp4", False, 20, 2, 4, {"layout": "tiled"}),
+    ("prefill_w4a16_T1024_tiled", 4, "A16", "nvfp4", False, 20, 2, 4, {"layout": "tiled"}),
     ("decode_w4a16_T1_shared_expert", 1, "A16", "nvfp4", True, 100, 8, 64, {}),
     ("decode_q4g64_T1", 1, "A16", "q4", False, 100, 8, 64, {}),
 )
@@ -524,7 +530,10 @@ def main(argv=None):
         key, wi, mode, fmt, shared, steps, nl, nb, extra = rows[0]
         w = synth.CONFIGS[wi] if not shared else synth.with_shared_expert(synth.CONFIGS[wi])
         rec = run_gpu(w, mode, min(steps, args.steps), args.warmup, nl, nb, fmt, shared, **extra)
-        print(json.dumps({key: _summary(w, mode, fmt, rec)}), flush=True)
+        summ = _summary(w, mode, fmt, rec)
+        if "layout" in extra:
+            summ["layout"] = extra["layout"]
+        print(json.dumps({key: summ}), flush=True)
         return 0
     w = synth.CONFIGS[args.workload]
     mode = w.modes[0]
@@ -559,6 +568,8 @@ def main(argv=None):
             print(f"[bench] sub-record {key}", file=sys.stderr, flush=True)
             rec = run_gpu(sw, smode, min(steps, args.steps), min(args.warmup, 10), nl, nb, fmt, shared, **extra)
             subs[key] = _summary(sw, smode, fmt, rec)
+            if "layout" in extra:
+                subs[key]["layout"] = extra["layout"]
             print(f"[bench]   {subs[key]['us_per_step']} us/step, {subs[key]['weight_gbs']} GB/s",
                   file=sys.stderr, flush=True)
     line = {

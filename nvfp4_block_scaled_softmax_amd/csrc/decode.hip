@@ -325,14 +325,30 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
   const int G = max_slots * nrb_gu;
   if (wg < G) {
     const int slot = wg / nrb_gu, rb = wg % nrb_gu;
+    // x of every token fits the tile's LDS (16/8-bit modes): it is staged while
+    // the plan is awaited, so no x load trails the weight loads
+    const bool xs = MODE != MOE_A4 && a.T <= cols_gu;
+    if (xs) {
+      stage_gateup_cols<MODE, true>(a, 0, 0, 0, a.T, nullptr, lds);
+      __syncthreads();
+    }
     const SlotPlan pl = plan_of(slot, 0);
     if (pl.e < 0) return;
     if (MODE == MOE_A16 && pl.outs_epoch != 0u) {   // single launch: h goes out as tagged words
-      gateup_tile<MODE, GL, GC, true>(a, pl.e, pl.row0, pl.rows, rb, cols_gu, lds, pl.tmask, st->h_tag,
-                                      pl.outs_epoch);
+      if (xs)
+        gateup_tile<MODE, GL, GC, true, false, true>(a, pl.e, pl.row0, pl.rows, rb, cols_gu, lds, pl.tmask,
+                                                     st->h_tag, pl.outs_epoch);
+      else
+        gateup_tile<MODE, GL, GC, true>(a, pl.e, pl.row0, pl.rows, rb, cols_gu, lds, pl.tmask, st->h_tag,
+                                        pl.outs_epoch);
       return;
     }
-    gateup_tile<MODE, GL, GC, true, MODE == MOE_A4>(a, pl.e, pl.row0, pl.rows, rb, cols_gu, lds, pl.tmask);
+    if constexpr (MODE != MOE_A4) {
+      if (xs) gateup_tile<MODE, GL, GC, true, false, true>(a, pl.e, pl.row0, pl.rows, rb, cols_gu, lds, pl.tmask);
+      else gateup_tile<MODE, GL, GC, true>(a, pl.e, pl.row0, pl.rows, rb, cols_gu, lds, pl.tmask);
+    } else {
+      gateup_tile<MODE, GL, GC, true, true>(a, pl.e, pl.row0, pl.rows, rb, cols_gu, lds, pl.tmask);
+    }
     wait_vmem();   // this wave's h has reached the device-coherent level
     __syncthreads();
     if (tid == 0)

@@ -212,7 +212,11 @@ __device__ void stage_gateup_quant_a4(const FfnArgs& a, int e, int row0, int c0,
 // 32) | epoch, written as one atomic store, for consumers that poll the words.
 // QX (4-bit mode): x is quantized in the tile (stage_gateup_quant_a4) instead of
 // read quantized from the workspace; row block 0's tile also writes it there.
-template <int MODE, int LPR, int CPL, bool COH = false, bool QX = false>
+// XS (16/8-bit modes, a.T <= max_cols): the caller has staged x of every token
+// into LDS (stage_gateup_cols by token) and synchronised; no x load then
+// follows the weight loads, so the compute of a chunk waits only for that
+// chunk's weights.
+template <int MODE, int LPR, int CPL, bool COH = false, bool QX = false, bool XS = false>
 __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, int ne, int rb,
                                             int max_cols, uint8_t* lds, int tmask = -1,
                                             uint64_t* htag = nullptr, uint32_t epoch = 0u) {
@@ -240,43 +244,56 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, i
     return (int)hld32<COH>(a.sorted_pairs, 4 * (size_t)(row0 + c0 + l));
   };
   int pair = col_pair(0);
+  const bool by_token = XS || (MODE != MOE_A4 && a.T <= max_cols);
+  if constexpr (XS) {   // the first column group's tokens, before the weight loads
+    if (threadIdx.x < min(max_cols, ne)) s_tok[threadIdx.x] = pair / a.k;
+    __syncthreads();
+  }
   __builtin_amdgcn_sched_barrier(0);
-  // this lane's weight chunks: RP h rows x CPL chunks, all loads in flight together
+  // this lane's weight chunks: RP h rows x CPL chunks, all loads in flight
+  // together, chunk by chunk in the order the compute below takes them
   uint4 wq[RP][CPL];
   uint32_t wsc[RP][CPL];
+  const uint8_t* crow[RP];
+  const uint8_t* srow[RP];
 #pragma unroll
+  for (int r = 0; r < RP; ++r) {
+    const int hl = slot * RP + r;  // h row within the wave's four
+    const size_t grow = (size_t)e * 2 * I + (size_t)half * I + i0 + wave * 4 + min(hl, 3);
+    crow[r] = a.gu_codes + grow * (H / 2);
+    srow[r] = a.gu_scales + grow * scale_row_bytes<MODE>(H);
+  }
   // Unconditional loads: lanes past the row's chunks or the wave's four rows
   // read a clamped (valid) address and their values are never used.  A load
   // under a branch makes the compiler merge its result with the branch's other
   // value, and that copy waits for the load before the next one is issued.
-  for (int r = 0; r < RP; ++r) {
-    const int hl = slot * RP + r;  // h row within the wave's four
-    const size_t grow = (size_t)e * 2 * I + (size_t)half * I + i0 + wave * 4 + min(hl, 3);
-    const uint8_t* crow = a.gu_codes + grow * (H / 2);
-    const uint8_t* srow = a.gu_scales + grow * scale_row_bytes<MODE>(H);
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = min(kl + j * LPR, NC - 1);
-      wq[r][j] = *reinterpret_cast<const uint4*>(crow + 16 * c);
-      wsc[r][j] = chunk_scale<MODE>(srow, c, a.tiled ? NC : 0);
+  for (int j = 0; j < CPL; ++j) {
+    const int c = min(kl + j * LPR, NC - 1);
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+      wq[r][j] = *reinterpret_cast<const uint4*>(crow[r] + 16 * c);
+      wsc[r][j] = chunk_scale<MODE>(srow[r], c, a.tiled ? NC : 0);
     }
   }
   __builtin_amdgcn_sched_barrier(0);   // every load issued before any use of one
   // Up to max_cols tokens in all (16/8-bit modes): x of every token goes to LDS
-  // now, with no wait for the pairs' tokens, and columns index it by token.
-  const bool by_token = MODE != MOE_A4 && a.T <= max_cols;
-  if (by_token) stage_gateup_cols<MODE, true>(a, e, 0, 0, a.T, nullptr, lds);
+  // now (unless the caller staged it), with no wait for the pairs' tokens, and
+  // columns index it by token.
+  if (!XS && by_token) stage_gateup_cols<MODE, true>(a, e, 0, 0, a.T, nullptr, lds);
   const float wsc_m = MODE == kModeQ4 ? 1.0f : a.gu_wscale[2 * e + half];   // (q4: no multiplier)
   const float in_m = MODE == MOE_A4 ? a.gu_inscale[2 * e + half] : 1.0f;
   const float dn_in = MODE == MOE_A4 ? a.dn_inscale[e] : 0.0f;   // the intermediate's input scale
 
   for (int c0 = 0; c0 < ne; c0 += max_cols) {
     const int ncol = min(max_cols, ne - c0);
-    if (threadIdx.x < ncol) s_tok[threadIdx.x] = pair / a.k;
-    __syncthreads();
-    if constexpr (MODE == MOE_A4 && QX) stage_gateup_quant_a4(a, e, row0, c0, ncol, s_tok, lds, rb == 0);
-    else if (!by_token) stage_gateup_cols<MODE>(a, e, row0, c0, ncol, s_tok, lds);
-    __syncthreads();
+    if (!XS || c0 > 0) {   // (XS: the first group's tokens went to LDS before the loads)
+      if (threadIdx.x < ncol) s_tok[threadIdx.x] = pair / a.k;
+      __syncthreads();
+      if constexpr (MODE == MOE_A4 && QX) stage_gateup_quant_a4(a, e, row0, c0, ncol, s_tok, lds, rb == 0);
+      else if (!by_token) stage_gateup_cols<MODE>(a, e, row0, c0, ncol, s_tok, lds);
+      __syncthreads();
+    }
     for (int col = 0; col < ncol; ++col) {
       const uint8_t* xc = lds + (size_t)(by_token ? s_tok[col] : col) * NC * S;
       // chunk-outer: each activation chunk is read from LDS once for all rows;
