@@ -313,6 +313,18 @@ __device__ __forceinline__ void hst128(void* base, size_t off, uint4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v4u{v.x, v.y, v.z, v.w}, coh_rsrc(base), (int)off, 0, kCohPolicy);
   else *reinterpret_cast<uint4*>(static_cast<uint8_t*>(base) + off) = v;
 }
+// Loads of data that a call reads once (expert weights, router rows):
+// non-temporal, so that streaming them does not displace what the caches hold
+// for the rest of the call and the next one (code, arguments, activations).
+__device__ __forceinline__ uint4 ld_stream128(const void* p) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_stream16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+}
+
 template <bool COH>
 __device__ __forceinline__ uint16_t hld16(const void* base, size_t off) {
   if constexpr (COH) return __builtin_amdgcn_raw_buffer_load_b16(coh_rsrc(base), (int)off, 0, kCohPolicy);

@@ -91,8 +91,8 @@ __host__ __device__ __forceinline__ int tiled_pair(int c, int nc) {
 // per two chunks.
 template <int MODE>
 __device__ __forceinline__ uint32_t chunk_scale(const uint8_t* srow, int c, int tiled_nc = 0) {
-  if constexpr (MODE == kModeQ4) return *reinterpret_cast<const uint16_t*>(srow + 2 * (c >> 1));
-  else return *reinterpret_cast<const uint16_t*>(srow + 2 * (tiled_nc ? tiled_pair(c, tiled_nc) : c));
+  if constexpr (MODE == kModeQ4) return ld_stream16(srow + 2 * (c >> 1));
+  else return ld_stream16(srow + 2 * (tiled_nc ? tiled_pair(c, tiled_nc) : c));
 }
 template <int MODE>
 __host__ __device__ constexpr int scale_row_bytes(int K) { return MODE == kModeQ4 ? K / 32 : K / 16; }

@@ -272,7 +272,7 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, i
     const int c = min(kl + j * LPR, NC - 1);
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
-      wq[r][j] = *reinterpret_cast<const uint4*>(crow[r] + 16 * c);
+      wq[r][j] = ld_stream128(crow[r] + 16 * c);
       wsc[r][j] = chunk_scale<MODE>(srow[r], c, a.tiled ? NC : 0);
     }
   }
@@ -401,7 +401,7 @@ __device__ __forceinline__ void down_tile(const FfnArgs& a, int e, int row0, int
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = min(kl + j * LPR, NC - 1);
-      wq[r][j] = *reinterpret_cast<const uint4*>(crow + 16 * c);
+      wq[r][j] = ld_stream128(crow + 16 * c);
       wsc[r][j] = chunk_scale<MODE>(srow, c, a.tiled ? NC : 0);
     }
   }

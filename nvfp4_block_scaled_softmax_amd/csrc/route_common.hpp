@@ -31,7 +31,7 @@ __device__ __forceinline__ void router_logits_wave(const uint16_t* __restrict__ 
   uint4 wv[kMaxChunks];
   const uint4* wrow = reinterpret_cast<const uint4*>(wr + (size_t)(e < E ? e : 0) * H);
 #pragma unroll
-  for (int j = 0; j < kMaxChunks; ++j) wv[j] = wrow[min(lane + kWave * j, nch - 1)];   // clamped; unused past nch
+  for (int j = 0; j < kMaxChunks; ++j) wv[j] = ld_stream128(wrow + min(lane + kWave * j, nch - 1));   // clamped; unused past nch
   __builtin_amdgcn_sched_barrier(0);
   batched_copy<NT, 2>(   // NT = threads of the workgroup
       T * nch, [&](int i) { return reinterpret_cast<const uint4*>(x)[i]; },
