@@ -251,7 +251,7 @@ __global__ void __launch_bounds__(kPermThreads)
   __shared__ int s_last;
   __shared__ TopkScratch s_topk[kPermWaves];
   const int tid = threadIdx.x, wave = tid / kWave;
-  router_logits_wave<kPermThreads, true>(x, wr, bias, T, H, E, blockIdx.x * kPermWaves + wave,
+  router_logits_wave<kPermThreads, true, false, 8>(x, wr, bias, T, H, E, blockIdx.x * kPermWaves + wave,
                            reinterpret_cast<uint4*>(smem), logits);
   wait_vmem();   // this wave's logits have reached the device-coherent level
   __syncthreads();

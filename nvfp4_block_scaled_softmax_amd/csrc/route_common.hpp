@@ -15,7 +15,9 @@ constexpr int kNarrowT = 8;
 // With TAG, a logit is not stored as a float but published as one 64-bit word
 // tagged[t * E + e] = (logit bits << 32) | epoch, written as one atomic store, so
 // that a reader polling the words knows when every logit of a call is there.
-template <int NT, bool COH = false, bool TAG = false>
+// XB: x chunks each thread keeps in flight while staging (all of them in one
+// round trip when T * H / 8 <= NT * XB).
+template <int NT, bool COH = false, bool TAG = false, int XB = 2>
 __device__ __forceinline__ void router_logits_wave(const uint16_t* __restrict__ x,
                                                    const uint16_t* __restrict__ wr,
                                                    const float* __restrict__ bias, int T, int H,
@@ -33,7 +35,7 @@ __device__ __forceinline__ void router_logits_wave(const uint16_t* __restrict__ 
 #pragma unroll
   for (int j = 0; j < kMaxChunks; ++j) wv[j] = ld_stream128(wrow + min(lane + kWave * j, nch - 1));   // clamped; unused past nch
   __builtin_amdgcn_sched_barrier(0);
-  batched_copy<NT, 2>(   // NT = threads of the workgroup
+  batched_copy<NT, XB>(   // NT = threads of the workgroup
       T * nch, [&](int i) { return reinterpret_cast<const uint4*>(x)[i]; },
       [&](int i, uint4 v) { xs[i] = v; });
   __syncthreads();
