@@ -189,11 +189,9 @@ def run_gpu(w, mode, steps, warmup, n_layers, n_batches, fmt="nvfp4", shared=Fal
     ms = ev[0].elapsed_time(ev[1]) / steps
     total_bytes = sum(combo_bytes[s % combos] for s in range(warmup, warmup + steps))
     n_e = float(np.mean([combo_n[s % combos] for s in range(warmup, warmup + steps)]))
-    launches = moe.layer_launches(mode, T, k, H, I)
+    launches = moe.block_launches(mode, T, k, H, I, w.Is) if shared else moe.layer_launches(mode, T, k, H, I)
     if fmt == "q4" and launches == 1:
         launches = 2   # q4_g64_fp16 experts take the two-launch form
-    if shared:
-        launches += 2  # the shared expert's two kernels go first
     rec = {"ms_per_step": ms, "bytes_per_step": total_bytes / steps, "gbs": total_bytes / steps / (ms * 1e-3) / 1e9,
            "experts_per_step": n_e, "launches": launches}
     if shared:

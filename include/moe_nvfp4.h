@@ -323,6 +323,13 @@ int moe_layer_is_fused(int T, int H, int I);
  * too: it then takes its call number from the workspace and advances it itself
  * (a number baked into the launch would repeat on every replay). */
 int moe_layer_launches(moe_act_mode mode, int T, int k, int H, int I);
+
+/* Kernel launches of one moe_block_forward call with a shared expert of
+ * intermediate width Is: 1 where the single-launch decode layer also runs the
+ * shared expert (its conditions, and Is a multiple of 32 up to 512: the shared
+ * expert's weights then stream while the tokens are routed), else the shared
+ * expert's two kernels plus moe_layer_launches (0 for the per-stage path). */
+int moe_block_launches(moe_act_mode mode, int T, int k, int H, int I, int Is);
 size_t moe_layer_workspace_bytes(moe_act_mode mode, int T, int k, int E, int H, int I);
 moe_status moe_layer_forward(const moe_nvfp4_experts* w, moe_act_mode mode, const uint16_t* x,
                              const uint16_t* w_router, const float* router_bias, int T, int k,

@@ -32,7 +32,7 @@ EXPORTS = ("moe_last_error", "moe_route_workspace_bytes", "moe_route_topk",
            "nvfp4_expert_ffn_workspace_bytes", "nvfp4_expert_ffn", "nvfp4_expert_ffn_stage",
            "moe_combine",
            "moe_layer_workspace_bytes", "moe_layer_workspace_layout", "moe_layer_wait_timeouts_offset",
-           "moe_layer_forward", "moe_layer_forward_stage", "moe_layer_is_fused", "moe_layer_launches",
+           "moe_layer_forward", "moe_layer_forward_stage", "moe_layer_is_fused", "moe_layer_launches", "moe_block_launches",
            "moe_layer_status", "moe_debug_nvfp4_matmul_workspace_bytes", "moe_debug_nvfp4_matmul",
            "moe_layer_forward_noalloc",
            "moe_shared_expert_workspace_bytes", "moe_shared_expert_forward", "moe_combine_shared",
@@ -90,6 +90,7 @@ def lib():
             "moe_layer_wait_timeouts_offset": ([], _Z),
             "moe_layer_is_fused": ([_I, _I, _I], _I),
             "moe_layer_launches": ([_I, _I, _I, _I, _I], _I),
+            "moe_block_launches": ([_I, _I, _I, _I, _I, _I], _I),
             "moe_layer_forward_stage": ([ctypes.POINTER(_Experts), _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _Z, _P], _I),
             "moe_layer_forward": ([ctypes.POINTER(_Experts), _I, _P, _P, _P, _I, _I, _P, _P, _P, _Z, _P], _I),
             "moe_layer_status": ([_P, _P], _I),
@@ -595,6 +596,12 @@ def moe_layer_forward_stage(experts: Experts, mode, stage, x, w_router, k, bias,
 def layer_launches(mode, T, k, H, I):
     """Kernel launches of one moe_layer_forward call outside graph capture (0: per-stage path)."""
     return int(lib().moe_layer_launches(_mode(mode), T, k, H, I))
+
+
+def block_launches(mode, T, k, H, I, Is):
+    """Kernel launches of one moe_block_forward call (1: the shared expert runs in the
+    single decode launch; 0: per-stage path)."""
+    return int(lib().moe_block_launches(_mode(mode), T, k, H, I, Is))
 
 
 def layer_wait_timeouts(ws):

@@ -81,12 +81,18 @@ size_t decode_state_bytes();
 size_t decode_timeouts_offset();
 bool decode_fusable(int T, int H, int I);
 int decode_launches(moe_act_mode mode, int T, int k, int H, int I);
+// Whether the single launch also runs a block's shared expert of width Is.
+bool decode_fuses_shared(moe_act_mode mode, int T, int k, int H, int I, int Is);
 // stage_mask: bit 0 routing (+ activation quantization), bit 1 experts + combine.
+// shared_y: the shared expert's gated output, computed before the call, or
+// (with fuse_sw, when decode_fuses_shared) by the single launch itself into
+// shared_y and sh_h (its intermediate).
 moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, int stage_mask,
                                const uint16_t* x, const uint16_t* w_router, const float* bias,
                                int T, int k, const uint16_t* residual, uint16_t* out,
                                int32_t* ids, float* tw, int32_t* offsets, int32_t* sorted,
                                int32_t* prow, float* y, float* logits, void* ffn_ws, void* state,
-                               const float* shared_y, hipStream_t s);
+                               const float* shared_y, hipStream_t s,
+                               const moe_shared_expert* fuse_sw = nullptr, void* sh_h = nullptr);
 
 }  // namespace moe

@@ -55,6 +55,7 @@
 #include "ffn_narrow.hpp"
 #include "permute_common.hpp"
 #include "route_common.hpp"
+#include "shared_common.hpp"
 
 namespace moe {
 
@@ -65,6 +66,9 @@ constexpr int kSmallP = 64;           // up to this many pairs the routing tail 
 // counting on line i % kArrivalLines, so that ~2000 adds at the start of a
 // launch do not queue on one address.
 constexpr int kArrivalLines = 64;
+// The single launch runs a block's shared expert too when its intermediate is
+// at most this wide (its down tile holds Is / 128 chunks per lane in registers).
+constexpr int kFusedShIs = 512;
 
 // Each counter sits on its own 128-byte line: many workgroups poll or bump them
 // at once, and counters sharing a line would queue behind each other.
@@ -99,6 +103,10 @@ struct DecodeState {
   // single-launch layer: the intermediate h, two bf16 values per tagged word,
   // [sorted row][I/2]; the down tiles poll them
   uint64_t h_tag[kSmallP * kMaxDim / 2];
+  // single-launch block: the shared expert's intermediate [T][Is/2] (two bf16
+  // per word) and its gated output [T][H], tagged the same way
+  uint64_t sh_h_tag[kNarrowT * kFusedShIs / 2];
+  uint64_t sh_y_tag[kNarrowT * kMaxDim];
 };
 
 size_t decode_state_bytes() { return sizeof(DecodeState); }
@@ -315,7 +323,8 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
                                              const float* __restrict__ tw,
                                              const uint16_t* __restrict__ residual,
                                              uint16_t* __restrict__ out, uint8_t* lds,
-                                             const float* __restrict__ shared_y, PlanOf&& plan_of) {
+                                             const float* __restrict__ shared_y, PlanOf&& plan_of,
+                                             const uint64_t* __restrict__ shared_ytag = nullptr) {
   __shared__ int s_flag;
   __shared__ int s_prow[kDecMaxSlots];            // the combine's pair rows, weights and residual,
   __shared__ float s_tw[kDecMaxSlots];            // loaded while the tile waits for gate/up
@@ -400,6 +409,7 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
         // output whose inputs were given up on, here or by a producer, is NaN
         uint32_t aborted = 0u;
         Patience pat;
+        uint64_t sv = (uint64_t)epoch;   // the shared expert's output word (fused block), value 0 until read
         for (int j0 = 0; j0 < a.k; j0 += 16) {   // as combine_acc4: j ascending, one fma each
           uint64_t v[16];
           while (true) {
@@ -411,6 +421,10 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
                                                  __HIP_MEMORY_SCOPE_AGENT)
                             : (uint64_t)epoch;   // value 0
               ready = ready && (uint32_t)v[u] == epoch;
+            }
+            if (shared_ytag && j0 == 0) {   // polled with the first group
+              sv = __hip_atomic_load(&shared_ytag[(size_t)t * a.H + o], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              ready = ready && (uint32_t)sv == epoch;
             }
             aborted |= ld_relaxed(&st->timeouts.v);
             if (ready) break;
@@ -425,7 +439,8 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
             if (j0 + u < a.k)
               acc = __builtin_fmaf(s_tw[t * a.k + j0 + u], __builtin_bit_cast(float, (uint32_t)(v[u] >> 32)), acc);
         }
-        if (shared_y) acc += shared_y[(size_t)t * a.H + o];   // as add_shared4, one element
+        if (shared_ytag) acc += __builtin_bit_cast(float, (uint32_t)(sv >> 32));   // as add_shared4
+        else if (shared_y) acc += shared_y[(size_t)t * a.H + o];                  // (one element)
         uint32_t ob = f32_to_bf16(acc);   // as combine_round4, one element
         if (residual) ob = f32_to_bf16(bf16_to_f32(s_res[t][ol]) + bf16_to_f32(ob));
         out[(size_t)t * a.H + o] = aborted != 0u ? kBf16NaN : (uint16_t)ob;
@@ -513,7 +528,7 @@ __global__ void __launch_bounds__(kTileThreads)
 // resident at once: at most 128 VGPRs (four waves per SIMD), which the shapes
 // up to H = 3072 and E = 512 meet without spilling; wider ones are left to the
 // compiler's choice.
-template <int S, int MODE, int GL, int GC, int DL, int DC>
+template <int S, int MODE, int GL, int GC, int DL, int DC, bool SH>
 __global__ void __launch_bounds__(kTileThreads, (GC <= 3 && S <= 8) ? 4 : 1)
     k_layer_decode(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                    const float* __restrict__ bias, float* __restrict__ logits,
@@ -521,7 +536,7 @@ __global__ void __launch_bounds__(kTileThreads, (GC <= 3 && S <= 8) ? 4 : 1)
                    DecodeState* __restrict__ st, int max_slots, int cols_gu, int cols_dn,
                    int32_t* __restrict__ pair_row, const uint16_t* __restrict__ residual,
                    uint16_t* __restrict__ out, uint32_t epoch_arg, uint32_t dn_hold,
-                   const float* __restrict__ shared_y) {
+                   const float* __restrict__ shared_y, SharedArgs sa, int sgu, int sdn) {
   extern __shared__ __align__(16) uint8_t lds[];
   // epoch_arg 0 (a call recorded into a graph, where an epoch baked into the
   // launch would repeat on every replay): the epoch is 2^31 | dev_epoch (never 0
@@ -633,8 +648,23 @@ __global__ void __launch_bounds__(kTileThreads, (GC <= 3 && S <= 8) ? 4 : 1)
     }
     return;
   }
+  // a block's shared expert (sgu + sdn workgroups, none for a plain layer): it
+  // needs no routing, so its weights stream while the call is routed; h and y
+  // go out as tagged words, the combine polls y
+  if constexpr (SH) {   // (a separate instantiation: a plain layer's kernel carries none of this)
+    if (wg < R + sgu) {
+      shared_gateup_tile<4 * GC, true>(sa, wg - R, lds, st->sh_h_tag, epoch);
+      return;
+    }
+    if (wg < R + sgu + sdn) {
+      shared_down_tile<kFusedShIs / 128, true>(sa, wg - R - sgu, lds, NoHook{}, st->sh_h_tag, epoch,
+                                               &st->timeouts.v, st->sh_y_tag);
+      return;
+    }
+  }
   expert_tiles<MODE, GL, GC, DL, DC>(
-      a, st, wg - R, dn_hold, max_slots, cols_gu, cols_dn, pair_row, tw, residual, out, lds, shared_y,
+      a, st, wg - R - (SH ? sgu + sdn : 0), dn_hold, max_slots, cols_gu, cols_dn, pair_row, tw, residual, out, lds,
+      shared_y,
       [&](int slot, int role) {
         if (tid == 0) {
           const uint64_t* e = &st->pub[role][slot];
@@ -657,7 +687,7 @@ __global__ void __launch_bounds__(kTileThreads, (GC <= 3 && S <= 8) ? 4 : 1)
         }
         __syncthreads();
         return s_pl;
-      });
+      }, SH ? st->sh_y_tag : nullptr);
 }
 
 // ------------------------------------------------------------------ launch
@@ -754,43 +784,57 @@ static void launch_b(const FfnArgs& a, DecodeState* st, int max_slots, const int
 }
 
 // ---- the single-launch layer (16-bit activations, up to kSmallP pairs)
+// sa: a block's shared expert run by the same launch (decode_fuses_shared), or null.
 template <int S, int GC, int DL>
 static void launch_one3(const FfnArgs& a, const uint16_t* x, const uint16_t* wr, const float* bias,
                         float* logits, int32_t* ids, float* tw, int32_t* prow, DecodeState* st,
-                        const uint16_t* residual, uint16_t* out, uint64_t epoch, const float* shy, hipStream_t s) {
+                        const uint16_t* residual, uint16_t* out, uint64_t epoch, const float* shy,
+                        const SharedArgs* sa, hipStream_t s) {
   const int P = a.T * a.k, max_slots = P < a.E ? P : a.E;
   const int cols = max(1, min(min(8, a.T), kLdsBudget / ((a.H / 32) * ChunkLds<MOE_A16>::kStride)));
   const int cols_dn = max(1, min(min(8, a.T), kLdsBudget / ((a.I / 32) * ChunkLds<MOE_A16>::kStride)));
   const int R = (a.E + kTileWaves - 1) / kTileWaves;
-  const int grid = R + max_slots * (a.I / kGuRows + (a.H + kDnRows - 1) / kDnRows);
+  const int sgu = sa ? sa->Is / kShGuRows : 0, sdn = sa ? (a.H + kShDnRows - 1) / kShDnRows : 0;
+  const int grid = R + sgu + sdn + max_slots * (a.I / kGuRows + (a.H + kDnRows - 1) / kDnRows);
   size_t lds = (size_t)a.T * a.H * 2;
   lds = std::max(lds, (size_t)cols * (a.H / 32) * ChunkLds<MOE_A16>::kStride);
   lds = std::max(lds, (size_t)cols_dn * (a.I / 32) * ChunkLds<MOE_A16>::kStride);
-  const int cap = resident_groups(reinterpret_cast<const void*>(&k_layer_decode<S, MOE_A16, 32, GC, DL, 1>), lds);
-  const uint32_t dn_hold = cap > 0 && grid <= cap ? kDnHoldTicksPerExpert : 0u;
-  hipLaunchKernelGGL((k_layer_decode<S, MOE_A16, 32, GC, DL, 1>), dim3(grid), dim3(kTileThreads), lds, s,
-                     x, wr, bias, logits, ids, tw, a, st, max_slots, cols, cols_dn, prow, residual, out,
-                     (uint32_t)epoch, dn_hold, shy);
+  if (sa) lds = std::max(lds, (size_t)a.T * sa->Is * 2);   // the shared down tile's h
+  const SharedArgs sarg = sa ? *sa : SharedArgs{};
+  auto go = [&](auto kernel) {
+    const int cap = resident_groups(reinterpret_cast<const void*>(kernel), lds);
+    const uint32_t dn_hold = cap > 0 && grid <= cap ? kDnHoldTicksPerExpert : 0u;
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kTileThreads), lds, s, x, wr, bias, logits, ids, tw, a, st,
+                       max_slots, cols, cols_dn, prow, residual, out, (uint32_t)epoch, dn_hold, shy, sarg, sgu,
+                       sdn);
+  };
+  if (sa) go(&k_layer_decode<S, MOE_A16, 32, GC, DL, 1, true>);
+  else go(&k_layer_decode<S, MOE_A16, 32, GC, DL, 1, false>);
 }
 
 template <int S, int GC>
 static void launch_one2(int dl, const FfnArgs& a, const uint16_t* x, const uint16_t* wr,
                         const float* bias, float* logits, int32_t* ids, float* tw, int32_t* prow,
                         DecodeState* st, const uint16_t* residual, uint16_t* out, uint64_t epoch,
-                        const float* shy, hipStream_t s) {
-  if (dl == 8) launch_one3<S, GC, 8>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, s);
-  else if (dl == 16) launch_one3<S, GC, 16>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, s);
-  else launch_one3<S, GC, 32>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, s);
+                        const float* shy, const SharedArgs* sa, hipStream_t s) {
+  if (dl == 8) launch_one3<S, GC, 8>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+  else if (dl == 16) launch_one3<S, GC, 16>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+  else launch_one3<S, GC, 32>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
 }
 
 template <int S>
 static void launch_one(const FfnArgs& a, const uint16_t* x, const uint16_t* wr, const float* bias,
                        float* logits, int32_t* ids, float* tw, int32_t* prow, DecodeState* st,
-                       const uint16_t* residual, uint16_t* out, uint64_t epoch, const float* shy, hipStream_t s) {
+                       const uint16_t* residual, uint16_t* out, uint64_t epoch, const float* shy,
+                       const SharedArgs* sa, hipStream_t s) {
   const int gc = gu_config(a.H / 32), dl = dn_config(a.I / 32);
-  if (gc == 2) launch_one2<S, 2>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, s);
-  else if (gc == 3) launch_one2<S, 3>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, s);
-  else launch_one2<S, 4>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, s);
+  if (gc == 2) launch_one2<S, 2>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+  else if (gc == 3) launch_one2<S, 3>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+  else launch_one2<S, 4>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+}
+
+bool decode_fuses_shared(moe_act_mode mode, int T, int k, int H, int I, int Is) {
+  return decode_fusable(T, H, I) && single_launch(mode, T, k) && Is >= 32 && Is <= kFusedShIs && Is % 32 == 0;
 }
 
 // Epochs of eager single-launch calls: 31 bits, not reused within 2^31 calls
@@ -803,7 +847,8 @@ moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, in
                                int T, int k, const uint16_t* residual, uint16_t* out,
                                int32_t* ids, float* tw, int32_t* offsets, int32_t* sorted,
                                int32_t* prow, float* y, float* logits, void* ffn_ws, void* state,
-                               const float* shared_y, hipStream_t s) {
+                               const float* shared_y, hipStream_t s, const moe_shared_expert* fuse_sw,
+                               void* sh_h) {
   DecodeState* st = static_cast<DecodeState*>(state);
   const int E = w.E, H = w.H;
   moe_status r;
@@ -814,15 +859,22 @@ moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, in
     if (hipStreamIsCapturing(s, &cs) != hipSuccess) return check_launch("moe_layer_forward (capture query)");
     {
       const FfnArgs a = make_ffn_args(w, mode, x, T, k, offsets, sorted, y, ffn_ws);
+      SharedArgs sarg;
+      const SharedArgs* sa = nullptr;
+      if (fuse_sw) {   // (the caller checked decode_fuses_shared)
+        sarg = make_shared_args(*fuse_sw, x, T, sh_h, const_cast<float*>(shared_y));
+        sa = &sarg;
+      }
       uint64_t epoch = 0;   // 0: read the device epoch
       if (cs == hipStreamCaptureStatusNone) {
         do epoch = ++g_epoch & 0x7FFFFFFFu; while (epoch == 0u);   // 0: a never-written entry
       }
-      if (E <= 64) launch_one<1>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shared_y, s);
-      else if (E <= 128) launch_one<2>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shared_y, s);
-      else if (E <= 256) launch_one<4>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shared_y, s);
-      else if (E <= 512) launch_one<8>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shared_y, s);
-      else launch_one<16>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shared_y, s);
+      const float* shy = sa ? nullptr : shared_y;   // (fused: the combine polls the launch's own)
+      if (E <= 64) launch_one<1>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+      else if (E <= 128) launch_one<2>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+      else if (E <= 256) launch_one<4>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+      else if (E <= 512) launch_one<8>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+      else launch_one<16>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
       return check_launch("moe_layer_forward (decode layer)");
     }
   }

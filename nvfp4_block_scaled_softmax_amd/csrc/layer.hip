@@ -69,6 +69,12 @@ extern "C" int moe_layer_launches(moe_act_mode mode, int T, int k, int H, int I)
   return moe::decode_launches(mode, T, k, H, I);
 }
 
+extern "C" int moe_block_launches(moe_act_mode mode, int T, int k, int H, int I, int Is) {
+  if (moe::decode_fuses_shared(mode, T, k, H, I, Is)) return 1;
+  const int n = moe::decode_launches(mode, T, k, H, I);
+  return n > 0 ? n + 2 : 0;
+}
+
 extern "C" size_t moe_layer_wait_timeouts_offset(void) {
   return moe::decode_timeouts_offset();   // the state block is at the start of the workspace
 }
@@ -123,15 +129,18 @@ static moe_status layer_call(const char* name, const moe_nvfp4_experts* w, moe_a
   int32_t* sorted = reinterpret_cast<int32_t*>(b + L.sorted);
   int32_t* prow = reinterpret_cast<int32_t*>(b + L.pair_row);
   float* y = reinterpret_cast<float*>(b + L.y);
-  // the shared expert needs no routing: its kernels go first, with the routing half
+  // the shared expert needs no routing: the single decode launch runs it too
+  // (decode_fuses_shared); otherwise its kernels go first, with the routing half
   float* shy = sw ? reinterpret_cast<float*>(b + L.sh_y) : nullptr;
-  if (sw && (stage_mask & 1) &&
+  const bool fuse_sw = sw && stage_mask == 3 && moe::decode_fuses_shared(mode, T, k, w->H, w->I, sw->Is);
+  if (sw && !fuse_sw && (stage_mask & 1) &&
       (st = moe::launch_shared_expert(*sw, x, T, b + L.sh_h, shy, s)) != MOE_OK)
     return st;
   if (moe::decode_fusable(T, w->H, w->I))
     return moe::launch_layer_decode(*w, mode, stage_mask, x, w_router, router_bias, T, k,
                                     residual, out, ids, tw, offs, sorted, prow, y,
-                                    reinterpret_cast<float*>(b + L.route), b + L.ffn, b + L.state, shy, s);
+                                    reinterpret_cast<float*>(b + L.route), b + L.ffn, b + L.state, shy, s,
+                                    fuse_sw ? sw : nullptr, b + L.sh_h);
   if (stage_mask & 1) {
     if ((st = moe::launch_route(x, w_router, router_bias, T, w->H, w->E, k, ids, tw,
                                 reinterpret_cast<float*>(b + L.route), s)) != MOE_OK)

@@ -37,6 +37,9 @@ struct SharedArgs {
   int tg;                 // tokens per pass of the gate/up tile (<= kShTok; x of tg tokens fits its LDS)
 };
 
+// The argument block of a shared expert call (shared.hip).
+SharedArgs make_shared_args(const moe_shared_expert& sw, const uint16_t* x, int T, void* h_ws, float* y);
+
 // Tokens per gate/up pass: x of that many tokens (H bf16 each) in kShLdsX bytes.
 constexpr int kShLdsX = 48 * 1024;
 __host__ __device__ constexpr int shared_tok_group(int H) { return kShLdsX / (2 * H) < kShTok ? kShLdsX / (2 * H) : kShTok; }

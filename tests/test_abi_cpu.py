@@ -66,6 +66,14 @@ def test_route_validation():
     assert code == "MOE_E_WORKSPACE" and "workspace" in text
 
 
+def test_block_launch_query():
+    L = moe.lib()
+    assert L.moe_block_launches(moe.MOE_A16, 1, 10, 3072, 512, 512) == 1        # shared expert in the one launch
+    assert L.moe_block_launches(moe.MOE_A16, 1, 10, 3072, 512, 1024) == 3       # too wide: its own two kernels
+    assert L.moe_block_launches(moe.MOE_A4, 8, 10, 3072, 512, 512) == 2 + 2
+    assert L.moe_block_launches(moe.MOE_A16, 1024, 10, 3072, 512, 512) == 0     # per-stage path
+
+
 def test_layer_stage_and_fused_queries():
     L = moe.lib()
     assert L.moe_layer_is_fused(1, 3072, 512) == 1 and L.moe_layer_is_fused(8, 3072, 512) == 1
