@@ -315,11 +315,10 @@ moe_status moe_layer_status(const void* ws, hipStream_t s);
 int moe_layer_is_fused(int T, int H, int I);
 
 /* Kernel launches of one moe_layer_forward call: 1 for the single-launch
- * decode layer (fused sizes, MOE_A16 with NVFP4 experts, T*k <= 64), 2 or 3
- * for the fused two-kernel path (routing, for MOE_A8 the activation
- * quantizer, experts + combine; MOE_A4 quantizes x in the expert kernel's
- * gate/up tiles; q4_g64_fp16 experts take this path), 0 when the per-stage
- * kernels run.  Under stream capture the single-launch layer is one graph node
+ * decode layer (fused sizes, MOE_A16 with NVFP4 experts, T*k <= 64), 2 for
+ * the fused two-kernel path (routing, experts + combine; MOE_A8 quantizes x
+ * in the routing kernel, MOE_A4 in the expert kernel's gate/up tiles;
+ * q4_g64_fp16 experts take this path), 0 when the per-stage kernels run.  Under stream capture the single-launch layer is one graph node
  * too: it then takes its call number from the workspace and advances it itself
  * (a number baked into the launch would repeat on every replay). */
 int moe_layer_launches(moe_act_mode mode, int T, int k, int H, int I);

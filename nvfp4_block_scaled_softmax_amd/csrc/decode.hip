@@ -239,14 +239,19 @@ __device__ void small_offsets(const int4* splan, int n, int P, int E, int32_t* _
 }
 
 // ------------------------------------------------------------------ A: routing
-// 8 waves, one expert row each.  Dynamic LDS: x of the T tokens.
+// 8 waves, one expert row each.  Dynamic LDS: x of the T tokens.  8-bit mode
+// (xq_codes not null): the workgroups also quantize x per token for the expert
+// half, from the x they hold in LDS, in the arithmetic of act_quant_fp8 (E4M3
+// codes [T][H], fp32 scales [T][H/16]); the expert kernel, a later launch,
+// reads them.
 template <int S>
 __global__ void __launch_bounds__(kPermThreads)
     k_route_decode(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                    const float* __restrict__ bias, int T, int H, int E, int k,
                    float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ tw,
                    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
-                   int32_t* __restrict__ pair_row, DecodeState* __restrict__ st) {
+                   int32_t* __restrict__ pair_row, DecodeState* __restrict__ st,
+                   uint8_t* __restrict__ xq_codes, float* __restrict__ xq_scales) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int cnt[kMaxExperts];
   __shared__ int base[kMaxExperts];
@@ -261,6 +266,25 @@ __global__ void __launch_bounds__(kPermThreads)
   const int tid = threadIdx.x, wave = tid / kWave;
   router_logits_wave<kPermThreads, true, false, 8>(x, wr, bias, T, H, E, blockIdx.x * kPermWaves + wave,
                            reinterpret_cast<uint4*>(smem), logits);
+  if (xq_codes) {   // (x of every token is in smem, staged by the call above)
+    const int nb = H / 16;
+    const uint16_t* xs = reinterpret_cast<const uint16_t*>(smem);
+    for (int i = blockIdx.x * kPermThreads + tid; i < T * nb; i += gridDim.x * kPermThreads) {
+      const uint4 u0 = *reinterpret_cast<const uint4*>(xs + (size_t)i * 16);
+      const uint4 u1 = *reinterpret_cast<const uint4*>(xs + (size_t)i * 16 + 8);
+      const uint32_t wv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        v[2 * j] = bf16_to_f32(wv[j] & 0xFFFFu);
+        v[2 * j + 1] = bf16_to_f32(wv[j] >> 16);
+      }
+      uint32_t w4[4];
+      const float sc = fp8_quant16(v, w4);
+      *reinterpret_cast<uint4*>(xq_codes + (size_t)i * 16) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      xq_scales[i] = sc;
+    }
+  }
   wait_vmem();   // this wave's logits have reached the device-coherent level
   __syncthreads();
   if (tid == 0) {
@@ -724,10 +748,11 @@ constexpr uint32_t kDnHoldTicksPerExpert = 30;
 template <int S>
 static void launch_a(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E,
                      int k, float* logits, int32_t* ids, float* tw, int32_t* offsets,
-                     int32_t* sorted, int32_t* prow, DecodeState* st, hipStream_t s) {
+                     int32_t* sorted, int32_t* prow, DecodeState* st, uint8_t* xq_codes, float* xq_scales,
+                     hipStream_t s) {
   hipLaunchKernelGGL(k_route_decode<S>, dim3((E + kPermWaves - 1) / kPermWaves), dim3(kPermThreads),
                      (size_t)T * H * 2, s, x, wr, bias, T, H, E, k, logits, ids, tw, offsets,
-                     sorted, prow, st);
+                     sorted, prow, st, xq_codes, xq_scales);
 }
 
 // (lanes per row, chunks per lane) of the narrow tiles for a reduction of NC
@@ -744,7 +769,7 @@ static bool single_launch(moe_act_mode mode, int T, int k) { return mode == MOE_
 
 int decode_launches(moe_act_mode mode, int T, int k, int H, int I) {
   if (T < 1 || k < 1 || !decode_fusable(T, H, I)) return 0;
-  return single_launch(mode, T, k) ? 1 : (mode == MOE_A8 ? 3 : 2);   // A8: the activation quantizer between
+  return single_launch(mode, T, k) ? 1 : 2;
 }
 
 template <int MODE, int GC, int DL>
@@ -878,18 +903,17 @@ moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, in
       return check_launch("moe_layer_forward (decode layer)");
     }
   }
-  if (stage_mask & 1) {   // routing, and the activation quantization of the 8/4-bit modes
-    if (E <= 64) launch_a<1>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
-    else if (E <= 128) launch_a<2>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
-    else if (E <= 256) launch_a<4>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
-    else if (E <= 512) launch_a<8>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
-    else launch_a<16>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, s);
+  if (stage_mask & 1) {   // routing (8-bit mode: with x quantized per token; 4-bit x is quantized in the gate/up tiles)
+    const FfnArgs q = make_ffn_args(w, mode, x, T, k, offsets, sorted, y, ffn_ws);
+    uint8_t* xqc = mode == MOE_A8 ? const_cast<uint8_t*>(q.xq_codes) : nullptr;
+    float* xqs = mode == MOE_A8 ? static_cast<float*>(const_cast<void*>(q.xq_scales)) : nullptr;
+    if (E <= 64) launch_a<1>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, xqc, xqs, s);
+    else if (E <= 128) launch_a<2>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, xqc, xqs, s);
+    else if (E <= 256) launch_a<4>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, xqc, xqs, s);
+    else if (E <= 512) launch_a<8>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, xqc, xqs, s);
+    else launch_a<16>(x, w_router, bias, T, H, E, k, logits, ids, tw, offsets, sorted, prow, st, xqc, xqs, s);
     r = check_launch("moe_layer_forward (decode routing)");
     if (r != MOE_OK) return r;
-    if (mode == MOE_A8) {   // x per token; 4-bit x is quantized in the gate/up tiles
-      r = launch_expert_ffn(w, mode, x, T, k, offsets, sorted, y, ffn_ws, 1, s, prow, ids);
-      if (r != MOE_OK) return r;
-    }
   }
   if (stage_mask & 2) {   // experts and combine
     const FfnArgs a = make_ffn_args(w, mode, x, T, k, offsets, sorted, y, ffn_ws);

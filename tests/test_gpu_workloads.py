@@ -276,7 +276,7 @@ def test_decode_edges(dev, w):
     per-stage entry points bit for bit, over three token batches on one workspace."""
     mode = w.modes[0]
     single = mode == "A16" and w.T * w.k <= 64
-    assert moe.layer_launches(mode, w.T, w.k, w.H, w.I) == (1 if single else (3 if mode == "A8" else 2))
+    assert moe.layer_launches(mode, w.T, w.k, w.H, w.I) == (1 if single else 2)
     ex, router, bias = gpu_layer(w, 0, mode, dev)
     ws = torch.zeros(moe.layer_workspace_bytes(mode, w.T, w.k, w.E, w.H, w.I), dtype=torch.uint8, device=dev)
     for batch in range(3):
