@@ -225,8 +225,11 @@ __device__ __forceinline__ Job wide_job(const int4* plan, int nrb, int slots) {
 // 16-byte LDS read.
 //
 // Activations: the chunk's tokens are expanded to f16 once per workgroup, 256
-// K values at a time, into one of two LDS buffers (row stride 528 B: 16 lanes
-// reading 16 B at consecutive tokens hit distinct banks).  One barrier per 256
+// K values at a time, into one of two LDS buffers (row stride 528 B: lanes
+// reading 16 B at consecutive tokens hit distinct banks).  Within a token's row
+// the 16-byte slot s sits at s ^ ((s >> 3) & 3) (slot_swz): a staging thread
+// writes four consecutive slots 4q .. 4q+3, and eight threads of one token
+// would otherwise write them to two bank groups.  One barrier per 256
 // K separates a buffer's writes from its reads; the buffer written during
 // chunk c (for chunk c + 1) was last read during chunk c - 1, before the
 // barrier that ended it.  Raw activation codes are loaded two chunks ahead.
@@ -253,6 +256,25 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for<B + 1, E>(f);
   }
 }
+
+// Physical 16-byte slot of logical slot s (0..31) in a token's LDS row: the
+// low two bits are XORed with bits 3-4, a permutation that spreads the slots
+// one staging instruction writes (s = 4 sq + q, sq = 0..7) over eight banks
+// groups and leaves the slot of a B-operand read (one s across 16 tokens) alone.
+__host__ __device__ constexpr int slot_swz(int s) { return s ^ ((s >> 3) & 3); }
+// The closed forms stage_chunk and wide_mainloop use: staging slot 4 sq + q at
+// 4 sq + (q ^ (sq >> 1)); read slot 16 h + 4 g + j at 16 h + 4 g + (j ^ (2 h + g / 2) % 4).
+constexpr bool slot_swz_forms() {
+  for (int sq = 0; sq < 8; ++sq)
+    for (int q = 0; q < 4; ++q)
+      if (slot_swz(4 * sq + q) != 4 * sq + (q ^ ((sq >> 1) & 3))) return false;
+  for (int h = 0; h < 2; ++h)
+    for (int g = 0; g < 4; ++g)
+      for (int j = 0; j < 4; ++j)
+        if (slot_swz(16 * h + 4 * g + j) != 16 * h + 4 * g + (j ^ ((2 * h + (g >> 1)) & 3))) return false;
+  return true;
+}
+static_assert(slot_swz_forms(), "slot swizzle closed forms");
 
 template <int NM>
 struct WideLds {
@@ -337,12 +359,14 @@ __device__ __forceinline__ void fp8x4_hilo(uint32_t w, float s, float pw, uint2&
 template <int MODE>
 __device__ __forceinline__ void stage_chunk(uint8_t* buf, const XFrag<MODE>& f, const Stager& sg, float pw) {
   if (!sg.on) return;
-  uint4* d = reinterpret_cast<uint4*>(buf + (sg.sm * kWideTok + sg.sn) * kTokStride + 64 * sg.sq);
+  // slots 4 sq + q of the token's row, at slot_swz(4 sq + q) = 4 sq + (q ^ x)
+  uint8_t* row = buf + (sg.sm * kWideTok + sg.sn) * kTokStride + 64 * sg.sq;
+  const int x = (sg.sq >> 1) & 3;
+  auto d = [&](int q) { return reinterpret_cast<uint4*>(row + 16 * (q ^ x)); };
   if constexpr (MODE == MOE_A16) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) d[q] = f.v[q];
+    for (int q = 0; q < 4; ++q) *d(q) = f.v[q];
   } else if constexpr (MODE == MOE_A8) {
-    uint4* dl = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(d) + kWideTok * kTokStride);   // plane 1
     const float s0 = __uint_as_float(f.s.x), s1 = __uint_as_float(f.s.y);
     const uint32_t w[8] = {f.c[0].x, f.c[0].y, f.c[0].z, f.c[0].w, f.c[1].x, f.c[1].y, f.c[1].z, f.c[1].w};
 #pragma unroll
@@ -350,16 +374,17 @@ __device__ __forceinline__ void stage_chunk(uint8_t* buf, const XFrag<MODE>& f, 
       uint2 h0, l0, h1, l1;
       fp8x4_hilo(w[2 * q], q < 2 ? s0 : s1, pw, h0, l0);
       fp8x4_hilo(w[2 * q + 1], q < 2 ? s0 : s1, pw, h1, l1);
-      d[q] = make_uint4(h0.x, h0.y, h1.x, h1.y);
-      dl[q] = make_uint4(l0.x, l0.y, l1.x, l1.y);
+      *d(q) = make_uint4(h0.x, h0.y, h1.x, h1.y);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(d(q)) + kWideTok * kTokStride) =   // plane 1
+          make_uint4(l0.x, l0.y, l1.x, l1.y);
     }
   } else {
     f16x2 s0, s1;
     scale_pair(f.s, s0, s1);
-    d[0] = bitcast<uint4>(expand8(f.c.x, s0));
-    d[1] = bitcast<uint4>(expand8(f.c.y, s0));
-    d[2] = bitcast<uint4>(expand8(f.c.z, s1));
-    d[3] = bitcast<uint4>(expand8(f.c.w, s1));
+    *d(0) = bitcast<uint4>(expand8(f.c.x, s0));
+    *d(1) = bitcast<uint4>(expand8(f.c.y, s0));
+    *d(2) = bitcast<uint4>(expand8(f.c.z, s1));
+    *d(3) = bitcast<uint4>(expand8(f.c.w, s1));
   }
 }
 
@@ -405,13 +430,16 @@ __device__ __forceinline__ void wide_mainloop(const Rows& w, int wc, int ws_row,
       expand_frag<MODE>(fw[u % kWSets], sc, av);
       const uint8_t* bm = lds.buf + cb * WideLds<NM>::kBuf + (MODE == MOE_A4 ? m : 0) * kWideTok * kTokStride +
                           (u % 2) * (kKStep * 2) + 64 * g;
+      // logical slot 16 (u % 2) + 4 g + j of the row sits at 16 (u % 2) + 4 g + (j ^ xr) (slot_swz)
+      const int xr = (2 * (u % 2) + (g >> 1)) & 3;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
           for (int b = 0; b < kB; ++b) {
-            const uint4 bv = *reinterpret_cast<const uint4*>(bm + (b * kWideTok + 16 * t + r) * kTokStride + 16 * j);
+            const uint4 bv =
+                *reinterpret_cast<const uint4*>(bm + (b * kWideTok + 16 * t + r) * kTokStride + 16 * (j ^ xr));
             acc[t] = wide_mfma<MODE>(av[j], bv, acc[t]);
           }
         }
