@@ -672,6 +672,110 @@ __global__ void __launch_bounds__(NW * kWave) k_down_wide(FfnArgs a, const int4*
   }
 }
 
+// Down with a short K (I <= 512, at most four 128-K steps): the chunk's whole
+// intermediate fits the two LDS buffers, so it is staged once and the
+// workgroup sweeps PASSES blocks of 16 NW output rows over it (wave w: rows
+// o0 = 16 NW (PASSES rb + p) + 16 w .. +15 in pass p), with the next pass's
+// weights loaded while the current one computes.  Staging (activation loads,
+// expansion, a barrier) is the fixed cost of a down workgroup at this K; the
+// sweep spreads it over PASSES times the weight rows.  Each output row is
+// computed as in k_down_wide: the same fragments, MFMA order and epilogue.
+template <int MODE, int NW, int PASSES>
+__global__ void __launch_bounds__(NW * kWave) k_down_wide_short(FfnArgs a, const int4* __restrict__ plan, int slots) {
+  constexpr int kRows = 16 * NW;
+  constexpr int NM = wide_planes<MODE, false>();
+  constexpr int kB = MODE == MOE_A8 ? 2 : 1;
+  constexpr int kSteps = 4;   // I <= 512
+  __shared__ WideLds<NM> lds;
+  __shared__ float s_pw[kWideTok];
+  const Job job = wide_job(plan, (a.H + kRows * PASSES - 1) / (kRows * PASSES), slots);
+  if (job.e < 0) return;
+  const int e = job.e, row0 = job.row0, np = job.ne;
+  const int H = a.H, I = a.I, nsteps = I / kKStep;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = lane_id();
+  const int r = lane & 15, g = lane >> 4;
+  auto row_of = [&](int n) { return row0 + n; };
+  Rows x;
+  if constexpr (MODE == MOE_A4)
+    x = make_rows(a.h_codes + (size_t)row0 * (I / 2), static_cast<const uint8_t*>(a.h_scales) + (size_t)row0 * (I / 16),
+                  np, I);
+  else
+    x = make_xrows<MODE>(a.h_codes, a.h_scales, row0 + np, I);
+  const int ntt = (np + 15) / 16;
+  const Stager sg = make_stager<MODE, NM>(np, ntt, I, row_of);
+
+  // the weights of pass p: the wave's 16 rows (clamped past H: computed, not stored)
+  const int wc = r * (I / 2) + 16 * g, ws_row = r * (I / 16);
+  auto wrows = [&](int p) {
+    const int o0 = (job.rb * PASSES + p) * kRows + wave * 16;
+    const size_t row16 = (size_t)e * H + (o0 < H ? o0 : H - 16);
+    return make_rows(a.dn_codes + row16 * (I / 2), a.dn_scales + row16 * (I / 16), 16, I);
+  };
+  uint4 fw[2][kSteps], sw[2];
+  auto load_pass = [&](int p, auto SET) {
+    constexpr int set = decltype(SET)::value;
+    const Rows w = wrows(p);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) fw[set][s] = load_wcodes(w, wc, min(s, nsteps - 1));
+    sw[set] = load_wscales(w, ws_row, g, 0);
+  };
+  load_pass(0, std::integral_constant<int, 0>{});
+  XFrag<MODE> fx[2];
+  load_chunk<MODE>(fx[0], x, sg, 0);
+  load_chunk<MODE>(fx[1], x, sg, min(1, (nsteps + 1) / 2 - 1));
+  float pw = 1.0f;
+  if constexpr (MODE == MOE_A8) {
+    token_pow2<NW>(static_cast<const float*>(a.h_scales), I, np, row_of, s_pw);
+    __syncthreads();
+    pw = s_pw[sg.sn];
+  }
+  stage_chunk<MODE>(lds.buf, fx[0], sg, pw);
+  stage_chunk<MODE>(lds.buf + WideLds<NM>::kBuf, fx[1], sg, pw);
+  __syncthreads();   // the only barrier after this point: LDS is read-only below
+
+  const float f = a.dn_wscale[e] * (MODE == MOE_A4 ? a.dn_inscale[e] : 1.0f);
+  static_for<0, PASSES>([&](auto P) {
+    constexpr int p = decltype(P)::value, set = p % 2;
+    if constexpr (p + 1 < PASSES) load_pass(p + 1, std::integral_constant<int, set ^ 1>{});   // in flight during this pass
+    __builtin_amdgcn_sched_barrier(0);
+    const int o0 = (job.rb * PASSES + p) * kRows + wave * 16;
+    if (o0 >= H) return;
+    f32x4 acc[kWideTiles];
+#pragma unroll
+    for (int t = 0; t < kWideTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    by_tiles(ntt, [&](auto NTc) {
+      constexpr int NT = decltype(NTc)::value;
+      static_for<0, kSteps>([&](auto U) {
+        constexpr int u = decltype(U)::value;
+        if (u >= nsteps) return;
+        WideOp<MODE> av[4];
+        expand_frag<MODE>(fw[set][u], window_scales<u>(sw[set], lane), av);
+        const uint8_t* bm = lds.buf + (u / 2) * WideLds<NM>::kBuf + (u % 2) * (kKStep * 2) + 64 * g;
+        const int xr = (2 * (u % 2) + (g >> 1)) & 3;   // slot_swz
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int b = 0; b < kB; ++b) {
+              const uint4 bv =
+                  *reinterpret_cast<const uint4*>(bm + (b * kWideTok + 16 * t + r) * kTokStride + 16 * (j ^ xr));
+              acc[t] = wide_mfma<MODE>(av[j], bv, acc[t]);
+            }
+      });
+    });
+#pragma unroll
+    for (int t = 0; t < kWideTiles; ++t) {
+      const int n = 16 * t + r;
+      if (t < ntt && n < np) {
+        const float ft = MODE == MOE_A8 ? f / s_pw[n] : f;
+        const float4 o = make_float4(acc[t][0] * ft, acc[t][1] * ft, acc[t][2] * ft, acc[t][3] * ft);
+        *reinterpret_cast<float4*>(a.y + (size_t)(row0 + n) * H + o0 + 4 * g) = o;
+      }
+    }
+  });
+}
+
 // Plan entries for P sorted rows: at most one partial chunk per active expert
 // (active experts <= min(E, P)) plus P / 32 full chunks.
 int wide_plan_entries(int P, int E) { return (P < E ? P : E) + P / kWideTok; }
@@ -692,8 +796,17 @@ __global__ void __launch_bounds__(256) k_debug_plan(int cols, int n_entries, int
 
 size_t debug_wide_plan_bytes(int cols) { return (size_t)((cols + kWideTok - 1) / kWideTok) * sizeof(int4); }
 
+// Output-row passes of a short-K down workgroup (k_down_wide_short).
+constexpr int kDownPasses = 3;
+
 template <int MODE>
 static moe_status launch_down(const FfnArgs& a, const int4* plan, int n, const char* what, hipStream_t s) {
+  if (a.I <= 4 * kKStep) {
+    const int nrb = (a.H + kDownRows * kDownPasses - 1) / (kDownRows * kDownPasses);
+    hipLaunchKernelGGL((k_down_wide_short<MODE, kDownWaves, kDownPasses>), dim3(wide_grid(n, nrb)),
+                       dim3(kDownWaves * kWave), 0, s, a, plan, n);
+    return check_launch(what);
+  }
   const int nrb = (a.H + kDownRows - 1) / kDownRows;
   hipLaunchKernelGGL((k_down_wide<MODE, kDownWaves>), dim3(wide_grid(n, nrb)), dim3(kDownWaves * kWave), 0, s, a,
                      plan, n);
