@@ -54,10 +54,20 @@ typedef enum {
 typedef enum {
   MOE_A16 = 0, /* bf16 activations on the 4-bit weights (W4A16) */
   MOE_A8 = 1,  /* E4M3 activations, one fp32 scale per 16 (W4A8) */
-  MOE_A4 = 2   /* NVFP4 activations under the matrix's fp32 input scale (W4A4) */
+  MOE_A4 = 2,  /* NVFP4 activations under the matrix's fp32 input scale (W4A4) */
+  /* range markers, not modes: with them every int32 is a value of the type in
+   * C and C++, so an out-of-range argument reaches the validation (MOE_E_ARG)
+   * as the caller passed it */
+  MOE_ACT_MODE_RANGE_MIN_ = -2147483647 - 1,
+  MOE_ACT_MODE_RANGE_MAX_ = 2147483647
 } moe_act_mode;
 
-typedef enum { MOE_DT_BF16 = 0, MOE_DT_F32 = 1 } moe_dtype;
+typedef enum {
+  MOE_DT_BF16 = 0,
+  MOE_DT_F32 = 1,
+  MOE_DTYPE_RANGE_MIN_ = -2147483647 - 1, /* range markers, as for moe_act_mode */
+  MOE_DTYPE_RANGE_MAX_ = 2147483647
+} moe_dtype;
 
 /* Encoding of the expert weights. */
 typedef enum {

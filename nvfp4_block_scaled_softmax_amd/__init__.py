@@ -15,7 +15,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_nvfp4.so")
+# MOE_NVFP4_LIB names another build of the same sources (the host-sanitizer
+# build of sanitize.py); by default the in-tree library.
+LIB_PATH = os.environ.get("MOE_NVFP4_LIB") or os.path.join(_HERE, "libmoe_nvfp4.so")
 
 MOE_A16, MOE_A8, MOE_A4 = 0, 1, 2
 MODES = {"A16": MOE_A16, "A8": MOE_A8, "A4": MOE_A4,

@@ -98,7 +98,8 @@ _cpu = None
 def _cpu_lib():
     global _cpu
     if _cpu is None:
-        path = os.path.join(_HERE, "libsynth_cpu.so")
+        # SYNTH_CPU_LIB: another build of synth_cpu.c (the host-sanitizer build)
+        path = os.environ.get("SYNTH_CPU_LIB") or os.path.join(_HERE, "libsynth_cpu.so")
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
         lib = ctypes.CDLL(path)
