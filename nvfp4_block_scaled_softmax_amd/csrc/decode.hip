@@ -258,7 +258,10 @@ __global__ void __launch_bounds__(kPermThreads)
   __shared__ int rank[kMaxExperts];
   __shared__ int wcnt[kPermWaves][kMaxExperts];
   __shared__ int wave_tot[kPermWaves];
-  __shared__ __align__(16) int pid[kSmallP];   // 16-byte aligned: rank_small reads it four at a time
+  // every pair's expert (T * k <= 8 * 64), 16-byte aligned: rank_small reads it
+  // four at a time; the generic permutation reads it too, not the ids stored
+  // to memory an instant before
+  __shared__ __align__(16) int pid[kNarrowT * kMaxTopK];
   __shared__ int s_n;
   __shared__ int4 splan[kSmallP];
   __shared__ int s_last;
@@ -297,8 +300,8 @@ __global__ void __launch_bounds__(kPermThreads)
   // ---- the last workgroup: every expert's logits are visible
   const int P = T * k;
   for (int t = wave; t < T; t += kPermWaves)
-    topk_wave<S, true>(logits, t, E, k, ids, tw, P <= kSmallP ? pid : nullptr, &s_topk[wave]);
-  __syncthreads();   // ids are written (same workgroup)
+    topk_wave<S, true>(logits, t, E, k, ids, tw, pid, &s_topk[wave]);
+  __syncthreads();   // pid is written
   if (P <= kSmallP) {
     const int n_act = rank_small<false>(pid, splan, &s_n, P, k, sorted_pairs, pair_row);
     small_offsets<kPermThreads>(splan, n_act, P, E, offsets);
@@ -311,7 +314,7 @@ __global__ void __launch_bounds__(kPermThreads)
       for (int w = 0; w < kPermWaves; ++w) wcnt[w][e] = 0;
     }
     __syncthreads();
-    for (int p = tid; p < P; p += kPermThreads) atomicAdd(&cnt[ids[p]], 1);
+    for (int p = tid; p < P; p += kPermThreads) atomicAdd(&cnt[pid[p]], 1);
     __syncthreads();
     const int total = scan_experts(cnt, base, E, wave_tot);
     for (int e = tid; e < E; e += kPermThreads) offsets[e] = base[e];
@@ -323,7 +326,7 @@ __global__ void __launch_bounds__(kPermThreads)
     for (int e = tid; e < E; e += kPermThreads)
       if (cnt[e] > 0) st->plan[rank[e]] = make_int4(e, base[e], cnt[e], 0);
     if (tid == 0) st->n_active = n_active;
-    scatter_range(ids, 0, P, E, base, wcnt, sorted_pairs, pair_row);
+    scatter_range(pid, 0, P, E, base, wcnt, sorted_pairs, pair_row);
   }
   // B's counters start at zero: the previous call's B has finished (it ran
   // before this kernel on the stream); clear what it may have counted, and the
@@ -508,8 +511,13 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
 
 // The expert half on its own: the routing kernel has finished, so the plan is
 // read with plain loads.
+// Four workgroups per CU (at most 128 VGPRs) where the tiles fit without
+// spilling: a call at T = 8 has thousands of tiles, so occupancy sets how many
+// rounds they take (4-bit mode: 129 VGPRs unbounded, 3 per CU).  The LDS side
+// of the same bound: launch_b stages at most kExpertGuCols columns.
+constexpr int kExpertGuCols = 4;
 template <int MODE, int GL, int GC, int DL, int DC>
-__global__ void __launch_bounds__(kTileThreads)
+__global__ void __launch_bounds__(kTileThreads, MODE == kModeQ4 ? 1 : 4)
     k_experts_decode(FfnArgs a, DecodeState* __restrict__ st, int max_slots, int cols_gu,
                      int cols_dn, const int32_t* __restrict__ pair_row,
                      const float* __restrict__ tw, const uint16_t* __restrict__ residual,
@@ -797,10 +805,15 @@ template <int MODE>
 static void launch_b(const FfnArgs& a, DecodeState* st, int max_slots, const int32_t* prow,
                      const float* tw, const uint16_t* residual, uint16_t* out, const float* shy,
                      hipStream_t s) {
-  // column groups as the per-stage kernels size them
+  // column groups as the per-stage kernels size them, gate/up at most 4: the
+  // dynamic LDS is sized for the widest slot, but a slot of a call with up to
+  // 8 tokens mostly holds 1 or 2 of them, and 8 columns of x (37 KB in the
+  // 4-bit mode at H = 3072) left room for only 3 workgroups per CU; with 4 the
+  // tiles run 4 per CU and a wider slot loops over its columns (W4A4 at T = 8:
+  // 84.4 -> 77.4 us per call)
   const int per_col_gu = (a.H / 32) * ChunkLds<MODE>::kStride;
   const int per_col_dn = (a.I / 32) * ChunkLds<MODE>::kStride;
-  const int cols_gu = max(1, min(min(8, a.T), kLdsBudget / per_col_gu));
+  const int cols_gu = max(1, min(min(kExpertGuCols, a.T), kLdsBudget / per_col_gu));
   const int cols_dn = max(1, min(min(8, a.T), kLdsBudget / per_col_dn));
   const int gc = gu_config(a.H / 32), dl = dn_config(a.I / 32);
   if (gc == 2) launch_b2<MODE, 2>(a, dl, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, shy, s);

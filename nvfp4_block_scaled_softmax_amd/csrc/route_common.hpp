@@ -62,10 +62,15 @@ __device__ __forceinline__ void router_logits_wave(const uint16_t* __restrict__ 
     }
   }
   const float b = bias ? bias[e] : 0.0f;
+  // every token's row sum at once (DPP steps and four lane reads, no LDS
+  // round trips), so the T reductions overlap instead of running in turn
+  float red[kNarrowT];
+#pragma unroll
+  for (int t = 0; t < kNarrowT; ++t) red[t] = t < T ? wave_sum(acc[t]) : 0.0f;
 #pragma unroll
   for (int t = 0; t < kNarrowT; ++t) {
     if (t < T) {
-      const float v = group_sum<kWave>(acc[t]);
+      const float v = red[t];
       if constexpr (TAG) {
         if (lane == 0)
           __hip_atomic_store(&tagged[(size_t)t * E + e],
