@@ -338,12 +338,18 @@ __global__ void __launch_bounds__(kPermThreads)
 }
 
 // ------------------------------------------------------------------ B: experts
+// Modes whose intermediate the single launch hands over as tagged words.
+template <int MODE>
+constexpr bool kTagH = MODE == MOE_A16 || MODE == MOE_A8;
+
 // The expert tiles of one call, wg counted from the first expert workgroup:
 // [0, G) gate/up tile (slot, rb) = (wg / nrb_gu, wg % nrb_gu); [G, G + D) down
 // tile of (slot, rb) likewise with nrb_dn.  plan_of(slot, role) gives the
 // slot's SlotPlan, expert < 0 for a slot past the active count (its tiles exit
-// at once).
-template <int MODE, int GL, int GC, int DL, int DC, typename PlanOf>
+// at once).  FUSED: the single launch, where the 8-bit x is not in the
+// workspace yet (the routing workgroups write it meanwhile), so the gate/up
+// tiles quantize it themselves while they wait for the plan.
+template <int MODE, int GL, int GC, int DL, int DC, bool FUSED = false, typename PlanOf>
 __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __restrict__ st, int wg,
                                              uint32_t dn_hold, int max_slots, int cols_gu, int cols_dn,
                                              const int32_t* __restrict__ pair_row,
@@ -363,20 +369,25 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
     const int slot = wg / nrb_gu, rb = wg % nrb_gu;
     // x of every token fits the tile's LDS (16/8-bit modes): it is staged while
     // the plan is awaited, so no x load trails the weight loads
-    const bool xs = MODE != MOE_A4 && a.T <= cols_gu;
+    const bool xs = MODE != MOE_A4 && a.T <= cols_gu;   // (always so in the single launch)
     if (xs) {
-      stage_gateup_cols<MODE, true>(a, 0, 0, 0, a.T, nullptr, lds);
+      if constexpr (FUSED && MODE == MOE_A8) stage_gateup_quant_a8(a, lds);
+      else stage_gateup_cols<MODE, true>(a, 0, 0, 0, a.T, nullptr, lds);
       __syncthreads();
     }
     const SlotPlan pl = plan_of(slot, 0);
     if (pl.e < 0) return;
-    if (MODE == MOE_A16 && pl.outs_epoch != 0u) {   // single launch: h goes out as tagged words
-      if (xs)
+    if (kTagH<MODE> && pl.outs_epoch != 0u) {   // single launch: h goes out as tagged words
+      if (FUSED && MODE == MOE_A8) {
         gateup_tile<MODE, GL, GC, true, false, true>(a, pl.e, pl.row0, pl.rows, rb, cols_gu, lds, pl.tmask,
                                                      st->h_tag, pl.outs_epoch);
-      else
+      } else if (xs) {
+        gateup_tile<MODE, GL, GC, true, false, true>(a, pl.e, pl.row0, pl.rows, rb, cols_gu, lds, pl.tmask,
+                                                     st->h_tag, pl.outs_epoch);
+      } else {
         gateup_tile<MODE, GL, GC, true>(a, pl.e, pl.row0, pl.rows, rb, cols_gu, lds, pl.tmask, st->h_tag,
                                         pl.outs_epoch);
+      }
       return;
     }
     if constexpr (MODE != MOE_A4) {
@@ -419,10 +430,10 @@ __device__ __forceinline__ void expert_tiles(const FfnArgs& a, DecodeState* __re
         const int t = i / kDnRows, o = rb * kDnRows + i % kDnRows;
         s_res[t][i % kDnRows] = residual && o < a.H ? residual[(size_t)t * a.H + o] : (uint16_t)0;
       }
-      if (!(MODE == MOE_A16 && pl.outs_epoch != 0u))   // (single launch: h words are polled instead)
+      if (!(kTagH<MODE> && pl.outs_epoch != 0u))   // (single launch: h words are polled instead)
         wait_at_least(&st->gu_done[slot].v, (uint32_t)nrb_gu, &st->timeouts.v);
     }, pl.outs_epoch != 0u ? st->y_tag : nullptr, pl.outs_epoch,
-       MODE == MOE_A16 && pl.outs_epoch != 0u ? st->h_tag : nullptr, &st->timeouts.v);
+       kTagH<MODE> && pl.outs_epoch != 0u ? st->h_tag : nullptr, &st->timeouts.v);
     if (pl.outs_epoch != 0u) {
       // single launch: the tile of slot 0 (always active) combines its row block
       // by polling the tagged outputs of every pair's row; the others are done
@@ -604,6 +615,30 @@ __global__ void __launch_bounds__(kTileThreads, (GC <= 3 && S <= 8) ? 4 : 1)
     router_logits_wave<kTileThreads, true, true>(x, wr, bias, T, H, E, wg * kTileWaves + wave,
                                                  reinterpret_cast<uint4*>(lds), logits,
                                                  st->logit_tag, epoch);
+    if constexpr (MODE == MOE_A8) {
+      // x quantized per token into the workspace (the gate/up tiles quantize
+      // their own copy in LDS; this one is for the caller), from the x that
+      // router_logits_wave staged in LDS, after the logits are out
+      const int nb = H / 16;
+      const uint16_t* xl = reinterpret_cast<const uint16_t*>(lds);
+      uint8_t* xc = const_cast<uint8_t*>(a.xq_codes);
+      float* xsc = static_cast<float*>(const_cast<void*>(a.xq_scales));
+      for (int i = wg * kTileThreads + tid; i < T * nb; i += R * kTileThreads) {
+        const uint4 u0 = *reinterpret_cast<const uint4*>(xl + (size_t)i * 16);
+        const uint4 u1 = *reinterpret_cast<const uint4*>(xl + (size_t)i * 16 + 8);
+        const uint32_t wv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          v[2 * j] = bf16_to_f32(wv[j] & 0xFFFFu);
+          v[2 * j + 1] = bf16_to_f32(wv[j] >> 16);
+        }
+        uint32_t w4[4];
+        const float sc = fp8_quant16(v, w4);
+        *reinterpret_cast<uint4*>(xc + (size_t)i * 16) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        xsc[i] = sc;
+      }
+    }
     if (wg != R - 1) return;   // the last routing workgroup runs the tail
     if (wave == 0) {   // the expert half's counters (left by the previous call) back to zero
       const int nrb_dn = (H + kDnRows - 1) / kDnRows;
@@ -694,7 +729,7 @@ __global__ void __launch_bounds__(kTileThreads, (GC <= 3 && S <= 8) ? 4 : 1)
       return;
     }
   }
-  expert_tiles<MODE, GL, GC, DL, DC>(
+  expert_tiles<MODE, GL, GC, DL, DC, true>(
       a, st, wg - R - (SH ? sgu + sdn : 0), dn_hold, max_slots, cols_gu, cols_dn, pair_row, tw, residual, out, lds,
       shared_y,
       [&](int slot, int role) {
@@ -773,7 +808,9 @@ bool decode_fusable(int T, int H, int I) {
   return T <= kNarrowT && gu_config(H / 32) > 0 && dn_config(I / 32) > 0;
 }
 
-static bool single_launch(moe_act_mode mode, int T, int k) { return mode == MOE_A16 && T * k <= kSmallP; }
+static bool single_launch(moe_act_mode mode, int T, int k) {
+  return (mode == MOE_A16 || mode == MOE_A8) && T * k <= kSmallP;
+}
 
 int decode_launches(moe_act_mode mode, int T, int k, int H, int I) {
   if (T < 1 || k < 1 || !decode_fusable(T, H, I)) return 0;
@@ -821,22 +858,23 @@ static void launch_b(const FfnArgs& a, DecodeState* st, int max_slots, const int
   else launch_b2<MODE, 4>(a, dl, st, max_slots, cols_gu, cols_dn, prow, tw, residual, out, shy, s);
 }
 
-// ---- the single-launch layer (16-bit activations, up to kSmallP pairs)
-// sa: a block's shared expert run by the same launch (decode_fuses_shared), or null.
-template <int S, int GC, int DL>
+// ---- the single-launch layer (16- and 8-bit activations, up to kSmallP pairs)
+// sa: a block's shared expert run by the same launch (decode_fuses_shared: 16-bit
+// mode only), or null.
+template <int MODE, int S, int GC, int DL>
 static void launch_one3(const FfnArgs& a, const uint16_t* x, const uint16_t* wr, const float* bias,
                         float* logits, int32_t* ids, float* tw, int32_t* prow, DecodeState* st,
                         const uint16_t* residual, uint16_t* out, uint64_t epoch, const float* shy,
                         const SharedArgs* sa, hipStream_t s) {
   const int P = a.T * a.k, max_slots = P < a.E ? P : a.E;
-  const int cols = max(1, min(min(8, a.T), kLdsBudget / ((a.H / 32) * ChunkLds<MOE_A16>::kStride)));
-  const int cols_dn = max(1, min(min(8, a.T), kLdsBudget / ((a.I / 32) * ChunkLds<MOE_A16>::kStride)));
+  const int cols = max(1, min(min(8, a.T), kLdsBudget / ((a.H / 32) * ChunkLds<MODE>::kStride)));
+  const int cols_dn = max(1, min(min(8, a.T), kLdsBudget / ((a.I / 32) * ChunkLds<MODE>::kStride)));
   const int R = (a.E + kTileWaves - 1) / kTileWaves;
   const int sgu = sa ? sa->Is / kShGuRows : 0, sdn = sa ? (a.H + kShDnRows - 1) / kShDnRows : 0;
   const int grid = R + sgu + sdn + max_slots * (a.I / kGuRows + (a.H + kDnRows - 1) / kDnRows);
   size_t lds = (size_t)a.T * a.H * 2;
-  lds = std::max(lds, (size_t)cols * (a.H / 32) * ChunkLds<MOE_A16>::kStride);
-  lds = std::max(lds, (size_t)cols_dn * (a.I / 32) * ChunkLds<MOE_A16>::kStride);
+  lds = std::max(lds, (size_t)cols * (a.H / 32) * ChunkLds<MODE>::kStride);
+  lds = std::max(lds, (size_t)cols_dn * (a.I / 32) * ChunkLds<MODE>::kStride);
   if (sa) lds = std::max(lds, (size_t)a.T * sa->Is * 2);   // the shared down tile's h
   const SharedArgs sarg = sa ? *sa : SharedArgs{};
   auto go = [&](auto kernel) {
@@ -846,33 +884,51 @@ static void launch_one3(const FfnArgs& a, const uint16_t* x, const uint16_t* wr,
                        max_slots, cols, cols_dn, prow, residual, out, (uint32_t)epoch, dn_hold, shy, sarg, sgu,
                        sdn);
   };
-  if (sa) go(&k_layer_decode<S, MOE_A16, 32, GC, DL, 1, true>);
-  else go(&k_layer_decode<S, MOE_A16, 32, GC, DL, 1, false>);
+  if constexpr (MODE == MOE_A16) {
+    if (sa) go(&k_layer_decode<S, MODE, 32, GC, DL, 1, true>);
+    else go(&k_layer_decode<S, MODE, 32, GC, DL, 1, false>);
+  } else {
+    go(&k_layer_decode<S, MODE, 32, GC, DL, 1, false>);
+  }
 }
 
-template <int S, int GC>
+template <int MODE, int S, int GC>
 static void launch_one2(int dl, const FfnArgs& a, const uint16_t* x, const uint16_t* wr,
                         const float* bias, float* logits, int32_t* ids, float* tw, int32_t* prow,
                         DecodeState* st, const uint16_t* residual, uint16_t* out, uint64_t epoch,
                         const float* shy, const SharedArgs* sa, hipStream_t s) {
-  if (dl == 8) launch_one3<S, GC, 8>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
-  else if (dl == 16) launch_one3<S, GC, 16>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
-  else launch_one3<S, GC, 32>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+  if (dl == 8) launch_one3<MODE, S, GC, 8>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+  else if (dl == 16) launch_one3<MODE, S, GC, 16>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+  else launch_one3<MODE, S, GC, 32>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
 }
 
-template <int S>
+template <int MODE, int S>
 static void launch_one(const FfnArgs& a, const uint16_t* x, const uint16_t* wr, const float* bias,
                        float* logits, int32_t* ids, float* tw, int32_t* prow, DecodeState* st,
                        const uint16_t* residual, uint16_t* out, uint64_t epoch, const float* shy,
                        const SharedArgs* sa, hipStream_t s) {
   const int gc = gu_config(a.H / 32), dl = dn_config(a.I / 32);
-  if (gc == 2) launch_one2<S, 2>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
-  else if (gc == 3) launch_one2<S, 3>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
-  else launch_one2<S, 4>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+  if (gc == 2) launch_one2<MODE, S, 2>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+  else if (gc == 3) launch_one2<MODE, S, 3>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+  else launch_one2<MODE, S, 4>(dl, a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+}
+
+template <int MODE>
+static void launch_one_mode(const FfnArgs& a, const uint16_t* x, const uint16_t* wr, const float* bias,
+                            float* logits, int32_t* ids, float* tw, int32_t* prow, DecodeState* st,
+                            const uint16_t* residual, uint16_t* out, uint64_t epoch, const float* shy,
+                            const SharedArgs* sa, hipStream_t s) {
+  const int E = a.E;
+  if (E <= 64) launch_one<MODE, 1>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+  else if (E <= 128) launch_one<MODE, 2>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+  else if (E <= 256) launch_one<MODE, 4>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+  else if (E <= 512) launch_one<MODE, 8>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+  else launch_one<MODE, 16>(a, x, wr, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
 }
 
 bool decode_fuses_shared(moe_act_mode mode, int T, int k, int H, int I, int Is) {
-  return decode_fusable(T, H, I) && single_launch(mode, T, k) && Is >= 32 && Is <= kFusedShIs && Is % 32 == 0;
+  return mode == MOE_A16 && decode_fusable(T, H, I) && single_launch(mode, T, k) && Is >= 32 &&
+         Is <= kFusedShIs && Is % 32 == 0;
 }
 
 // Epochs of eager single-launch calls: 31 bits, not reused within 2^31 calls
@@ -908,11 +964,10 @@ moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, in
         do epoch = ++g_epoch & 0x7FFFFFFFu; while (epoch == 0u);   // 0: a never-written entry
       }
       const float* shy = sa ? nullptr : shared_y;   // (fused: the combine polls the launch's own)
-      if (E <= 64) launch_one<1>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
-      else if (E <= 128) launch_one<2>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
-      else if (E <= 256) launch_one<4>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
-      else if (E <= 512) launch_one<8>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
-      else launch_one<16>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+      if (mode == MOE_A8)
+        launch_one_mode<MOE_A8>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
+      else
+        launch_one_mode<MOE_A16>(a, x, w_router, bias, logits, ids, tw, prow, st, residual, out, epoch, shy, sa, s);
       return check_launch("moe_layer_forward (decode layer)");
     }
   }
@@ -931,10 +986,10 @@ moe_status launch_layer_decode(const moe_nvfp4_experts& w, moe_act_mode mode, in
   if (stage_mask & 2) {   // experts and combine
     const FfnArgs a = make_ffn_args(w, mode, x, T, k, offsets, sorted, y, ffn_ws);
     const int P = T * k, max_slots = P < E ? P : E;
-    switch (mode) {
+    switch ((int)mode) {   // (kModeQ4 is the library's internal mode of q4_g64_fp16 experts)
       case MOE_A16: launch_b<MOE_A16>(a, st, max_slots, prow, tw, residual, out, shared_y, s); break;
       case MOE_A8: launch_b<MOE_A8>(a, st, max_slots, prow, tw, residual, out, shared_y, s); break;
-      case (moe_act_mode)kModeQ4: launch_b<kModeQ4>(a, st, max_slots, prow, tw, residual, out, shared_y, s); break;
+      case kModeQ4: launch_b<kModeQ4>(a, st, max_slots, prow, tw, residual, out, shared_y, s); break;
       default: launch_b<MOE_A4>(a, st, max_slots, prow, tw, residual, out, shared_y, s); break;
     }
     return check_launch("moe_layer_forward (decode experts)");

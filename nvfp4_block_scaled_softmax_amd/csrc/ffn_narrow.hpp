@@ -16,6 +16,35 @@ constexpr int kTileWaves = kTileThreads / kWave;
 
 constexpr int kStageBatch = 4;
 
+// Tagged words of one row of the 8-bit intermediate (see gateup_tile).
+__host__ __device__ constexpr int h8_words(int I) { return I / 4 + I / 16; }
+
+// 8-bit mode, x of tokens 0..T-1 quantized in the tile: every 16-value block of
+// a token's bf16 row as act_quant_fp8 computes it (fp8_quant16), written into
+// the LDS chunk layout stage_gateup_cols uses (32 codes, then the two blocks'
+// fp32 scales), columns by token.
+__device__ void stage_gateup_quant_a8(const FfnArgs& a, uint8_t* lds) {
+  constexpr int S = ChunkLds<MOE_A8>::kStride;
+  const int H = a.H, NC = H / 32, nb = H / 16;
+  for (int i = threadIdx.x; i < a.T * nb; i += kTileThreads) {
+    const int t = i / nb, b = i % nb;
+    const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)t * H + 16 * b);
+    const uint4 u0 = src[0], u1 = src[1];
+    const uint32_t wv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[2 * j] = bf16_to_f32(wv[j] & 0xFFFFu);
+      v[2 * j + 1] = bf16_to_f32(wv[j] >> 16);
+    }
+    uint32_t w4[4];
+    const float sc = fp8_quant16(v, w4);
+    uint8_t* c = lds + ((size_t)t * NC + b / 2) * S;
+    *reinterpret_cast<uint4*>(c + 16 * (b % 2)) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    *reinterpret_cast<float*>(c + 32 + 4 * (b % 2)) = sc;
+  }
+}
+
 // tok[col]: the token of column col (the 16/8-bit modes read x by token);
 // with BY_TOKEN the columns are the tokens 0..ncol-1 themselves.
 template <int MODE, bool BY_TOKEN = false>
@@ -207,9 +236,11 @@ __device__ void stage_gateup_quant_a4(const FfnArgs& a, int e, int row0, int c0,
   }
 }
 
-// htag (16-bit activations only): every pair of h values (2i, 2i+1) of a row is
-// also published as one 64-bit word htag[row * I/2 + i] = (their bf16 bits <<
-// 32) | epoch, written as one atomic store, for consumers that poll the words.
+// htag: the intermediate is also published as 64-bit words (payload << 32) |
+// epoch, each written as one atomic store, for consumers that poll the words:
+// 16-bit mode, the bf16 pair (2i, 2i+1) of a row in htag[row * I/2 + i]; 8-bit
+// mode, row r's words at htag + r * h8_words(I): four E4M3 codes (values 4i ..
+// 4i+3) in word i < I/4, then block b's fp32 scale in word I/4 + b.
 // QX (4-bit mode): x is quantized in the tile (stage_gateup_quant_a4) instead of
 // read quantized from the workspace; row block 0's tile also writes it there.
 // XS (16/8-bit modes, a.T <= max_cols): the caller has staged x of every token
@@ -352,6 +383,15 @@ __device__ __forceinline__ void gateup_tile(const FfnArgs& a, int e, int row0, i
           const float sc = fp8_quant16(hbuf[col], w4);
           hst128<COH>(a.h_codes, r * I + i0, make_uint4(w4[0], w4[1], w4[2], w4[3]));
           hst32<COH>(a.h_scales, 4 * (r * (I / 16) + rb), __builtin_bit_cast(uint32_t, sc));
+          if (htag) {   // the block's 16 codes and its scale as tagged words
+            uint64_t* hw = htag + r * h8_words(I);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              __hip_atomic_store(&hw[i0 / 4 + q], (uint64_t)w4[q] << 32 | epoch, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&hw[I / 4 + rb], (uint64_t)__builtin_bit_cast(uint32_t, sc) << 32 | epoch,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
         } else {
           uint32_t lo, hi;
           const uint32_t sc = nvfp4_quant16(hbuf[col], dn_in, lo, hi);
@@ -372,7 +412,7 @@ template <int MODE, int LPR, int CPL, bool COH, typename Wait>
 // With ytag, every output value is also published as one 64-bit word
 // ytag[row * H + o] = (value bits << 32) | epoch (one atomic store), for a
 // consumer that polls the words instead of waiting on a counter.
-// With htag (16-bit activations), h is read from the tagged words that
+// With htag (16- and 8-bit activations), h is read from the tagged words that
 // gateup_tile publishes, each polled until it carries epoch (a bounded wait on
 // abort_word, see Patience; a thread that gives up uses whatever it read).
 __device__ __forceinline__ void down_tile(const FfnArgs& a, int e, int row0, int ne, int rb,
@@ -430,6 +470,28 @@ __device__ __forceinline__ void down_tile(const FfnArgs& a, int e, int row0, int
           v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         *reinterpret_cast<uint32_t*>(lds + ((size_t)col * NC + p / 16) * S + 4 * (p % 16)) = (uint32_t)(v >> 32);
+      }
+    } else if (MODE == MOE_A8 && htag) {
+      // a row's words: codes 4p .. 4p+3 in word p < I/4 (chunk p / 8, bytes
+      // 4 (p % 8) of it), then block b's scale (chunk b / 2, after its codes)
+      const int nw = h8_words(I), ncw = I / 4;
+      Patience pat;
+      bool gave_up = false;
+      for (int i = threadIdx.x; i < ncol * nw; i += kTileThreads) {
+        const int col = i / nw, p = i % nw;
+        const uint64_t* w = htag + (size_t)(row0 + c0 + col) * nw + p;
+        uint64_t v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        while ((uint32_t)v != epoch && !gave_up) {
+          if (pat.expired(abort_word)) {
+            gave_up = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+          v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        uint8_t* dst = p < ncw ? lds + ((size_t)col * NC + p / 8) * S + 4 * (p % 8)
+                               : lds + ((size_t)col * NC + (p - ncw) / 2) * S + 32 + 4 * ((p - ncw) % 2);
+        *reinterpret_cast<uint32_t*>(dst) = (uint32_t)(v >> 32);
       }
     } else {
       stage_down_cols<MODE, COH>(a, row0, c0, ncol, lds);

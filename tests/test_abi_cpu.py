@@ -84,7 +84,8 @@ def test_layer_stage_and_fused_queries():
     assert moe.layer_launches("A16", 1, 10, 3072, 512) == 1
     assert moe.layer_launches("A16", 6, 10, 3072, 512) == 1
     assert moe.layer_launches("A16", 7, 10, 3072, 512) == 2
-    assert moe.layer_launches("A8", 2, 10, 3072, 512) == 2   # x quantized in the routing kernel
+    assert moe.layer_launches("A8", 2, 10, 3072, 512) == 1   # x quantized in the gate/up tiles
+    assert moe.layer_launches("A8", 7, 10, 3072, 512) == 2   # more than 64 pairs: x quantized in the routing kernel
     assert moe.layer_launches("A4", 8, 10, 3072, 512) == 2   # x quantized in the gate/up tiles
     assert moe.layer_launches("A16", 9, 10, 3072, 512) == 0
     assert moe.layer_launches("A16", 1, 2, 256, 128) == 0

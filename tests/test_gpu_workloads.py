@@ -255,7 +255,7 @@ def test_stack_layers(dev, mode):
 
 
 # ------------------------------------------------------------------ decode edges
-# Shapes at the corners of the fused decode paths (single launch: 16-bit
+# Shapes at the corners of the fused decode paths (single launch: 16- and 8-bit
 # activations, up to 64 pairs; two launches otherwise): a router grid that does
 # not fill its last workgroup, one pair, exactly 64 pairs with shared experts,
 # 1024 experts (16 logits per top-k lane), the widest fused tiles (H=4096,
@@ -267,6 +267,7 @@ EDGES = [
     synth.Workload(23, "edge: E=1024", E=1024, k=6, H=1056, I=160, T=3, modes=("A16",)),
     synth.Workload(24, "edge: H=4096 I=1024", E=64, k=4, H=4096, I=1024, T=2, modes=("A16",)),
     synth.Workload(25, "edge: A8", E=40, k=5, H=1056, I=160, T=5, modes=("A8",)),
+    synth.Workload(26, "edge: A8 two launches", E=40, k=9, H=1056, I=160, T=8, modes=("A8",)),
 ]
 
 
@@ -275,7 +276,7 @@ def test_decode_edges(dev, w):
     """Full oracle parity of the fused forward on edge shapes, its equality with the
     per-stage entry points bit for bit, over three token batches on one workspace."""
     mode = w.modes[0]
-    single = mode == "A16" and w.T * w.k <= 64
+    single = mode in ("A16", "A8") and w.T * w.k <= 64
     assert moe.layer_launches(mode, w.T, w.k, w.H, w.I) == (1 if single else 2)
     ex, router, bias = gpu_layer(w, 0, mode, dev)
     ws = torch.zeros(moe.layer_workspace_bytes(mode, w.T, w.k, w.E, w.H, w.I), dtype=torch.uint8, device=dev)
