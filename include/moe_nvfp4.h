@@ -291,8 +291,8 @@ moe_status moe_combine_shared(const float* y_pairs, const int32_t* pair_row, con
  *   residual is not NULL (residual may equal x; out must not alias x).
  *   ws: moe_layer_workspace_bytes(mode, T, k, E, H, I) bytes, 256-byte aligned,
  *   zero-filled before its first use: up to 8 tokens the layer runs fused (one
- *   launch for 16-bit activations and up to 64 pairs, else the routing in one
- *   launch and the experts with the combine in another) and keeps
+ *   launch for 16- and 8-bit activations and up to 64 pairs, else the routing
+ *   in one launch and the experts with the combine in another) and keeps
  *   inter-workgroup state in the workspace: counters, which every call leaves at
  *   zero, and words stamped with a per-call number, which need no reset.
  *   Calls sharing a workspace must not overlap.
@@ -325,17 +325,18 @@ moe_status moe_layer_status(const void* ws, hipStream_t s);
 int moe_layer_is_fused(int T, int H, int I);
 
 /* Kernel launches of one moe_layer_forward call: 1 for the single-launch
- * decode layer (fused sizes, MOE_A16 with NVFP4 experts, T*k <= 64), 2 for
- * the fused two-kernel path (routing, experts + combine; MOE_A8 quantizes x
- * in the routing kernel, MOE_A4 in the expert kernel's gate/up tiles;
- * q4_g64_fp16 experts take this path), 0 when the per-stage kernels run.  Under stream capture the single-launch layer is one graph node
+ * decode layer (fused sizes, MOE_A16 or MOE_A8 with NVFP4 experts, T*k <= 64;
+ * MOE_A8 quantizes x in the gate/up tiles), 2 for the fused two-kernel path
+ * (routing, experts + combine; MOE_A8 quantizes x in the routing kernel,
+ * MOE_A4 in the expert kernel's gate/up tiles; q4_g64_fp16 experts take this
+ * path), 0 when the per-stage kernels run.  Under stream capture the single-launch layer is one graph node
  * too: it then takes its call number from the workspace and advances it itself
  * (a number baked into the launch would repeat on every replay). */
 int moe_layer_launches(moe_act_mode mode, int T, int k, int H, int I);
 
 /* Kernel launches of one moe_block_forward call with a shared expert of
  * intermediate width Is: 1 where the single-launch decode layer also runs the
- * shared expert (its conditions, and Is a multiple of 32 up to 512: the shared
+ * shared expert (its conditions with MOE_A16, and Is a multiple of 32 up to 512: the shared
  * expert's weights then stream while the tokens are routed), else the shared
  * expert's two kernels plus moe_layer_launches (0 for the per-stage path). */
 int moe_block_launches(moe_act_mode mode, int T, int k, int H, int I, int Is);
