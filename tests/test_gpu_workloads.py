@@ -339,36 +339,38 @@ def test_decode_tied_logits(dev, w, group):
     assert moe.layer_wait_timeouts(ws) == 0
 
 
-def test_decode_graph_replay(dev):
+@pytest.mark.parametrize("wi,mode", [(1, "A16"), (3, "A8")])
+def test_decode_graph_replay(dev, wi, mode):
     """Under stream capture the single-launch layer is recorded as one node that
     takes its epoch from the workspace and advances it itself (an epoch baked
     into the launch would repeat on replay).  Three replays, each with eager
     single-launch calls and a synchronisation before it, all equal the eager
     result bit for bit and pass the full oracle check; the graph holds one
-    kernel node per layer call."""
-    w = synth.CONFIGS[1]
-    ex, router, bias = gpu_layer(w, 0, "A16", dev)
-    nws = moe.layer_workspace_bytes("A16", w.T, w.k, w.E, w.H, w.I)
+    kernel node per layer call.  16-bit activations at T=1 and 8-bit at T=2
+    (x quantized inside the launch)."""
+    w = synth.CONFIGS[wi]
+    ex, router, bias = gpu_layer(w, 0, mode, dev)
+    nws = moe.layer_workspace_bytes(mode, w.T, w.k, w.E, w.H, w.I)
     ws_g = torch.zeros(nws, dtype=torch.uint8, device=dev)
     ws_e = torch.zeros(nws, dtype=torch.uint8, device=dev)
     x_g = bench.token_batch(w, 0, dev).clone()
     out_g = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev)
-    moe.moe_layer_forward(ex, "A16", x_g, router, w.k, ws=ws_g, out=out_g)   # warm up outside capture
+    moe.moe_layer_forward(ex, mode, x_g, router, w.k, ws=ws_g, out=out_g)   # warm up outside capture
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        moe.moe_layer_forward(ex, "A16", x_g, router, w.k, ws=ws_g, out=out_g)
-    assert moe.layer_launches("A16", w.T, w.k, w.H, w.I) == 1
+        moe.moe_layer_forward(ex, mode, x_g, router, w.k, ws=ws_g, out=out_g)
+    assert moe.layer_launches(mode, w.T, w.k, w.H, w.I) == 1
     for rep, batch in enumerate((1, 2, 3)):
-        say("graph replay", rep, "batch", batch)
+        say("graph replay", mode, rep, "batch", batch)
         x_new = bench.token_batch(w, batch, dev)
-        ref, _ = moe.moe_layer_forward(ex, "A16", x_new, router, w.k, ws=ws_e)   # eager, one launch
+        ref, _ = moe.moe_layer_forward(ex, mode, x_new, router, w.k, ws=ws_e)   # eager, one launch
         x_g.copy_(x_new)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out_g.view(torch.int16), ref.view(torch.int16)), rep
-        check_call(w, "A16", 0, synth.tokens(w, batch=batch), out_g, ws_g)   # the replay against the oracle
+        check_call(w, mode, 0, synth.tokens(w, batch=batch), out_g, ws_g)   # the replay against the oracle
     assert moe.layer_wait_timeouts(ws_g) == 0 and moe.layer_wait_timeouts(ws_e) == 0
 
 
