@@ -50,7 +50,7 @@ def test_shared_expert_matches_oracle(dev, H, Is, T):
     say("ok", info["shared_y_worst_rel"], info["shared_ties"])
 
 
-BLOCKS = [(0, "A16", 4), (1, "A16", 1), (2, "A4", 8), (1, "A16", 24)]
+BLOCKS = [(0, "A16", 4), (1, "A16", 1), (2, "A4", 8), (1, "A16", 24), (3, "A8", 2)]
 
 
 @pytest.mark.parametrize("wi,mode,T", BLOCKS, ids=[f"w{wi}-{m}-T{t}" for wi, m, t in BLOCKS])
