@@ -26,7 +26,7 @@ def say(*a):
     print("[case]", *a, flush=True)
 
 
-@pytest.mark.parametrize("wi,mode,Ts", [(1, "A16", (24, 8, 1)), (2, "A4", (8, 2))])
+@pytest.mark.parametrize("wi,mode,Ts", [(1, "A16", (24, 8, 1)), (2, "A4", (8, 2)), (3, "A8", (8, 2))])
 def test_noalloc_equals_workspace_call(dev, wi, mode, Ts):
     w = synth.CONFIGS[wi]
     ex, router, bias = bench.build_layer(w, 0, dev, mode)
